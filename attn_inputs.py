@@ -1,0 +1,86 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and bench.py.
+
+This module holds workload shapes and random draws only; none of the
+attention arithmetic.  The oracle and the HIP path both consume the tensors
+it returns, so they see bit-identical inputs.
+
+Recipe (the pages fix no random generator; this is the plainest reading):
+a CPU ``torch.Generator`` seeded with ``seed`` draws Q, K, V and then dO, in
+that order, each as ``torch.randn`` in float32 of shape [B, H, N, d].  Q and
+K are multiplied by ``qk_std`` (3 for the long-sequence large-logit
+workload), and every tensor is then rounded to the working dtype with
+``.to(dtype)`` (round-to-nearest-even for bfloat16).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: torch.dtype
+    causal: bool
+    seed: int
+    qk_std: float = 1.0
+    backward: bool = False
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(self.d) ** 0.5
+
+    def fwd_flops(self) -> float:
+        """4*B*H*N^2*d, halved under the causal mask."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2 if self.causal else f
+
+    def bwd_flops(self) -> float:
+        """2.5 times the forward count (five contractions instead of two)."""
+        return 2.5 * self.fwd_flops()
+
+
+# The five workloads: shapes, dtypes, masks and distributions as specified.
+WORKLOADS = {
+    "single_head_f32": Workload("single_head_f32", 1, 1, 256, 64, torch.float32, False, 1),
+    "h8_n1024_d64": Workload("h8_n1024_d64", 1, 8, 1024, 64, torch.bfloat16, False, 2),
+    "h8_n1024_d64_causal": Workload("h8_n1024_d64_causal", 1, 8, 1024, 64, torch.bfloat16, True, 2),
+    "b4_h16_n4096_d128_causal": Workload("b4_h16_n4096_d128_causal", 4, 16, 4096, 128,
+                                         torch.bfloat16, True, 3),
+    "h32_n16384_d128_causal_bigqk": Workload("h32_n16384_d128_causal_bigqk", 1, 32, 16384, 128,
+                                             torch.bfloat16, True, 4, qk_std=3.0),
+    "b2_h16_n4096_d64_causal_fwdbwd": Workload("b2_h16_n4096_d64_causal_fwdbwd", 2, 16, 4096, 64,
+                                               torch.bfloat16, True, 5, backward=True),
+}
+
+HEADLINE = "b4_h16_n4096_d128_causal"
+
+
+def make_inputs(B: int, H: int, N: int, d: int, dtype: torch.dtype = torch.bfloat16,
+                seed: int = 0, qk_std: float = 1.0, with_dout: bool = False):
+    """Return CPU tensors (q, k, v[, dout]) of shape [B, H, N, d] in ``dtype``."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    shape = (B, H, N, d)
+    q = torch.randn(shape, generator=g, dtype=torch.float32)
+    k = torch.randn(shape, generator=g, dtype=torch.float32)
+    v = torch.randn(shape, generator=g, dtype=torch.float32)
+    dout = torch.randn(shape, generator=g, dtype=torch.float32) if with_dout else None
+    if qk_std != 1.0:
+        q = q * qk_std
+        k = k * qk_std
+    out = [q.to(dtype), k.to(dtype), v.to(dtype)]
+    if with_dout:
+        out.append(dout.to(dtype))
+    return tuple(out)
+
+
+def workload_inputs(w: Workload, with_dout: bool | None = None):
+    if with_dout is None:
+        with_dout = w.backward
+    return make_inputs(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.qk_std, with_dout)

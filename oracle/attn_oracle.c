@@ -1,0 +1,247 @@
+/*
+ * attn_oracle.c - fp64 CPU oracle for scaled-dot-product attention.
+ *
+ * TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT.  Only the test suite, the
+ * smoke check in __graft_entry__.py and the CPU-baseline leg of bench.py may
+ * load this library.  It shares no code, header, table or helper with the HIP
+ * library under tiled_online_softmax_attn_amd/, and it includes nothing from
+ * there.
+ *
+ * What it computes is the plain definition of attention, written out with
+ * the N x N score matrix S and probability matrix P materialised:
+ *
+ *   S = scale * Q K^T                       (CS336 Lecture 5 notes "GPUs, TPUs",
+ *                                            section 8.1; CS149 Lecture 9 notes
+ *                                            "Efficiently Evaluating DNNs on
+ *                                            GPUs", section 8)
+ *   causal: S_ij = -inf for key j > query i  (query i sees keys 0..i)
+ *   P = row softmax of S, with the row maximum subtracted
+ *                                           (CS149 L9 notes section 8; PDC
+ *                                            notes Lecture 4, section 4.13.2)
+ *   O = P V                                 (CS149 L9 notes section 8)
+ *   lse_i = m_i + ln(l_i)                   (CS336 L5 notes section 8.3: the
+ *                                            logsumexp kept for the backward)
+ *
+ * and the exact gradient of sum(dO * O) with respect to Q, K, V, in the terms
+ * of CS336 L5 notes section 8.4 and Exercise 9:
+ *
+ *   dV = P^T dO,  dP = dO V^T,  D_i = sum_k dO_ik O_ik,
+ *   dS = P * (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q.
+ *
+ * Everything is double precision.  Callers widen their inputs exactly (bf16
+ * and fp32 values are exactly representable as doubles).  No blocking, no
+ * online rescaling, no reordering: rows are independent, and OpenMP only
+ * splits the rows of a matrix over threads, which does not change any sum.
+ *
+ * Every function returns 0 on success and a negative value on bad arguments
+ * (-1 null pointer, -2 bad size, -3 allocation failure).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* Safe softmax of one row (CS149 L9 notes section 8; PDC notes 4.13.2):
+ * m = max x, f = exp(x - m), l = sum f, p = f / l.  Entries equal to -inf
+ * (masked) get p = 0.  At least one entry must be finite. */
+int oracle_softmax_row(const double* x, int64_t n, double* p, double* m_out,
+                       double* l_out) {
+  if (!x || !p) return -1;
+  if (n < 1) return -2;
+  double m = -INFINITY;
+  for (int64_t j = 0; j < n; ++j)
+    if (x[j] > m) m = x[j];
+  double l = 0.0;
+  for (int64_t j = 0; j < n; ++j) {
+    p[j] = exp(x[j] - m);
+    l += p[j];
+  }
+  for (int64_t j = 0; j < n; ++j) p[j] = p[j] / l;
+  if (m_out) *m_out = m;
+  if (l_out) *l_out = l;
+  return 0;
+}
+
+/* Score row i: s[j] = scale * <q_i, k_j>, or -inf where the causal mask hides
+ * key j from query i. */
+static void score_row(const double* q, const double* k, int64_t N, int64_t d,
+                      int causal, double scale, int64_t i, double* s) {
+  const double* qi = q + i * d;
+  for (int64_t j = 0; j < N; ++j) {
+    if (causal && j > i) {
+      s[j] = -INFINITY;
+      continue;
+    }
+    const double* kj = k + j * d;
+    double dot = 0.0;
+    for (int64_t c = 0; c < d; ++c) dot += qi[c] * kj[c];
+    s[j] = scale * dot;
+  }
+}
+
+/* Forward for one head.  q, k, v: [N][d]; o: [N][d]; lse: [N].
+ * p_out, if not NULL, receives P as [N][N]. */
+int oracle_attn_fwd_head(const double* q, const double* k, const double* v,
+                         int64_t N, int64_t d, int causal, double scale,
+                         double* o, double* lse, double* p_out) {
+  if (!q || !k || !v || !o || !lse) return -1;
+  if (N < 1 || d < 1) return -2;
+  double* S = (double*)malloc(sizeof(double) * (size_t)N * (size_t)N);
+  double* P = p_out ? p_out : (double*)malloc(sizeof(double) * (size_t)N * (size_t)N);
+  if (!S || !P) {
+    free(S);
+    if (!p_out) free(P);
+    return -3;
+  }
+  /* S = scale * Q K^T (+ mask) */
+#pragma omp parallel for schedule(dynamic, 8)
+  for (int64_t i = 0; i < N; ++i) score_row(q, k, N, d, causal, scale, i, S + i * N);
+  /* P = softmax(S) row by row; lse = m + ln l */
+#pragma omp parallel for schedule(dynamic, 8)
+  for (int64_t i = 0; i < N; ++i) {
+    double m, l;
+    oracle_softmax_row(S + i * N, N, P + i * N, &m, &l);
+    lse[i] = m + log(l);
+  }
+  /* O = P V */
+#pragma omp parallel for schedule(dynamic, 8)
+  for (int64_t i = 0; i < N; ++i) {
+    double* oi = o + i * d;
+    for (int64_t c = 0; c < d; ++c) oi[c] = 0.0;
+    for (int64_t j = 0; j < N; ++j) {
+      const double pij = P[i * N + j];
+      const double* vj = v + j * d;
+      for (int64_t c = 0; c < d; ++c) oi[c] += pij * vj[c];
+    }
+  }
+  free(S);
+  if (!p_out) free(P);
+  return 0;
+}
+
+/* Forward for selected query rows of one head: the same definition, one row
+ * at a time (S row, softmax, P row times V).  rows: nrows query indices in
+ * [0, N); o_rows: [nrows][d]; lse_rows: [nrows]. */
+int oracle_attn_fwd_rows(const double* q, const double* k, const double* v,
+                         int64_t N, int64_t d, int causal, double scale,
+                         const int64_t* rows, int64_t nrows, double* o_rows,
+                         double* lse_rows) {
+  if (!q || !k || !v || !rows || !o_rows || !lse_rows) return -1;
+  if (N < 1 || d < 1 || nrows < 0) return -2;
+  for (int64_t r = 0; r < nrows; ++r)
+    if (rows[r] < 0 || rows[r] >= N) return -2;
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)N);
+    double* p = (double*)malloc(sizeof(double) * (size_t)N);
+    if (!s || !p) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t i = rows[r];
+        double m, l;
+        score_row(q, k, N, d, causal, scale, i, s);
+        oracle_softmax_row(s, N, p, &m, &l);
+        lse_rows[r] = m + log(l);
+        double* orow = o_rows + r * d;
+        for (int64_t c = 0; c < d; ++c) orow[c] = 0.0;
+        for (int64_t j = 0; j < N; ++j) {
+          const double* vj = v + j * d;
+          for (int64_t c = 0; c < d; ++c) orow[c] += p[j] * vj[c];
+        }
+      }
+    }
+    free(s);
+    free(p);
+  }
+  return failed ? -3 : 0;
+}
+
+/* Backward for one head (CS336 L5 notes section 8.4): the exact gradient of
+ * sum(dO * O).  Inputs q, k, v, dout: [N][d].  Outputs dq, dk, dv: [N][d].
+ * o_out [N][d], lse_out [N] and D_out [N], when not NULL, receive the
+ * oracle's own O, lse and D = rowsum(dO * O). */
+int oracle_attn_bwd_head(const double* q, const double* k, const double* v,
+                         const double* dout, int64_t N, int64_t d, int causal,
+                         double scale, double* dq, double* dk, double* dv,
+                         double* o_out, double* lse_out, double* D_out) {
+  if (!q || !k || !v || !dout || !dq || !dk || !dv) return -1;
+  if (N < 1 || d < 1) return -2;
+  const size_t nn = (size_t)N * (size_t)N;
+  double* P = (double*)malloc(sizeof(double) * nn);
+  double* dS = (double*)malloc(sizeof(double) * nn);
+  double* O = (double*)malloc(sizeof(double) * (size_t)N * (size_t)d);
+  double* L = (double*)malloc(sizeof(double) * (size_t)N);
+  double* D = (double*)malloc(sizeof(double) * (size_t)N);
+  if (!P || !dS || !O || !L || !D) {
+    free(P); free(dS); free(O); free(L); free(D);
+    return -3;
+  }
+  int rc = oracle_attn_fwd_head(q, k, v, N, d, causal, scale, O, L, P);
+  if (rc != 0) {
+    free(P); free(dS); free(O); free(L); free(D);
+    return rc;
+  }
+  /* D_i = sum_k dO_ik O_ik */
+  for (int64_t i = 0; i < N; ++i) {
+    double acc = 0.0;
+    for (int64_t c = 0; c < d; ++c) acc += dout[i * d + c] * O[i * d + c];
+    D[i] = acc;
+  }
+  /* dP = dO V^T, then dS = P * (dP - D) */
+#pragma omp parallel for schedule(dynamic, 8)
+  for (int64_t i = 0; i < N; ++i) {
+    for (int64_t j = 0; j < N; ++j) {
+      double dp = 0.0;
+      for (int64_t c = 0; c < d; ++c) dp += dout[i * d + c] * v[j * d + c];
+      dS[i * N + j] = P[i * N + j] * (dp - D[i]);
+    }
+  }
+  /* dQ = scale * dS K */
+#pragma omp parallel for schedule(dynamic, 8)
+  for (int64_t i = 0; i < N; ++i) {
+    for (int64_t c = 0; c < d; ++c) dq[i * d + c] = 0.0;
+    for (int64_t j = 0; j < N; ++j) {
+      const double g = dS[i * N + j];
+      for (int64_t c = 0; c < d; ++c) dq[i * d + c] += g * k[j * d + c];
+    }
+    for (int64_t c = 0; c < d; ++c) dq[i * d + c] *= scale;
+  }
+  /* dK = scale * dS^T Q and dV = P^T dO, one key row j at a time */
+#pragma omp parallel for schedule(dynamic, 8)
+  for (int64_t j = 0; j < N; ++j) {
+    for (int64_t c = 0; c < d; ++c) {
+      dk[j * d + c] = 0.0;
+      dv[j * d + c] = 0.0;
+    }
+    for (int64_t i = 0; i < N; ++i) {
+      const double g = dS[i * N + j];
+      const double pij = P[i * N + j];
+      for (int64_t c = 0; c < d; ++c) {
+        dk[j * d + c] += g * q[i * d + c];
+        dv[j * d + c] += pij * dout[i * d + c];
+      }
+    }
+    for (int64_t c = 0; c < d; ++c) dk[j * d + c] *= scale;
+  }
+  if (o_out) memcpy(o_out, O, sizeof(double) * (size_t)N * (size_t)d);
+  if (lse_out) memcpy(lse_out, L, sizeof(double) * (size_t)N);
+  if (D_out) memcpy(D_out, D, sizeof(double) * (size_t)N);
+  free(P); free(dS); free(O); free(L); free(D);
+  return 0;
+}

@@ -1,0 +1,332 @@
+"""Pins for the fp64 oracle: checks against facts fixed by the pages and by
+mathematics, never against the oracle itself.
+
+Each pin is a function ``pin_xxx(lib)`` that raises AssertionError when the
+oracle library ``lib`` violates it.  ``test_oracle_pins.py`` runs them on the
+real oracle; ``test_oracle_mutants.py`` runs them on copies of the oracle with
+one planted mistake each and requires every copy to fail at least one pin.
+
+What pins what:
+* worked example - CS336 Lecture 5 notes (GPUs, TPUs), Exercise 8: online
+  softmax over [1, 3 | 2, 5] with printed m and l after each block.
+* blocked identities - CS149 Lecture 9 notes (Efficiently Evaluating DNNs on
+  GPUs), section 9: m = max of block maxima, l = sum_b e^{m_b - m} l_b.
+* streaming and blocked loops - PDC notes Lecture 4, section 4.13.3 (one key
+  at a time with a running o) and CS149 L9 notes Example 4 (blocked loops
+  with per-block max and alpha/beta rescale), re-derived here independently;
+  block sizes that do not divide N as CS336 L5 notes Exercise 10 asks.
+* brute force - the textbook formula O_i = sum_j e^{s_ij} V_j / sum_j e^{s_ij}
+  (no max subtraction) in 50-digit decimal arithmetic.
+* closed forms - Q = 0, constant V, causal row 0, N = 1.
+* large logits - PDC notes 4.13.2: e^x overflows for x near 1000 unless the
+  row maximum is subtracted.
+* backward - finite differences of the 50-digit forward; the D identity of
+  CS336 L5 notes Exercise 9; sum_j dV_j = sum_i dO_i; sum_j dK_j = 0.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from decimal import Decimal, getcontext
+
+import numpy as np
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ---------------------------------------------------------------- helpers
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def dec_forward(q, k, v, causal, scale, prec=50):
+    """Textbook attention in Decimal: no max subtraction, no blocking.
+    Returns (O, lse) as nested lists of Decimal."""
+    getcontext().prec = prec
+    N, d = len(q), len(q[0])
+    sc = Decimal(scale)
+    O, lse = [], []
+    for i in range(N):
+        w = []
+        for j in range(N):
+            if causal and j > i:
+                w.append(Decimal(0))
+                continue
+            s = sum((q[i][c] * k[j][c] for c in range(d)), Decimal(0)) * sc
+            w.append(s.exp())
+        Z = sum(w, Decimal(0))
+        O.append([sum((w[j] * v[j][c] for j in range(N)), Decimal(0)) / Z for c in range(d)])
+        lse.append(Z.ln())
+    return O, lse
+
+
+def _to_dec(a):
+    return [[Decimal(float(x)) for x in row] for row in np.asarray(a, dtype=np.float64)]
+
+
+def _assert_close(a, b, rtol, atol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    assert np.all(np.isfinite(a)), f"{what}: non-finite values"
+    err = np.abs(a - b)
+    bound = atol + rtol * np.abs(b)
+    assert np.all(err <= bound), f"{what}: max err {err.max():.3e} (worst excess {(err - bound).max():.3e})"
+
+
+# ---------------------------------------------------------------- forward pins
+def pin_worked_example(lib):
+    """CS336 L5 notes Exercise 8, printed values."""
+    with open(os.path.join(GOLDEN, "online_softmax_ex8.json")) as f:
+        g = json.load(f)
+    x = np.array(g["x"])
+    # block-by-block online update as the notes state it (section 8.2):
+    # m' = max(m, max block), l' = l e^{m - m'} + sum_block e^{x - m'}
+    m, l = -math.inf, 0.0
+    seen = []
+    for lo, hi in g["blocks"]:
+        blk = x[lo:hi]
+        m_new = max(m, float(blk.max()))
+        l = l * math.exp(m - m_new) + float(np.exp(blk - m_new).sum())
+        m = m_new
+        seen.append((m, l))
+    assert seen[0][0] == g["after_block_1"]["m"]
+    assert abs(seen[0][1] - g["after_block_1"]["l"]) < 1e-4
+    assert seen[1][0] == g["after_block_2"]["m"]
+    assert abs(seen[1][1] - g["after_block_2"]["l"]) < 1e-4
+    # the oracle's one-shot softmax must land on the printed final state
+    p, m1, l1 = oracle.softmax_row(x, lib=lib)
+    assert m1 == g["after_block_2"]["m"]
+    assert abs(l1 - g["after_block_2"]["l"]) < 1e-4
+    assert abs(p[3] - g["softmax_of_x4"]["value"]) < 1e-3
+    # and exactly on the online result (same quantity, different order)
+    assert abs(l1 - seen[1][1]) < 1e-15 * 2
+
+
+def pin_blocked_identity(lib):
+    """CS149 L9 notes section 9: merging per-block (m_b, l_b, softmax_b)
+    reproduces the one-shot softmax, for block splits that do not divide n."""
+    rng = _rng(11)
+    for n, cuts in [(37, [5, 17, 30]), (64, [1, 2, 40]), (9, [4]), (100, [33, 66, 99])]:
+        x = rng.normal(0, 4, n)
+        p, m, l = oracle.softmax_row(x, lib=lib)
+        edges = [0] + cuts + [n]
+        parts = [oracle.softmax_row(x[a:b], lib=lib) for a, b in zip(edges[:-1], edges[1:])]
+        m_merged = max(mb for _, mb, _ in parts)
+        l_merged = sum(math.exp(mb - m_merged) * lb for _, mb, lb in parts)
+        assert m_merged == m
+        assert abs(l_merged - l) <= 1e-14 * l
+        f = np.concatenate([pb * lb * math.exp(mb - m_merged) for pb, mb, lb in parts])
+        _assert_close(f / l_merged, p, 1e-14, 1e-300, "blocked softmax")
+        # the plain definition, evaluated directly
+        ref = np.exp(x - x.max()) / np.exp(x - x.max()).sum()
+        _assert_close(p, ref, 1e-14, 1e-300, "softmax definition")
+
+
+def _stream_one_key(q, k, v, causal, scale):
+    """PDC notes 4.13.3: keys one at a time with a running (m, l, o)."""
+    N, d = q.shape
+    O = np.zeros((N, d))
+    for i in range(N):
+        m, l, o = -math.inf, 0.0, np.zeros(d)
+        for j in range(N if not causal else i + 1):
+            x = scale * float(q[i] @ k[j])
+            m_new = max(m, x)
+            l = l * math.exp(m - m_new) + math.exp(x - m_new)
+            o = o * math.exp(m - m_new) + math.exp(x - m_new) * v[j]
+            m = m_new
+        O[i] = o / l
+    return O
+
+
+def _blocked_alpha_beta(q, k, v, causal, scale, bq, bk):
+    """CS149 L9 notes Example 4 structure: Q blocks outside, K/V blocks
+    inside, per-block max and alpha/beta rescale, normalise at the end."""
+    N, d = q.shape
+    O = np.zeros((N, d))
+    m_run = np.full(N, -np.inf)
+    l_run = np.zeros(N)
+    for i0 in range(0, N, bq):
+        qi = q[i0:i0 + bq]
+        rows = np.arange(i0, min(N, i0 + bq))
+        for j0 in range(0, N, bk):
+            cols = np.arange(j0, min(N, j0 + bk))
+            s = scale * (qi @ k[j0:j0 + bk].T)
+            if causal:
+                s = np.where(cols[None, :] > rows[:, None], -np.inf, s)
+            m_blk = s.max(axis=1)
+            live = np.isfinite(m_blk)
+            m_blk_safe = np.where(live, m_blk, 0.0)
+            p = np.where(live[:, None], np.exp(s - m_blk_safe[:, None]), 0.0)
+            l_blk = p.sum(axis=1)
+            m_new = np.maximum(m_run[rows], np.where(live, m_blk, -np.inf))
+            alpha = np.where(np.isfinite(m_run[rows]), np.exp(m_run[rows] - m_new), 0.0)
+            beta = np.where(live, np.exp(m_blk_safe - m_new), 0.0)
+            O[rows] = O[rows] * alpha[:, None] + (p * beta[:, None]) @ v[j0:j0 + bk]
+            l_run[rows] = l_run[rows] * alpha + l_blk * beta
+            m_run[rows] = m_new
+    return O / l_run[:, None], m_run + np.log(l_run)
+
+
+def pin_streaming_and_blocked(lib):
+    rng = _rng(12)
+    for N, d, causal in [(23, 5, False), (23, 5, True), (40, 8, True), (7, 3, False)]:
+        q, k, v = rng.normal(size=(3, N, d))
+        scale = 1 / math.sqrt(d)
+        o, lse = oracle.attn_fwd(q, k, v, causal, scale, lib=lib)
+        _assert_close(_stream_one_key(q, k, v, causal, scale), o, 1e-12, 1e-13, "streaming")
+        for bq, bk in [(4, 4), (5, 7), (16, 3), (N, N), (1, 1)]:
+            ob, lb = _blocked_alpha_beta(q, k, v, causal, scale, bq, bk)
+            _assert_close(ob, o, 1e-12, 1e-13, f"blocked {bq}x{bk}")
+            _assert_close(lb, lse, 1e-13, 1e-13, f"blocked lse {bq}x{bk}")
+
+
+def pin_rows_sum_to_one(lib):
+    rng = _rng(13)
+    for causal in (False, True):
+        q, k, v = rng.normal(size=(3, 2, 33, 6))
+        o, lse, p = oracle.attn_fwd(q, k, v, causal, 0.4, return_p=True, lib=lib)
+        assert np.all(p >= 0)
+        _assert_close(p.sum(-1), np.ones((2, 33)), 1e-13, 0, "row sums")
+        if causal:
+            assert np.all(np.triu(p, 1) == 0), "causal P must vanish above the diagonal"
+        # O is P V (definition) and lse = ln sum exp(s)
+        _assert_close(o, p @ v, 1e-12, 1e-13, "O = P V")
+
+
+def pin_constant_v(lib):
+    rng = _rng(14)
+    for causal in (False, True):
+        q, k = rng.normal(size=(2, 29, 7))
+        c = rng.normal(size=7)
+        v = np.tile(c, (29, 1))
+        o, _ = oracle.attn_fwd(q, k, v, causal, 0.3, lib=lib)
+        _assert_close(o, np.tile(c, (29, 1)), 1e-13, 1e-13, "constant V")
+
+
+def pin_q_zero(lib):
+    rng = _rng(15)
+    N, d = 31, 4
+    k, v = rng.normal(size=(2, N, d))
+    q = np.zeros((N, d))
+    o, lse = oracle.attn_fwd(q, k, v, False, 0.5, lib=lib)
+    _assert_close(o, np.tile(v.mean(0), (N, 1)), 1e-13, 1e-13, "Q=0 mean")
+    _assert_close(lse, np.full(N, math.log(N)), 1e-14, 0, "Q=0 lse")
+    o, lse = oracle.attn_fwd(q, k, v, True, 0.5, lib=lib)
+    prefix = np.cumsum(v, axis=0) / np.arange(1, N + 1)[:, None]
+    _assert_close(o, prefix, 1e-13, 1e-13, "Q=0 causal prefix mean")
+    _assert_close(lse, np.log(np.arange(1, N + 1)), 1e-14, 1e-15, "Q=0 causal lse")
+
+
+def pin_row0_and_single_key(lib):
+    rng = _rng(16)
+    q, k, v = rng.normal(size=(3, 12, 5))
+    o, lse = oracle.attn_fwd(q, k, v, True, 0.7, lib=lib)
+    _assert_close(o[0], v[0], 0, 0, "causal row 0")
+    assert abs(lse[0] - 0.7 * float(q[0] @ k[0])) < 1e-14
+    o, lse = oracle.attn_fwd(q[:1], k[:1], v[:1], False, 0.7, lib=lib)
+    _assert_close(o[0], v[0], 0, 0, "N=1")
+    assert abs(lse[0] - 0.7 * float(q[0] @ k[0])) < 1e-14
+
+
+def pin_brute_force(lib):
+    rng = _rng(17)
+    for N, d, causal, spread in [(5, 3, False, 1.0), (6, 4, True, 2.0), (4, 2, False, 3.0),
+                                 (6, 3, True, 1.0), (1, 4, True, 1.0)]:
+        q, k, v = rng.normal(0, spread, size=(3, N, d))
+        scale = 1 / math.sqrt(d)
+        o, lse = oracle.attn_fwd(q, k, v, causal, scale, lib=lib)
+        Od, Ld = dec_forward(_to_dec(q), _to_dec(k), _to_dec(v), causal, scale)
+        _assert_close(o, np.array([[float(x) for x in r] for r in Od]), 1e-13, 1e-14, "brute O")
+        _assert_close(lse, np.array([float(x) for x in Ld]), 1e-14, 1e-14, "brute lse")
+
+
+def pin_large_logits(lib):
+    """Logits near +-1000 (PDC notes 4.13.2) and the large-logit workload
+    regime (Q, K ~ N(0, 9)): finite results equal to 50-digit brute force."""
+    rng = _rng(18)
+    for N, d, causal, qs in [(6, 4, False, 40.0), (6, 4, True, 40.0), (5, 8, False, 3.0)]:
+        q = rng.normal(0, qs, size=(N, d))
+        k = rng.normal(0, qs, size=(N, d))
+        v = rng.normal(size=(N, d))
+        scale = 1 / math.sqrt(d)
+        o, lse = oracle.attn_fwd(q, k, v, causal, scale, lib=lib)
+        assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+        Od, Ld = dec_forward(_to_dec(q), _to_dec(k), _to_dec(v), causal, scale)
+        _assert_close(o, np.array([[float(x) for x in r] for r in Od]), 1e-12, 1e-12, "large O")
+        _assert_close(lse, np.array([float(x) for x in Ld]), 1e-14, 1e-12, "large lse")
+
+
+def pin_rows_entry(lib):
+    """The row-sampled entry point returns the head entry point's rows."""
+    rng = _rng(19)
+    for causal in (False, True):
+        q, k, v = rng.normal(size=(3, 50, 6))
+        o, lse = oracle.attn_fwd(q, k, v, causal, 0.35, lib=lib)
+        rows = np.array([49, 0, 17, 3, 3, 31])
+        orow, lrow = oracle.attn_fwd_rows(q, k, v, causal, 0.35, rows, lib=lib)
+        _assert_close(orow, o[rows], 0, 0, "rows O")
+        _assert_close(lrow, lse[rows], 0, 0, "rows lse")
+
+
+# ---------------------------------------------------------------- backward pins
+def pin_bwd_finite_differences(lib):
+    """Gradient of L = sum(dO * O) by central differences of the 50-digit
+    forward (independent of the oracle's forward and backward)."""
+    rng = _rng(20)
+    h = Decimal("1e-15")
+    for N, d, causal in [(4, 3, False), (5, 2, True), (3, 4, True)]:
+        q, k, v, do = rng.normal(size=(4, N, d))
+        scale = 1 / math.sqrt(d)
+        g = oracle.attn_bwd(q, k, v, do, causal, scale, lib=lib)
+        base = {"q": _to_dec(q), "k": _to_dec(k), "v": _to_dec(v)}
+        dod = _to_dec(do)
+
+        def loss(t):
+            O, _ = dec_forward(t["q"], t["k"], t["v"], causal, scale)
+            return sum((O[i][c] * dod[i][c] for i in range(N) for c in range(d)), Decimal(0))
+
+        for name in ("q", "k", "v"):
+            fd = np.zeros((N, d))
+            for i in range(N):
+                for c in range(d):
+                    t = {n: [row[:] for row in a] for n, a in base.items()}
+                    t[name][i][c] = base[name][i][c] + h
+                    lp = loss(t)
+                    t[name][i][c] = base[name][i][c] - h
+                    lm = loss(t)
+                    fd[i, c] = float((lp - lm) / (2 * h))
+            _assert_close(g["d" + name], fd, 1e-10, 1e-12, f"finite differences d{name}")
+
+
+def pin_bwd_D_identity(lib):
+    """CS336 L5 notes Exercise 9: sum_j P_ij dP_ij = sum_k dO_ik O_ik."""
+    rng = _rng(21)
+    for causal in (False, True):
+        q, k, v, do = rng.normal(size=(4, 37, 8))
+        g = oracle.attn_bwd(q, k, v, do, causal, 0.3, lib=lib)
+        _, _, p = oracle.attn_fwd(q, k, v, causal, 0.3, return_p=True, lib=lib)
+        dP = do @ v.T
+        _assert_close(g["D"], (p * dP).sum(-1), 1e-12, 1e-12, "D identity")
+        _assert_close(g["D"], (do * g["o"]).sum(-1), 1e-12, 1e-12, "D definition")
+
+
+def pin_bwd_invariants(lib):
+    """Rows of P sum to 1, so sum_j dV_j = sum_i dO_i; softmax is shift
+    invariant along a row, so each row of dS sums to 0 and sum_j dK_j = 0."""
+    rng = _rng(22)
+    for causal in (False, True):
+        q, k, v, do = rng.normal(size=(4, 45, 6))
+        g = oracle.attn_bwd(q, k, v, do, causal, 0.4, lib=lib)
+        _assert_close(g["dv"].sum(0), do.sum(0), 1e-12, 1e-12, "sum dV")
+        _assert_close(g["dk"].sum(0), np.zeros(6), 0, 1e-12 * np.abs(g["dk"]).sum(), "sum dK")
+
+
+FORWARD_PINS = [pin_worked_example, pin_blocked_identity, pin_streaming_and_blocked,
+                pin_rows_sum_to_one, pin_constant_v, pin_q_zero, pin_row0_and_single_key,
+                pin_brute_force, pin_large_logits, pin_rows_entry]
+BACKWARD_PINS = [pin_bwd_finite_differences, pin_bwd_D_identity, pin_bwd_invariants]
+ALL_PINS = FORWARD_PINS + BACKWARD_PINS

@@ -1,0 +1,57 @@
+"""Planted mistakes in copies of the oracle must each fail a pin (CPU only).
+
+Each mutant is the oracle's C source with one plausible mistake put in by a
+text substitution (a dropped term, a wrong sign, a wrong index, a
+transposed operand, an off-by-one mask), built with gcc into a temporary
+directory.  The real oracle source is never modified.  A mutant that passes
+every pin would mean the pins leave that part of the oracle unchecked.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "attn_oracle.c")
+
+MUTANTS = {
+    "no_max_subtraction": ("p[j] = exp(x[j] - m);", "p[j] = exp(x[j]);"),
+    "mask_off_by_one": ("if (causal && j > i) {", "if (causal && j >= i && j > 0) {"),
+    "mask_dropped": ("if (causal && j > i) {", "if (0) {"),
+    "scale_dropped": ("s[j] = scale * dot;", "s[j] = dot;"),
+    "lse_without_max": ("lse[i] = m + log(l);", "lse[i] = log(l);"),
+    "lse_log2": ("lse[i] = m + log(l);", "lse[i] = m + log2(l);"),
+    "pv_wrong_row": ("const double* vj = v + j * d;\n      for (int64_t c = 0; c < d; ++c) oi[c]",
+                     "const double* vj = v + i * d;\n      for (int64_t c = 0; c < d; ++c) oi[c]"),
+    "no_normalisation": ("for (int64_t j = 0; j < n; ++j) p[j] = p[j] / l;", ""),
+    "ds_sign": ("dS[i * N + j] = P[i * N + j] * (dp - D[i]);", "dS[i * N + j] = P[i * N + j] * (dp + D[i]);"),
+    "ds_no_D": ("dS[i * N + j] = P[i * N + j] * (dp - D[i]);", "dS[i * N + j] = P[i * N + j] * dp;"),
+    "dq_no_scale": ("    for (int64_t c = 0; c < d; ++c) dq[i * d + c] *= scale;\n", ""),
+    "dk_transposed": ("const double g = dS[i * N + j];\n      const double pij",
+                      "const double g = dS[j * N + i];\n      const double pij"),
+    "dv_uses_dS": ("dv[j * d + c] += pij * dout[i * d + c];", "dv[j * d + c] += g * dout[i * d + c];"),
+    "D_uses_V": ("acc += dout[i * d + c] * O[i * d + c];", "acc += dout[i * d + c] * v[i * d + c];"),
+    "dq_uses_V": ("dq[i * d + c] += g * k[j * d + c];", "dq[i * d + c] += g * v[j * d + c];"),
+    "rows_wrong_index": ("const int64_t i = rows[r];", "const int64_t i = r;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mut = tmp_path / f"mut_{name}.c"
+    mut.write_text(src.replace(old, new))
+    so = str(tmp_path / f"libmut_{name}.so")
+    oracle.build(str(mut), so)
+    lib = oracle.load(so)
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, RuntimeError, FloatingPointError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"
