@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Throughput of the fused attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+the forward (attn_fwd: O and lse) and the backward (attn_bwd's three phases:
+preprocess D, main, dQ convert) on the causal B=4 H=16 N=4096 d=128 bf16
+workload.  Inputs are generated on the host from a fixed seed, copied to the
+GPU, and resident in HBM before the timed region starts.
+
+Prints ONE JSON line.  `value` is fwd+bwd TFLOP/s by the formula
+4*B*H*N^2*d (halved for causal) for the forward plus 2.5x that for the
+backward, over the K timed steps.  `roofline` describes the kernel with the
+largest share of the step time, timed live with HIP events recorded on the
+stream the kernels run on.  `cpu_baseline` times the fp64 CPU oracle on a
+bounded sample of the same workload (whole heads, forward + backward).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+KERNELS = ("fwd", "bwd_preprocess", "bwd_main", "bwd_dq_convert")
+CSRC = os.path.join(ROOT, "tiled_online_softmax_attn_amd", "csrc")
+KERNEL_SOURCES = {"fwd": "attn_fwd.hip", "bwd_preprocess": "attn_bwd.hip",
+                  "bwd_main": "attn_bwd.hip", "bwd_dq_convert": "attn_bwd.hip"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def eprint(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest(kernel: str) -> str:
+    h = hashlib.sha256()
+    for name in (KERNEL_SOURCES[kernel], "device_common.h"):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel source changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        e = t[workload][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if e.get("source_digest") != source_digest(kernel):
+        return None
+    return e["fetch_bytes"] + e["write_bytes"]
+
+
+def algorithmic(w, kernel: str):
+    """(amount, unit, bound) per launch: FLOPs for the MFMA kernels, bytes for
+    the memory-bound helpers."""
+    BHN = w.B * w.H * w.N
+    if kernel == "fwd":
+        return w.fwd_flops(), "flop", "mfma"
+    if kernel == "bwd_main":
+        return w.bwd_flops(), "flop", "mfma"
+    if kernel == "bwd_preprocess":  # read O, dO (bf16); write D (fp32), zero dQ acc (fp32)
+        return BHN * w.d * 2 * 2 + BHN * 4 + BHN * w.d * 4, "byte", "hbm"
+    # convert: read dQ acc (fp32), write dQ (bf16)
+    return BHN * w.d * 4 + BHN * w.d * 2, "byte", "hbm"
+
+
+def cpu_baseline(w, q, k, v, do, budget_s: float):
+    import numpy as np
+
+    import oracle
+    lib = oracle.load()
+    scale = float(np.float32(w.scale))
+    f64 = lambda t: t.to("cpu").double().numpy()
+    heads, t0 = 0, time.perf_counter()
+    per_head = (w.fwd_flops() + w.bwd_flops()) / (w.B * w.H)
+    for b in range(w.B):
+        for h in range(w.H):
+            qh, kh, vh, dh = f64(q[b, h]), f64(k[b, h]), f64(v[b, h]), f64(do[b, h])
+            oracle.attn_fwd(qh, kh, vh, w.causal, scale, lib=lib)
+            oracle.attn_bwd(qh, kh, vh, dh, w.causal, scale, lib=lib)
+            heads += 1
+            eprint(f"[cpu_baseline] oracle head {heads}: {time.perf_counter() - t0:.1f} s")
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        else:
+            continue
+        break
+    el = time.perf_counter() - t0
+    return {"value": per_head * heads / el / 1e12, "unit": "TFLOP/s",
+            "cores": oracle.num_threads(lib), "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} heads of {w.name} (fp64 forward + backward per "
+                      f"head, S and P materialised), {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None, help="workload name (default: the headline)")
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        eprint("bench.py: this build runs on exactly one GPU; multi-GPU runs are not "
+               "supported (heads would shard across GPUs with no exchange).")
+        sys.exit(2)
+
+    import torch
+
+    import tiled_online_softmax_attn_amd as T
+    from attn_inputs import HEADLINE, WORKLOADS, workload_inputs
+
+    w = WORKLOADS[args.workload or HEADLINE]
+    if not torch.cuda.is_available():
+        eprint("bench.py needs a GPU")
+        sys.exit(1)
+    T.lib()
+    dev = torch.device("cuda:0")
+    eprint(f"[bench] generating inputs for {w.name}")
+    q, k, v, do = workload_inputs(w, with_dout=True)
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    B, H, N, d = w.B, w.H, w.N, w.d
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, N), device=dev, dtype=torch.float32)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    ws = torch.empty(T.attn_bwd_workspace_bytes(B, H, N, d, w.dtype), device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        if events is not None:
+            events[0].record(stream)
+        T.attn_fwd(qd, kd, vd, o, lse, w.causal, w.scale, stream)
+        if events is not None:
+            events[1].record(stream)
+        for ph in range(3):
+            T.attn_bwd_phase(ph, qd, kd, vd, o, dod, lse, dq, dk, dv, ws, w.causal, w.scale,
+                             stream)
+            if events is not None:
+                events[2 + ph].record(stream)
+
+    eprint(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    eprint(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_kernel_ms = {kn: 0.0 for kn in KERNELS}
+    for e in evs:
+        for i, kn in enumerate(KERNELS):
+            per_kernel_ms[kn] += e[i].elapsed_time(e[i + 1])
+    event_total_ms = evs[0][0].elapsed_time(evs[-1][-1])
+    ms_per_step = wall * 1e3 / args.steps
+    flops_step = w.fwd_flops() + w.bwd_flops()
+    value = flops_step * args.steps / wall / 1e12
+
+    kernels = {}
+    for kn in KERNELS:
+        avg_ms = per_kernel_ms[kn] / args.steps
+        amount, unit, bound = algorithmic(w, kn)
+        if unit == "flop":
+            achieved, peak, u = amount / (avg_ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+        else:
+            achieved, peak, u = amount / (avg_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+        kernels[kn] = {"avg_ms": round(avg_ms, 5), "bound": bound, "achieved": round(achieved, 2),
+                       "peak": peak, "unit": u, "frac": round(achieved / peak, 4),
+                       "traffic": measured_traffic(kn, w.name)}
+    dominant = max(KERNELS, key=lambda kn: per_kernel_ms[kn])
+    dk_ = kernels[dominant]
+    roofline = {"kernel": dominant, "bound": dk_["bound"], "achieved": dk_["achieved"],
+                "peak": dk_["peak"], "unit": dk_["unit"], "frac": dk_["frac"],
+                "traffic": dk_["traffic"]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        eprint("[bench] timing the oracle on the host")
+        cpu = cpu_baseline(w, q, k, v, do, args.cpu_baseline_seconds)
+
+    fwd_ms = kernels["fwd"]["avg_ms"]
+    bwd_ms = sum(kernels[kn]["avg_ms"] for kn in KERNELS[1:])
+    out = {
+        "metric": "fused attention fwd/bwd TFLOP/s + % bf16 MFMA peak, causal B4 H16 N4096 d128",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q, K, V, dO)",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
+                   "step": "forward + backward"},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": round(w.fwd_flops() / (fwd_ms * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(w.bwd_flops() / (bwd_ms * 1e-3) / 1e12, 2),
+        "event_ms_per_step": round(event_total_ms / args.steps, 4),
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

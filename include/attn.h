@@ -1,0 +1,126 @@
+/*
+ * attn.h - C ABI of the MI355X (gfx950) fused attention library (libattn.so).
+ *
+ * The operation is scaled-dot-product attention computed with blocked online
+ * softmax, never materialising the N x N score matrix:
+ *
+ *   forward   O = softmax(scale * Q K^T [+ causal mask]) V  and, per query
+ *             row, the natural-log logsumexp lse_i = ln sum_j e^{scale q_i.k_j}
+ *             over the keys the row sees.  (CS336 Lecture 5 notes "GPUs,
+ *             TPUs", sections 8.1-8.3; CS149 Lecture 9 notes "Efficiently
+ *             Evaluating DNNs on GPUs", sections 8-9; PDC notes Lecture 4,
+ *             sections 4.8 and 4.13.)
+ *   backward  from Q, K, V, O, lse and dO, recomputes P = e^{scale*S - lse}
+ *             block by block and returns dQ, dK, dV of sum(dO * O), with
+ *             D_i = rowsum(dO_i * O_i).  (CS336 L5 notes section 8.4 and
+ *             Exercise 9.)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors are DEVICE pointers to contiguous row-major arrays.  Q, K, V, O,
+ *   dO, dQ, dK, dV have shape [B][H][N][d] (a head's rows are tokens); lse is
+ *   float32 [B][H][N].  Element type is given by `dtype`; lse is always fp32.
+ * - Q, K and V all have the same N (self-attention).  `causal` != 0 hides key
+ *   j from query i when j > i (the diagonal is visible).  `scale` multiplies
+ *   Q K^T before the softmax; pass 1/sqrt(d) for the usual scaling.
+ * - N may be any value >= 1 (no tile multiple is required); d must be 64 or
+ *   128.  bf16 is supported by every entry point; fp32 by the forward only.
+ * - The caller owns every buffer (including the backward workspace).  The
+ *   library never allocates, frees or synchronises; it enqueues kernels on
+ *   `stream` (a hipStream_t, NULL = the default stream) and returns.  Results
+ *   are ready when that stream is synchronised.  Execution errors inside a
+ *   kernel surface at that synchronisation, not in the return code.
+ * - Arguments are validated on the host before anything is enqueued; on a
+ *   non-zero return nothing was written.  Outputs must not alias inputs.
+ * - All pointers must be 16-byte aligned (the kernels use 128-bit accesses).
+ * - Calls are thread-safe: the library keeps no per-call global state.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of Q, K, V, O, dO, dQ, dK, dV. */
+typedef enum {
+  ATTN_DTYPE_F32 = 0,  /* float32 storage; the arithmetic is fp32 */
+  ATTN_DTYPE_BF16 = 1  /* bfloat16 storage; bf16 MFMA with fp32 accumulation */
+} attn_dtype_t;
+
+/* Return codes. */
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = -1,      /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = -2,     /* B, H or N < 1, or sizes overflow 64-bit offsets */
+  ATTN_ERR_DTYPE = -3,     /* unknown dtype, or dtype not supported by this entry point */
+  ATTN_ERR_HEADDIM = -4,   /* d is not 64 or 128 */
+  ATTN_ERR_ALIGN = -5,     /* a pointer is not 16-byte aligned */
+  ATTN_ERR_SCALE = -6,     /* scale is not finite */
+  ATTN_ERR_WORKSPACE = -7, /* workspace NULL or smaller than attn_bwd_workspace_bytes() */
+  ATTN_ERR_HIP = -8        /* the HIP runtime refused a launch */
+} attn_status_t;
+
+/* Forward pass (CS336 L5 notes section 8.3).
+ *   q, k, v : [B][H][N][d] in `dtype`, read only.
+ *   o       : [B][H][N][d] in `dtype`, written: softmax(scale*QK^T [mask]) V.
+ *   lse     : [B][H][N] float32, written: per-row natural-log logsumexp of
+ *             the scaled, masked scores.
+ *   dtype   : ATTN_DTYPE_BF16 or ATTN_DTYPE_F32.
+ *   stream  : hipStream_t to enqueue on (NULL = default stream).
+ * Returns ATTN_OK or an attn_status_t error code. */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int N, int d, int causal, float scale, int dtype,
+             void* stream);
+
+/* Bytes of device workspace attn_bwd needs for these sizes: the D vector
+ * (B*H*N fp32) followed by a dQ fp32 accumulator (B*H*N*d fp32), each
+ * 256-byte aligned.  Returns 0 for invalid sizes. */
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int d, int dtype);
+
+/* Backward pass (CS336 L5 notes section 8.4): recomputes attention from the
+ * saved logsumexp and returns the gradients of sum(dout * O).
+ *   q, k, v     : forward inputs, [B][H][N][d] in `dtype`.
+ *   o, lse      : the forward outputs for those inputs (o in `dtype`, lse
+ *                 float32 [B][H][N]), as attn_fwd wrote them.
+ *   dout        : [B][H][N][d] in `dtype`, the gradient flowing into O.
+ *   dq, dk, dv  : [B][H][N][d] in `dtype`, written.
+ *   workspace   : device scratch of at least attn_bwd_workspace_bytes()
+ *                 bytes, owned by the caller; contents on entry are ignored.
+ *   dtype       : ATTN_DTYPE_BF16 only (ATTN_ERR_DTYPE otherwise).
+ * Calls that share a workspace must not overlap in time.
+ * Returns ATTN_OK or an attn_status_t error code. */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o,
+             const void* dout, const float* lse, void* dq, void* dk, void* dv,
+             void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+             int causal, float scale, int dtype, void* stream);
+
+/* One phase of attn_bwd, for callers that schedule or time the phases
+ * separately.  attn_bwd(...) is exactly phases 0, 1, 2 in this order on one
+ * stream, with the same arguments:
+ *   0  preprocess: D = rowsum(dO * O) into the workspace; zero the dQ
+ *      accumulator (CS336 L5 notes section 8.4 and Exercise 9)
+ *   1  main: recompute P per block and accumulate dK, dV (written) and dQ
+ *      (fp32 accumulator in the workspace)
+ *   2  convert: dq = bf16(dQ accumulator)
+ * A phase reads what the earlier phases left in the workspace; running them
+ * out of order gives undefined results (no fault).  Errors as attn_bwd, plus
+ * ATTN_ERR_SHAPE for a phase outside 0..2. */
+int attn_bwd_phase(int phase, const void* q, const void* k, const void* v, const void* o,
+                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                   void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                   int causal, float scale, int dtype, void* stream);
+
+/* Static, human-readable text for a return code (never NULL). */
+const char* attn_status_str(int status);
+
+/* Library ABI version; bumped when a signature changes. */
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

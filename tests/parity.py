@@ -1,0 +1,107 @@
+"""Shared helpers for the GPU parity tests: run the HIP path through the C
+ABI, run the fp64 oracle on the same seeded inputs, compare.
+
+Tolerances (stated by the benchmark spec for this path):
+* fp32 inputs: max |gpu - oracle| <= 1e-5 on O and lse;
+* bf16 inputs: elementwise |gpu - oracle| <= 2e-2 + 1e-2 * |oracle| on O, lse,
+  dQ, dK and dV (absolute 2e-2 plus relative 1e-2, the allclose reading).
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import tiled_online_softmax_attn_amd as T
+
+BF16_ATOL, BF16_RTOL = 2e-2, 1e-2
+F32_ATOL = 1e-5
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def f32_scale(scale: float) -> float:
+    """The scale the kernels receive (a float32), widened for the oracle."""
+    return float(np.float32(scale))
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def compare(gpu, ref, dtype: torch.dtype, what: str) -> dict:
+    """Assert the stated tolerance; return the error summary."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape, f"{what}: shape {gpu.shape} vs {ref.shape}"
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite GPU values"
+    err = np.abs(gpu - ref)
+    max_abs = float(err.max()) if err.size else 0.0
+    max_rel = float((err / np.maximum(np.abs(ref), 1e-6)).max()) if err.size else 0.0
+    if dtype == torch.float32:
+        assert max_abs <= F32_ATOL, f"{what}: max abs err {max_abs:.3e} > {F32_ATOL}"
+    else:
+        bound = BF16_ATOL + BF16_RTOL * np.abs(ref)
+        bad = err > bound
+        assert not bad.any(), (f"{what}: {int(bad.sum())} of {err.size} elements outside "
+                               f"2e-2 + 1e-2|ref| (max abs {max_abs:.3e})")
+    return {"max_abs": max_abs, "max_rel": max_rel}
+
+
+def gpu_forward(q, k, v, causal, scale):
+    """q, k, v: CPU tensors [B,H,N,d]. Returns CPU (o, lse)."""
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    B, H, N, d = q.shape
+    o = torch.full_like(qd, float("nan"))
+    lse = torch.full((B, H, N), float("nan"), device=dev, dtype=torch.float32)
+    T.attn_fwd(qd, kd, vd, o, lse, causal, scale)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def gpu_backward(q, k, v, o, lse, dout, causal, scale):
+    """All CPU tensors in; runs attn_bwd on the GPU; returns CPU dq, dk, dv."""
+    dev = torch.device("cuda:0")
+    B, H, N, d = q.shape
+    args = [t.to(dev) for t in (q, k, v, o, dout)]
+    lse_d = lse.to(dev)
+    ws = torch.full((T.attn_bwd_workspace_bytes(B, H, N, d),), 0xFF, device=dev, dtype=torch.uint8)
+    dq, dk, dv = (torch.full_like(args[0], float("nan")) for _ in range(3))
+    T.attn_bwd(args[0], args[1], args[2], args[3], args[4], lse_d, dq, dk, dv, ws, causal, scale)
+    torch.cuda.synchronize()
+    return dq.cpu(), dk.cpu(), dv.cpu()
+
+
+def sample_rows(N: int, n_random: int, seed: int) -> np.ndarray:
+    """Query rows to check at full size: both ends, tile edges, random."""
+    fixed = {0, 1, 2, N - 1, N - 2, N // 2}
+    for t in (63, 64, 65, 127, 128, 129, 255, 256):
+        if t < N:
+            fixed.add(t)
+    rng = np.random.default_rng(seed)
+    rnd = rng.integers(0, N, size=n_random)
+    return np.array(sorted(fixed | set(int(x) for x in rnd)), dtype=np.int64)
+
+
+def oracle_full_fwd(q, k, v, causal, scale):
+    return oracle.attn_fwd(to_np(q), to_np(k), to_np(v), causal, f32_scale(scale))
+
+
+def oracle_rows_fwd(q, k, v, causal, scale, b, h, rows):
+    return oracle.attn_fwd_rows(to_np(q[b, h]), to_np(k[b, h]), to_np(v[b, h]), causal,
+                                f32_scale(scale), rows)
+
+
+def describe(err: dict) -> str:
+    return f"max_abs={err['max_abs']:.3e} max_rel={err['max_rel']:.3e}"
+
+
+__all__ = ["compare", "gpu_forward", "gpu_backward", "sample_rows", "oracle_full_fwd",
+           "oracle_rows_fwd", "to_np", "f32_scale", "log", "describe", "math"]

@@ -1,0 +1,107 @@
+"""The C-ABI library loads and exports every entry point include/attn.h
+declares; host-side argument validation (no GPU work is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\**\s+\**(attn_[a-z_0-9]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def _lib():
+    import tiled_online_softmax_attn_amd as T
+    try:
+        return T.lib()
+    except T.AttnLibraryMissing:
+        pytest.skip("libattn.so not built (run __graft_entry__.build())")
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == sorted(["attn_fwd", "attn_bwd", "attn_bwd_phase",
+                                           "attn_bwd_workspace_bytes", "attn_status_str",
+                                           "attn_abi_version"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libattn.so does not export {name}"
+    import tiled_online_softmax_attn_amd as T
+    assert set(T.EXPORTS) == set(declared_functions())
+
+
+def test_status_strings_and_version():
+    lib = _lib()
+    assert lib.attn_abi_version() == 1
+    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, 12345]:
+        s = lib.attn_status_str(code)
+        assert isinstance(s, bytes) and len(s) > 0
+
+
+def test_workspace_size():
+    lib = _lib()
+    B, H, N, d = 2, 16, 4096, 64
+    n = lib.attn_bwd_workspace_bytes(B, H, N, d, 1)
+    need = B * H * N * 4 + B * H * N * d * 4
+    assert need <= n <= need + 512
+    assert lib.attn_bwd_workspace_bytes(0, 1, 1, 64, 1) == 0
+    assert lib.attn_bwd_workspace_bytes(1, 1, 1, 96, 1) == 0
+    assert lib.attn_bwd_workspace_bytes(1, 1, 1, 64, 0) == 0  # fp32 backward unsupported
+
+
+# Validation returns before anything touches the GPU, so these run anywhere.
+FAKE = 1 << 20  # a 16-byte aligned non-null address, never dereferenced on error paths
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(q=0), -1), (dict(lse=0), -1),
+    (dict(B=0), -2), (dict(H=-1), -2), (dict(N=0), -2),
+    (dict(d=96), -4), (dict(d=32), -4),
+    (dict(dtype=7), -3),
+    (dict(q=FAKE + 8), -5), (dict(o=FAKE + 2), -5),
+    (dict(scale=float("inf")), -6), (dict(scale=float("nan")), -6),
+])
+def test_fwd_validation(args, code):
+    lib = _lib()
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, N=16, d=64, causal=0,
+             scale=0.125, dtype=1, stream=None)
+    a.update(args)
+    rc = lib.attn_fwd(a["q"] or None, a["k"], a["v"], a["o"], a["lse"] or None, a["B"], a["H"],
+                      a["N"], a["d"], a["causal"], a["scale"], a["dtype"], a["stream"])
+    assert rc == code
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(dout=0), -1), (dict(dtype=0), -3), (dict(N=0), -2), (dict(d=80), -4),
+    (dict(ws=0), -7), (dict(ws_bytes=16), -7), (dict(dk=FAKE + 4), -5),
+    (dict(scale=float("-inf")), -6),
+])
+def test_bwd_validation(args, code):
+    lib = _lib()
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, dout=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+             ws=FAKE, ws_bytes=1 << 30, B=1, H=1, N=16, d=64, causal=1, scale=0.125, dtype=1)
+    a.update(args)
+    rc = lib.attn_bwd(*(a[n] or None for n in ("q", "k", "v", "o", "dout", "lse", "dq", "dk",
+                                               "dv", "ws")),
+                      a["ws_bytes"], a["B"], a["H"], a["N"], a["d"], a["causal"], a["scale"],
+                      a["dtype"], None)
+    assert rc == code
+
+
+def test_bwd_phase_validation():
+    lib = _lib()
+    args = [FAKE] * 10 + [1 << 30, 1, 1, 16, 64, 1, 0.125, 1, None]
+    assert lib.attn_bwd_phase(3, *args) == -2
+    assert lib.attn_bwd_phase(-1, *args) == -2
+    bad = list(args)
+    bad[9] = None  # workspace
+    assert lib.attn_bwd_phase(1, *bad) == -7

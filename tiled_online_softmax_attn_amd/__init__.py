@@ -1,0 +1,179 @@
+"""Python binding of libattn.so, the MI355X (gfx950) fused attention library.
+
+The functions here marshal arguments only: they read pointers, shapes and the
+current HIP stream from torch tensors and call the C ABI declared in
+``include/attn.h`` with the same names.  Every step of the computation runs
+in the library's HIP kernels; there is no fallback.  If ``libattn.so`` has not
+been built (``python -m tiled_online_softmax_attn_amd.build``), importing the
+library raises ``AttnLibraryMissing``.
+
+Tensors: Q, K, V, O, dO, dQ, dK, dV are CUDA(HIP) tensors of shape
+[B, H, N, d], contiguous, all of one dtype (torch.bfloat16, or torch.float32
+for the forward only); lse is float32 [B, H, N].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn.so")
+
+ATTN_DTYPE_F32 = 0
+ATTN_DTYPE_BF16 = 1
+STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_DTYPE",
+          -4: "ATTN_ERR_HEADDIM", -5: "ATTN_ERR_ALIGN", -6: "ATTN_ERR_SCALE",
+          -7: "ATTN_ERR_WORKSPACE", -8: "ATTN_ERR_HIP"}
+EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_phase", "attn_bwd_workspace_bytes",
+           "attn_status_str", "attn_abi_version")
+
+
+class AttnLibraryMissing(RuntimeError):
+    pass
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {STATUS.get(code, code)} ({status_str(code)})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libattn.so and declare its ABI (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise AttnLibraryMissing(
+                f"{LIB_PATH} is not built; run `python -m tiled_online_softmax_attn_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        L.attn_fwd.restype = i
+        L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+        L.attn_bwd.restype = i
+        L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                               i, i, i, i, i, f, i, vp]
+        L.attn_bwd_phase.restype = i
+        L.attn_bwd_phase.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                     i, i, i, i, i, f, i, vp]
+        L.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
+        L.attn_status_str.restype = ctypes.c_char_p
+        L.attn_status_str.argtypes = [i]
+        L.attn_abi_version.restype = i
+        L.attn_abi_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def status_str(code: int) -> str:
+    return lib().attn_status_str(int(code)).decode()
+
+
+def attn_status_str(code: int) -> str:
+    return status_str(code)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return ATTN_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return ATTN_DTYPE_F32
+    return -1
+
+
+def _stream_handle(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _shape(q: torch.Tensor):
+    if q.dim() != 4:
+        raise ValueError("expected a [B, H, N, d] tensor")
+    return tuple(int(x) for x in q.shape)
+
+
+def _check_contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [B, H, N, d] (lse [B, H, N])")
+
+
+def attn_fwd(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
+    """Enqueue the forward: o = softmax(scale q k^T [+ causal]) v, lse = row
+    logsumexp.  All tensors preallocated by the caller."""
+    _check_contig(q, k, v, o, lse)
+    B, H, N, d = _shape(q)
+    rc = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                        int(bool(causal)), float(scale), _dtype_code(q), _stream_handle(stream))
+    if rc != 0:
+        raise AttnError(rc, "attn_fwd")
+
+
+def attn_bwd_workspace_bytes(B: int, H: int, N: int, d: int,
+                             dtype: torch.dtype = torch.bfloat16) -> int:
+    code = ATTN_DTYPE_BF16 if dtype == torch.bfloat16 else ATTN_DTYPE_F32
+    return int(lib().attn_bwd_workspace_bytes(B, H, N, d, code))
+
+
+def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool, scale: float,
+             stream=None) -> None:
+    """Enqueue the backward: dq, dk, dv of sum(dout * o).  ``workspace`` is a
+    device tensor of at least attn_bwd_workspace_bytes() bytes."""
+    _check_contig(q, k, v, o, dout, lse, dq, dk, dv)
+    B, H, N, d = _shape(q)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                        _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, B, H, N, d,
+                        int(bool(causal)), float(scale), _dtype_code(q), _stream_handle(stream))
+    if rc != 0:
+        raise AttnError(rc, "attn_bwd")
+
+
+def attn_bwd_phase(phase: int, q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool,
+                   scale: float, stream=None) -> None:
+    """Enqueue one phase of attn_bwd (0 preprocess, 1 main, 2 dQ convert)."""
+    _check_contig(q, k, v, o, dout, lse, dq, dk, dv)
+    B, H, N, d = _shape(q)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().attn_bwd_phase(int(phase), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                              _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes,
+                              B, H, N, d, int(bool(causal)), float(scale), _dtype_code(q),
+                              _stream_handle(stream))
+    if rc != 0:
+        raise AttnError(rc, f"attn_bwd_phase({phase})")
+
+
+# ------------------------------------------------------------ conveniences
+def flash_attention_forward(q, k, v, causal: bool = False, scale: float | None = None):
+    """Allocate o and lse with torch and run attn_fwd; returns (o, lse)."""
+    B, H, N, d = _shape(q)
+    if scale is None:
+        scale = d ** -0.5
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
+    attn_fwd(q, k, v, o, lse, causal, scale)
+    return o, lse
+
+
+def flash_attention_backward(q, k, v, o, lse, dout, causal: bool = False,
+                             scale: float | None = None, workspace=None):
+    """Allocate dq, dk, dv (and a workspace if none is given) and run attn_bwd."""
+    B, H, N, d = _shape(q)
+    if scale is None:
+        scale = d ** -0.5
+    if workspace is None:
+        workspace = torch.empty(attn_bwd_workspace_bytes(B, H, N, d, q.dtype), device=q.device,
+                                dtype=torch.uint8)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal, scale)
+    return dq, dk, dv

@@ -1,0 +1,120 @@
+// attn_api.cpp - the C ABI declared in include/attn.h: host-side argument
+// validation, then dispatch to the kernel launchers on the caller's stream.
+#include "attn.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "attn_launch.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape checks shared by every entry point.  Element counts must fit in
+// int64 offsets and the workgroup count in a 32-bit grid.
+int check_shape(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
+  const int64_t bh = (int64_t)B * (int64_t)H;
+  if (bh > (int64_t)1 << 31) return ATTN_ERR_SHAPE;
+  const int64_t tiles = bh * (((int64_t)N + 63) / 64);
+  if (tiles > (int64_t)INT32_MAX) return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+namespace attn {
+size_t bwd_delta_bytes(int B, int H, int N) {
+  return round256((size_t)B * (size_t)H * (size_t)N * sizeof(float));
+}
+size_t bwd_dq_acc_bytes(int B, int H, int N, int d) {
+  return round256((size_t)B * (size_t)H * (size_t)N * (size_t)d * sizeof(float));
+}
+}  // namespace attn
+
+extern "C" {
+
+int attn_abi_version(void) { return kAbiVersion; }
+
+const char* attn_status_str(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "B, H and N must be >= 1 and the sizes must fit 64-bit offsets";
+    case ATTN_ERR_DTYPE: return "dtype not supported by this entry point";
+    case ATTN_ERR_HEADDIM: return "head dimension d must be 64 or 128";
+    case ATTN_ERR_ALIGN: return "pointers must be 16-byte aligned";
+    case ATTN_ERR_SCALE: return "scale must be finite";
+    case ATTN_ERR_WORKSPACE: return "workspace is NULL or smaller than attn_bwd_workspace_bytes()";
+    case ATTN_ERR_HIP: return "the HIP runtime refused the kernel launch";
+    default: return "unknown attn status";
+  }
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+             int N, int d, int causal, float scale, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+  int rc = check_shape(B, H, N, d);
+  if (rc != ATTN_OK) return rc;
+  if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F32) return ATTN_ERR_DTYPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return ATTN_ERR_ALIGN;
+  if (!isfinite(scale)) return ATTN_ERR_SCALE;
+  attn::FwdArgs a{q, k, v, o, lse, B, H, N, d, causal != 0, scale, dtype == ATTN_DTYPE_BF16,
+                  stream};
+  return attn::launch_fwd(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int d, int dtype) {
+  if (check_shape(B, H, N, d) != ATTN_OK || dtype != ATTN_DTYPE_BF16) return 0;
+  return attn::bwd_delta_bytes(B, H, N) + attn::bwd_dq_acc_bytes(B, H, N, d);
+}
+
+static int bwd_common(int phase, const void* q, const void* k, const void* v, const void* o,
+                      const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                      void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                      int causal, float scale, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL;
+  int rc = check_shape(B, H, N, d);
+  if (rc != ATTN_OK) return rc;
+  if (phase < -1 || phase > 2) return ATTN_ERR_SHAPE;
+  if (dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
+  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return ATTN_ERR_ALIGN;
+  if (!isfinite(scale)) return ATTN_ERR_SCALE;
+  const size_t need = attn_bwd_workspace_bytes(B, H, N, d, dtype);
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+  float* delta = (float*)workspace;
+  float* dq_acc = (float*)((char*)workspace + attn::bwd_delta_bytes(B, H, N));
+  attn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, delta, dq_acc, B, H, N, d,
+                  causal != 0, scale, stream};
+  const hipError_t e = phase < 0 ? attn::launch_bwd(a) : attn::launch_bwd_phase(a, phase);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, void* workspace,
+             size_t workspace_bytes, int B, int H, int N, int d, int causal, float scale,
+             int dtype, void* stream) {
+  return bwd_common(-1, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N,
+                    d, causal, scale, dtype, stream);
+}
+
+int attn_bwd_phase(int phase, const void* q, const void* k, const void* v, const void* o,
+                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                   void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                   int causal, float scale, int dtype, void* stream) {
+  if (phase < 0 || phase > 2) return ATTN_ERR_SHAPE;
+  return bwd_common(phase, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H,
+                    N, d, causal, scale, dtype, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,371 @@
+// attn_fwd.hip - fused attention forward for gfx950.
+//
+// Method (CS336 Lecture 5 notes "GPUs, TPUs", section 8.3; CS149 Lecture 9
+// notes "Efficiently Evaluating DNNs on GPUs", section 9): one workgroup owns
+// a block of queries and streams the key/value blocks past it, keeping the
+// running row maximum m, the running sum l and the output accumulator O on
+// chip.  For each key block:
+//   S = Q K^T * scale,  m' = max(m, rowmax S),  P = e^{S - m'},
+//   l = e^{m - m'} l + rowsum P,  O = e^{m - m'} O + P V,  m = m'
+// and at the end O /= l, lse = m + ln l.  Under the causal mask, key blocks
+// wholly in the future of the query block are never visited (section 8.3).
+//
+// bf16 path (the throughput path):
+//   * 256 threads = 4 waves; 128 queries per workgroup, 32 per wave.
+//   * Each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so that in
+//     the accumulator every lane owns ONE query (column l % 32) and 16 keys.
+//     Row max / row sum are then in-lane plus one permlane32 swap.
+//   * Q^T is held in registers for the whole kernel (B operand).
+//   * O^T = V^T P^T: P^T feeds the B operand straight from the S^T
+//     accumulator (bf16-rounded), and V^T comes from row-major V in LDS via
+//     ds_read_b64_tr_b16.  The O^T accumulator keeps one query per lane, so
+//     the e^{m - m'} rescale and the final 1/l are per-lane scalars.
+//   * K and V tiles (64 keys) are double-buffered in LDS; the global loads of
+//     tile j+1 are in flight while tile j is computed.
+//   * The exponentials run in base 2 with scale*log2(e) folded into one FMA.
+//
+// fp32 path: plain fp32 FMAs (no bf16 rounding anywhere), 2 threads per query.
+#include "device_common.h"
+#include "attn_launch.h"
+
+namespace attn {
+namespace {
+
+constexpr int kFwdThreads = 256;
+constexpr int kFwdBQ = 128;  // queries per workgroup
+constexpr int kFwdBK = 64;   // keys per K/V tile
+
+template <int D>
+struct FwdLds {
+  static constexpr int kStrideK = D + 8;   // 16-byte row pad: conflict-free b128 row reads
+  static constexpr int kStrideV = D + 16;  // 32-byte row pad: conflict-free transpose reads
+  static constexpr int kElemsK = kFwdBK * kStrideK;
+  static constexpr int kElemsV = kFwdBK * kStrideV;
+  static constexpr int kStage = kElemsK + kElemsV;
+  static constexpr int kChunks = kFwdBK * D / 8;             // 16-byte chunks per tile
+  static constexpr int kChunksPerThread = kChunks / kFwdThreads;
+  static_assert(kChunks % kFwdThreads == 0, "tile must split evenly over threads");
+};
+
+// Workgroup id -> (head, query tile).  Heavy causal tiles (late queries see
+// more keys) are issued first.  With B*H a multiple of 8 every query tile of
+// one head lands on the same XCD (ids are dealt round-robin over the 8 XCDs),
+// so a head's K/V stay in one L2.
+__device__ __forceinline__ void fwd_tile_coords(int bid, int BH, int n_qtiles, bool causal,
+                                                int& bh, int& qt) {
+  const int rank = bid / BH;
+  bh = bid - rank * BH;
+  qt = causal ? (n_qtiles - 1 - rank) : rank;
+}
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(kFwdThreads, 2)
+attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                     const __bf16* __restrict__ v, __bf16* __restrict__ o,
+                     float* __restrict__ lse, int BH, int N, int n_qtiles, float scale_log2) {
+  using L = FwdLds<D>;
+  constexpr int KS = D / 16;  // k-steps of the S^T MFMA
+  constexpr int DB = D / 32;  // 32-wide d blocks of O^T
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * L::kStage];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int half = lane >> 5;
+
+  int bh, qt;
+  fwd_tile_coords(blockIdx.x, BH, n_qtiles, CAUSAL, bh, qt);
+  const int64_t head = (int64_t)bh * N * D;
+  const __bf16* qh = q + head;
+  const __bf16* kh = k + head;
+  const __bf16* vh = v + head;
+
+  const int q_wave0 = qt * kFwdBQ + wave * 32;  // first query of this wave
+  const int qry = q_wave0 + l32;                 // this lane's query
+
+  // Q^T fragments (B operand): lane holds Q[qry][16 s + 8 half + e].
+  bf16x8 qf[KS];
+  {
+    const bf16x8 zero = {};
+    const __bf16* qrow = qh + (int64_t)(qry < N ? qry : 0) * D + half * 8;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qf[s] = (qry < N) ? *reinterpret_cast<const bf16x8*>(qrow + 16 * s) : zero;
+  }
+
+  const int kv_end = CAUSAL ? min(N, (qt + 1) * kFwdBQ) : N;
+  const int n_tiles = (kv_end + kFwdBK - 1) / kFwdBK;
+
+  // global -> register staging of one K/V tile
+  uint4 rk[L::kChunksPerThread], rv[L::kChunksPerThread];
+  auto load_tile = [&](int j) {
+#pragma unroll
+    for (int r = 0; r < L::kChunksPerThread; ++r) {
+      const int c = tid + r * kFwdThreads;
+      const int row = c / (D / 8);
+      const int col = (c % (D / 8)) * 8;
+      const int key = j * kFwdBK + row;
+      if (key < N) {
+        rk[r] = *reinterpret_cast<const uint4*>(kh + (int64_t)key * D + col);
+        rv[r] = *reinterpret_cast<const uint4*>(vh + (int64_t)key * D + col);
+      } else {
+        rk[r] = make_uint4(0, 0, 0, 0);
+        rv[r] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto store_tile = [&](int st) {
+    __bf16* ks = smem + st * L::kStage;
+    __bf16* vs = ks + L::kElemsK;
+#pragma unroll
+    for (int r = 0; r < L::kChunksPerThread; ++r) {
+      const int c = tid + r * kFwdThreads;
+      const int row = c / (D / 8);
+      const int col = (c % (D / 8)) * 8;
+      *reinterpret_cast<uint4*>(ks + row * L::kStrideK + col) = rk[r];
+      *reinterpret_cast<uint4*>(vs + row * L::kStrideV + col) = rv[r];
+    }
+  };
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int b = 0; b < DB; ++b) oacc[b] = f32x16{};
+  float m_run = -INFINITY;  // running max, in units of log2 (scores * scale * log2 e)
+  float l_run = 0.f;        // this lane's share of the running sum (its 32 keys per tile)
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int j = 0; j < n_tiles; ++j) {
+    const int st = j & 1;
+    if (j + 1 < n_tiles) load_tile(j + 1);
+
+    const int key0 = j * kFwdBK;
+    // Whole tile in this wave's future: nothing to add (wave-uniform).
+    const bool skip = CAUSAL && key0 > q_wave0 + 31;
+    if (!skip) {
+      const ATTN_LDS __bf16* ks = (const ATTN_LDS __bf16*)(smem + st * L::kStage);
+      const ATTN_LDS __bf16* vs = ks + L::kElemsK;
+
+      // ---- S^T = K Q^T for two 32-key halves of the tile
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sacc[kb] = f32x16{};
+        const ATTN_LDS __bf16* krow = ks + (kb * 32 + l32) * L::kStrideK + half * 8;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(krow + 16 * s);
+          sacc[kb] = mfma_32x32x16(a, qf[s], sacc[kb]);
+        }
+      }
+
+      // ---- mask: keys past N, and (causal) keys after the query
+      const bool need_mask = (key0 + kFwdBK > N) || (CAUSAL && key0 + kFwdBK - 1 > q_wave0);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = key0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+            if (key >= N || (CAUSAL && key > qry)) sacc[kb][i] = -INFINITY;
+          }
+      }
+
+      // ---- online softmax statistics (per lane = per query)
+      float mx = sacc[0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+      mx = max_across_halves(mx);
+      const float m_new = fmaxf(m_run, mx * scale_log2);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      m_run = m_new;
+
+      float psum = 0.f;
+      bf16x8 pf[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = fast_exp2(fmaf(sacc[kb][i], scale_log2, -m_use));
+          psum += p;
+          pf[kb][i >> 3][i & 7] = (__bf16)p;
+        }
+      l_run = l_run * alpha + psum;
+
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[b][i] *= alpha;
+
+      // ---- O^T += V^T P^T
+      const int g16 = lane & 15;
+      const int grp = lane >> 4;
+#pragma unroll
+      for (int b = 0; b < DB; ++b) {
+        const int col = b * 32 + (grp & 1) * 16 + 4 * (g16 & 3);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int row = kb * 32 + t * 16 + half * 4 + (g16 >> 2);
+            const bf16x4 lo = lds_read_tr4(vs + row * L::kStrideV + col);
+            const bf16x4 hi = lds_read_tr4(vs + (row + 8) * L::kStrideV + col);
+            oacc[b] = mfma_32x32x16(concat4(lo, hi), pf[kb][t], oacc[b]);
+          }
+      }
+    }
+
+    if (j + 1 < n_tiles) store_tile(st ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = O / l, lse = ln2 * (m + log2 l)
+  const float l_tot = sum_across_halves(l_run);
+  if (qry < N) {
+    const float inv = 1.f / l_tot;
+    __bf16* orow = o + head + (int64_t)qry * D;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(oacc[b][r * 4 + e] * inv);
+        *reinterpret_cast<bf16x4*>(orow + b * 32 + r * 8 + half * 4) = w;
+      }
+    if (half == 0) lse[(int64_t)bh * N + qry] = kLn2 * (m_run + fast_log2(l_tot));
+  }
+}
+
+// ---------------------------------------------------------------- fp32 path
+constexpr int kF32Threads = 256;
+constexpr int kF32BQ = 128;  // 2 threads per query
+constexpr int kF32BK = 32;
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(kF32Threads)
+attn_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                    const float* __restrict__ v, float* __restrict__ o,
+                    float* __restrict__ lse, int BH, int N, int n_qtiles, float scale_log2) {
+  constexpr int DH = D / 2;  // dims owned by each thread of a pair
+  __shared__ __attribute__((aligned(16))) float ks[kF32BK * D];
+  __shared__ __attribute__((aligned(16))) float vs[kF32BK * D];
+
+  const int tid = threadIdx.x;
+  const int pair_half = tid & 1;
+  int bh, qt;
+  fwd_tile_coords(blockIdx.x, BH, n_qtiles, CAUSAL, bh, qt);
+  const int64_t head = (int64_t)bh * N * D;
+  const int qry = qt * kF32BQ + (tid >> 1);
+  const int q_block_last = min(N, (qt + 1) * kF32BQ) - 1;
+
+  float qr[DH], oa[DH];
+  const float* qrow = q + head + (int64_t)(qry < N ? qry : 0) * D + pair_half * DH;
+#pragma unroll
+  for (int c = 0; c < DH; ++c) {
+    qr[c] = (qry < N) ? qrow[c] : 0.f;
+    oa[c] = 0.f;
+  }
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int kv_end = CAUSAL ? q_block_last + 1 : N;
+  for (int key0 = 0; key0 < kv_end; key0 += kF32BK) {
+    __syncthreads();
+    for (int c = tid; c < kF32BK * D / 4; c += kF32Threads) {
+      const int row = c / (D / 4);
+      const int col = (c % (D / 4)) * 4;
+      const int key = key0 + row;
+      float4 kk = make_float4(0.f, 0.f, 0.f, 0.f), vv = kk;
+      if (key < N) {
+        kk = *reinterpret_cast<const float4*>(k + head + (int64_t)key * D + col);
+        vv = *reinterpret_cast<const float4*>(v + head + (int64_t)key * D + col);
+      }
+      *reinterpret_cast<float4*>(ks + row * D + col) = kk;
+      *reinterpret_cast<float4*>(vs + row * D + col) = vv;
+    }
+    __syncthreads();
+
+    float s[kF32BK];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int jj = 0; jj < kF32BK; ++jj) {
+      const float* kr = ks + jj * D + pair_half * DH;
+      float part = 0.f;
+#pragma unroll
+      for (int c = 0; c < DH; ++c) part = fmaf(qr[c], kr[c], part);
+      float dot = part + __shfl_xor(part, 1);
+      const int key = key0 + jj;
+      if (key >= N || (CAUSAL && key > qry)) dot = -INFINITY;
+      s[jj] = dot;
+      mx = fmaxf(mx, dot);
+    }
+    const float m_new = fmaxf(m_run, mx * scale_log2);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int c = 0; c < DH; ++c) oa[c] *= alpha;
+#pragma unroll
+    for (int jj = 0; jj < kF32BK; ++jj) {
+      const float p = fast_exp2(fmaf(s[jj], scale_log2, -m_use));
+      psum += p;
+      const float* vr = vs + jj * D + pair_half * DH;
+#pragma unroll
+      for (int c = 0; c < DH; ++c) oa[c] = fmaf(p, vr[c], oa[c]);
+    }
+    l_run = l_run * alpha + psum;
+  }
+
+  if (qry < N) {
+    const float inv = 1.f / l_run;
+    float* orow = o + head + (int64_t)qry * D + pair_half * DH;
+#pragma unroll
+    for (int c = 0; c < DH; c += 4)
+      *reinterpret_cast<float4*>(orow + c) =
+          make_float4(oa[c] * inv, oa[c + 1] * inv, oa[c + 2] * inv, oa[c + 3] * inv);
+    if (pair_half == 0) lse[(int64_t)bh * N + qry] = kLn2 * (m_run + fast_log2(l_run));
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bf16(const FwdArgs& a) {
+  const int n_qtiles = (a.N + kFwdBQ - 1) / kFwdBQ;
+  const int BH = a.B * a.H;
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)(BH * n_qtiles)),
+                     dim3(kFwdThreads), 0, (hipStream_t)a.stream, (const __bf16*)a.q,
+                     (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse, BH, a.N,
+                     n_qtiles, a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_f32(const FwdArgs& a) {
+  const int n_qtiles = (a.N + kF32BQ - 1) / kF32BQ;
+  const int BH = a.B * a.H;
+  hipLaunchKernelGGL((attn_fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)(BH * n_qtiles)),
+                     dim3(kF32Threads), 0, (hipStream_t)a.stream, (const float*)a.q,
+                     (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, BH, a.N,
+                     n_qtiles, a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs& a) {
+  const bool c = a.causal != 0;
+  if (a.bf16) {
+    if (a.d == 128) return c ? launch_bf16<128, true>(a) : launch_bf16<128, false>(a);
+    return c ? launch_bf16<64, true>(a) : launch_bf16<64, false>(a);
+  }
+  if (a.d == 128) return c ? launch_f32<128, true>(a) : launch_f32<128, false>(a);
+  return c ? launch_f32<64, true>(a) : launch_f32<64, false>(a);
+}
+
+}  // namespace attn

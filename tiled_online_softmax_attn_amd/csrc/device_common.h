@@ -1,0 +1,73 @@
+// device_common.h - gfx950 building blocks shared by the attention kernels.
+//
+// Lane layouts used throughout (wave64, checked on gfx950 hardware):
+//
+//   v_mfma_f32_32x32x16_bf16  D[32x32] += A[32x16] * B[16x32]
+//     A operand: lane l holds A[l % 32][(l / 32) * 8 + e],  e = 0..7
+//     B operand: lane l holds B[(l / 32) * 8 + e][l % 32],  e = 0..7
+//     C/D:       lane l holds D[(i / 4) * 8 + (l / 32) * 4 + (i % 4)][l % 32],
+//                i = 0..15
+//
+//   ds_read_b64_tr_b16 (LDS transpose read): inside each group of 16 lanes,
+//     if lane j of the group points at 4 consecutive 16-bit elements L[j][0..3],
+//     lane i of the group receives element e = L[4 e + i / 4][i % 4].
+//     So when lane j points at row (r0 + j / 4), columns (c0 + 4 (j % 4)) of a
+//     row-major tile, lane i receives column c0 + i of rows r0 .. r0 + 3.
+//
+//   v_permlane32_swap(x, x) returns {x of lanes 0-31 in both halves,
+//     x of lanes 32-63 in both halves}.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define ATTN_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 2^x with the hardware transcendental unit (v_exp_f32).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// log2(x) with the hardware transcendental unit (v_log_f32).
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Transpose read of 4 bf16 from LDS (see the layout note above).
+__device__ __forceinline__ bf16x4 lds_read_tr4(const ATTN_LDS __bf16* p) {
+  short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS short4v*)p);
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ bf16x8 concat4(bf16x4 lo, bf16x4 hi) {
+  bf16x8 r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
+// max of x over lanes l and l ^ 32.
+__device__ __forceinline__ float max_across_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                            __builtin_bit_cast(unsigned, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+
+// x of lane l plus x of lane l ^ 32.
+__device__ __forceinline__ float sum_across_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                            __builtin_bit_cast(unsigned, x), false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+}  // namespace attn
