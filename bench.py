@@ -3,7 +3,7 @@
 
 One step = one pass of the whole path over one batch of synthetic input:
 the forward (attn_fwd: O and lse) and the backward (attn_bwd's three phases:
-preprocess D, main, dQ convert) on the causal B=4 H=16 N=4096 d=128 bf16
+preprocess D, dK/dV, dQ) on the causal B=4 H=16 N=4096 d=128 bf16
 workload.  Inputs are generated on the host from a fixed seed, copied to the
 GPU, and resident in HBM before the timed region starts.
 
@@ -28,10 +28,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-KERNELS = ("fwd", "bwd_preprocess", "bwd_main", "bwd_dq_convert")
+KERNELS = ("fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq")
 CSRC = os.path.join(ROOT, "tiled_online_softmax_attn_amd", "csrc")
 KERNEL_SOURCES = {"fwd": "attn_fwd.hip", "bwd_preprocess": "attn_bwd.hip",
-                  "bwd_main": "attn_bwd.hip", "bwd_dq_convert": "attn_bwd.hip"}
+                  "bwd_dkdv": "attn_bwd.hip", "bwd_dq": "attn_bwd.hip"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -63,16 +63,21 @@ def measured_traffic(kernel: str, workload: str):
 
 def algorithmic(w, kernel: str):
     """(amount, unit, bound) per launch: FLOPs for the MFMA kernels, bytes for
-    the memory-bound helpers."""
+    the memory-bound preprocess.  A block product over the unmasked causal
+    half costs 2*B*H*N^2*d/2 FLOPs (half the forward's count).  Each backward
+    kernel is credited with the products it actually runs: dK/dV runs four
+    (S, dP, dV, dK), dQ runs three (S, dP, dQ).  The step value uses the
+    formula count (2.5x the forward for the whole backward), so the extra
+    recompute lowers `value` but not these per-kernel rates."""
     BHN = w.B * w.H * w.N
     if kernel == "fwd":
         return w.fwd_flops(), "flop", "mfma"
-    if kernel == "bwd_main":
-        return w.bwd_flops(), "flop", "mfma"
-    if kernel == "bwd_preprocess":  # read O, dO (bf16); write D (fp32), zero dQ acc (fp32)
-        return BHN * w.d * 2 * 2 + BHN * 4 + BHN * w.d * 4, "byte", "hbm"
-    # convert: read dQ acc (fp32), write dQ (bf16)
-    return BHN * w.d * 4 + BHN * w.d * 2, "byte", "hbm"
+    if kernel == "bwd_dkdv":
+        return w.fwd_flops() * 4 / 2, "flop", "mfma"
+    if kernel == "bwd_dq":
+        return w.fwd_flops() * 3 / 2, "flop", "mfma"
+    # preprocess: read O, dO (bf16); write D (fp32)
+    return BHN * w.d * 2 * 2 + BHN * 4, "byte", "hbm"
 
 
 def cpu_baseline(w, q, k, v, do, budget_s: float):

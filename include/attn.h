@@ -76,12 +76,14 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              void* stream);
 
 /* Bytes of device workspace attn_bwd needs for these sizes: the D vector
- * (B*H*N fp32) followed by a dQ fp32 accumulator (B*H*N*d fp32), each
- * 256-byte aligned.  Returns 0 for invalid sizes. */
+ * (B*H*N fp32), rounded up to a multiple of 256.  Returns 0 for invalid
+ * sizes or an unsupported dtype. */
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d, int dtype);
 
 /* Backward pass (CS336 L5 notes section 8.4): recomputes attention from the
- * saved logsumexp and returns the gradients of sum(dout * O).
+ * saved logsumexp and returns the gradients of sum(dout * O).  Every output
+ * element is written exactly once (no atomics), so results are bitwise
+ * reproducible.
  *   q, k, v     : forward inputs, [B][H][N][d] in `dtype`.
  *   o, lse      : the forward outputs for those inputs (o in `dtype`, lse
  *                 float32 [B][H][N]), as attn_fwd wrote them.
@@ -100,11 +102,11 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
 /* One phase of attn_bwd, for callers that schedule or time the phases
  * separately.  attn_bwd(...) is exactly phases 0, 1, 2 in this order on one
  * stream, with the same arguments:
- *   0  preprocess: D = rowsum(dO * O) into the workspace; zero the dQ
- *      accumulator (CS336 L5 notes section 8.4 and Exercise 9)
- *   1  main: recompute P per block and accumulate dK, dV (written) and dQ
- *      (fp32 accumulator in the workspace)
- *   2  convert: dq = bf16(dQ accumulator)
+ *   0  preprocess: D = rowsum(dO * O) into the workspace (CS336 L5 notes
+ *      section 8.4 and Exercise 9)
+ *   1  dK and dV: key blocks outside, query blocks inside; writes dk, dv
+ *   2  dQ: query blocks outside, key blocks inside; writes dq
+ * Phases 1 and 2 only read what phase 0 wrote, not each other's output.
  * A phase reads what the earlier phases left in the workspace; running them
  * out of order gives undefined results (no fault).  Errors as attn_bwd, plus
  * ATTN_ERR_SHAPE for a phase outside 0..2. */

@@ -33,9 +33,6 @@ namespace attn {
 size_t bwd_delta_bytes(int B, int H, int N) {
   return round256((size_t)B * (size_t)H * (size_t)N * sizeof(float));
 }
-size_t bwd_dq_acc_bytes(int B, int H, int N, int d) {
-  return round256((size_t)B * (size_t)H * (size_t)N * (size_t)d * sizeof(float));
-}
 }  // namespace attn
 
 extern "C" {
@@ -73,7 +70,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
 
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d, int dtype) {
   if (check_shape(B, H, N, d) != ATTN_OK || dtype != ATTN_DTYPE_BF16) return 0;
-  return attn::bwd_delta_bytes(B, H, N) + attn::bwd_dq_acc_bytes(B, H, N, d);
+  return attn::bwd_delta_bytes(B, H, N);
 }
 
 static int bwd_common(int phase, const void* q, const void* k, const void* v, const void* o,
@@ -92,9 +89,7 @@ static int bwd_common(int phase, const void* q, const void* k, const void* v, co
   const size_t need = attn_bwd_workspace_bytes(B, H, N, d, dtype);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
-  float* delta = (float*)workspace;
-  float* dq_acc = (float*)((char*)workspace + attn::bwd_delta_bytes(B, H, N));
-  attn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, delta, dq_acc, B, H, N, d,
+  attn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, B, H, N, d,
                   causal != 0, scale, stream};
   const hipError_t e = phase < 0 ? attn::launch_bwd(a) : attn::launch_bwd_phase(a, phase);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;

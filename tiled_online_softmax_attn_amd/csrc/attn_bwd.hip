@@ -1,31 +1,34 @@
 // attn_bwd.hip - fused attention backward for gfx950 (bf16 in/out, fp32 math).
 //
 // Method (CS336 Lecture 5 notes "GPUs, TPUs", section 8.4 and Exercise 9):
-// nothing N x N is stored by the forward; the backward recomputes it block by
-// block from Q, K, V, O, the logsumexp L and dO:
+// nothing N x N is kept from the forward; the backward recomputes it block by
+// block from Q, K, V, the logsumexp L and dO:
 //   P = e^{scale*S - L},  dV += P^T dO,  dP = dO V^T,
 //   dS = P * (dP - D)  with  D_i = rowsum(dO_i * O_i),
 //   dQ += scale * dS K,  dK += scale * dS^T Q.
-// The loop order is key/value blocks outside, query blocks inside (the
-// outer-K/V schedule of PDC notes Lecture 4, section 4.12), so dK and dV stay
-// in registers for the whole kernel, and dQ, which every key block adds to,
-// is accumulated with fp32 atomics (PDC notes Lecture 5, section 5.11) into a
-// workspace that a last kernel rounds to bf16.  Three launches on one stream:
-//   1. bwd_preprocess: D = rowsum(dO * O), dQ accumulator = 0
-//   2. bwd_main:       one workgroup per (head, 128-key block)
-//   3. bwd_dq_convert: dQ = bf16(accumulator)
-// A kernel boundary is the global synchronisation between the steps (PDC
-// notes Lecture 5, section 5.14).
+// Three launches on one stream (a kernel boundary is the global
+// synchronisation between them, PDC notes Lecture 5, section 5.14):
+//   phase 0  bwd_preprocess: D = rowsum(dO * O)                 (HBM-bound)
+//   phase 1  bwd_dkdv:  key/value blocks outside, query blocks inside (the
+//            outer-K/V schedule of PDC notes Lecture 4, section 4.12): dK and
+//            dV of a 128-key block stay in registers for the whole kernel.
+//   phase 2  bwd_dq:    query blocks outside, key/value blocks inside (the
+//            forward's schedule): dQ of a 128-query block stays in registers.
+// Splitting dQ from dK/dV recomputes S and dP once more (7 block products
+// instead of 5) but removes every cross-workgroup reduction: on this chip a
+// device-wide fp32 atomic add is carried out past the per-XCD L2, and the
+// atomic form of dQ measured 2.3 GB of extra memory writes per launch at
+// B=4, H=16, N=4096, d=128.  Both kernels write their results exactly once,
+// so the backward is deterministic.
 //
-// bwd_main layout (4 waves, 32 keys each; query tiles of 64 rows):
-//   * S = Q K^T and dP = dO V^T use v_mfma_f32_32x32x16_bf16 with K^T and V^T
-//     fragments held in registers; in their accumulators each lane owns one
-//     key (column l % 32) and 16 queries.
-//   * dV += P^T dO and dK += dS^T Q take P^T / dS^T straight from those
-//     accumulators as the A operand; dO and Q come from LDS through the
-//     transpose read ds_read_b64_tr_b16.
-//   * dS^T is staged in LDS (bf16, key-major) so that the four waves can form
-//     the 64 x d block of dQ over all 128 keys of the workgroup.
+// Register layouts (v_mfma_f32_32x32x16_bf16; see device_common.h):
+//   bwd_dkdv: S = Q K^T and dP = dO V^T with K^T / V^T fragments resident in
+//     registers; every lane owns one key.  dV += P^T dO and dK += dS^T Q take
+//     P^T / dS^T straight from those accumulators as the A operand and read
+//     dO / Q through the LDS transpose read.
+//   bwd_dq: S^T = K Q^T and dP^T = V dO^T with Q^T / dO^T fragments resident;
+//     every lane owns one query.  dQ^T += K^T dS^T takes dS^T from the
+//     accumulator as the B operand and reads K^T through the transpose read.
 #include "device_common.h"
 #include "attn_launch.h"
 
@@ -33,34 +36,13 @@ namespace attn {
 namespace {
 
 constexpr int kBwdThreads = 256;
-constexpr int kBwdBK = 128;  // keys per workgroup (32 per wave)
-constexpr int kBwdBQ = 64;   // queries per inner step
 
-template <int D>
-struct BwdLds {
-  static constexpr int kStrideQ = D + 16;        // Q and dO tiles, [query][d]
-  static constexpr int kStrideK = D + 16;        // K block, [key][d]
-  static constexpr int kStrideS = kBwdBQ + 16;   // dS^T, [key][query]
-  static constexpr int kElemsQ = kBwdBQ * kStrideQ;
-  // bf16 element offsets
-  static constexpr int kOffQ = 0;                       // [2][BQ][strideQ]
-  static constexpr int kOffDO = kOffQ + 2 * kElemsQ;    // [2][BQ][strideQ]
-  static constexpr int kOffK = kOffDO + 2 * kElemsQ;    // [BK][strideK]
-  static constexpr int kOffS = kOffK + kBwdBK * kStrideK;  // [BK][strideS]
-  static constexpr int kElemsBf16 = kOffS + kBwdBK * kStrideS;
-  // fp32 arrays after the bf16 region: L (log2 units) and D, [2][BQ] each
-  static constexpr int kBytes = kElemsBf16 * 2 + 2 * 2 * kBwdBQ * 4;
-  static constexpr int kChunks = kBwdBQ * D / 8;  // 16-byte chunks per Q (or dO) tile
-  static constexpr int kChunksPerThread = kChunks / kBwdThreads;
-  static_assert(kChunks % kBwdThreads == 0, "tile must split evenly over threads");
-};
-
-// ---------------------------------------------------------------- 1. preprocess
-// 8 threads per row; each handles d/8 consecutive elements.
+// ---------------------------------------------------------------- phase 0
+// D_i = sum_k dO_ik O_ik; 8 threads per row, each over d/8 consecutive columns.
 template <int D>
 __global__ void __launch_bounds__(256)
 bwd_preprocess_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ dout,
-                      float* __restrict__ delta, float* __restrict__ dq_acc, int64_t rows) {
+                      float* __restrict__ delta, int64_t rows) {
   constexpr int PER = D / 8;
   const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
   const int part = threadIdx.x & 7;
@@ -75,9 +57,6 @@ bwd_preprocess_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ d
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
     }
-    float* zrow = dq_acc + row * D + part * PER;
-#pragma unroll
-    for (int c = 0; c < PER; c += 4) *reinterpret_cast<float4*>(zrow + c) = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   acc += __shfl_xor(acc, 1);
   acc += __shfl_xor(acc, 2);
@@ -85,34 +64,36 @@ bwd_preprocess_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ d
   if (row < rows && part == 0) delta[row] = acc;
 }
 
-// ---------------------------------------------------------------- 3. dQ convert
-__global__ void __launch_bounds__(256)
-bwd_dq_convert_kernel(const float* __restrict__ dq_acc, __bf16* __restrict__ dq, int64_t n8) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const float4 a = *reinterpret_cast<const float4*>(dq_acc + i * 8);
-  const float4 b = *reinterpret_cast<const float4*>(dq_acc + i * 8 + 4);
-  bf16x8 r;
-  r[0] = (__bf16)a.x; r[1] = (__bf16)a.y; r[2] = (__bf16)a.z; r[3] = (__bf16)a.w;
-  r[4] = (__bf16)b.x; r[5] = (__bf16)b.y; r[6] = (__bf16)b.z; r[7] = (__bf16)b.w;
-  *reinterpret_cast<bf16x8*>(dq + i * 8) = r;
-}
+// ---------------------------------------------------------------- phase 1
+constexpr int kKvBK = 128;  // keys per workgroup (32 per wave)
+constexpr int kKvBQ = 64;   // queries per inner step
 
-// ---------------------------------------------------------------- 2. main
+template <int D>
+struct DkdvLds {
+  static constexpr int kStride = D + 16;  // Q and dO tiles [query][d]: conflict-free b128 and transpose reads
+  static constexpr int kElems = kKvBQ * kStride;
+  static constexpr int kOffQ = 0;                 // [2][BQ][stride]
+  static constexpr int kOffDO = 2 * kElems;       // [2][BQ][stride]
+  static constexpr int kElemsBf16 = 4 * kElems;
+  static constexpr int kBytes = kElemsBf16 * 2 + 2 * 2 * kKvBQ * 4;  // + L, D [2][BQ] fp32
+  static constexpr int kChunksPerThread = kKvBQ * D / 8 / kBwdThreads;
+  static_assert(kKvBQ * D / 8 % kBwdThreads == 0, "tile must split evenly over threads");
+};
+
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(kBwdThreads, 1)
-bwd_main_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 const __bf16* __restrict__ v, const __bf16* __restrict__ dout,
                 const float* __restrict__ lse, const float* __restrict__ delta,
-                float* __restrict__ dq_acc, __bf16* __restrict__ dk, __bf16* __restrict__ dv,
-                int BH, int N, int n_kblocks, float scale, float scale_log2) {
-  using L = BwdLds<D>;
+                __bf16* __restrict__ dk, __bf16* __restrict__ dv, int BH, int N, float scale,
+                float scale_log2) {
+  using L = DkdvLds<D>;
   constexpr int KS = D / 16;  // k-steps over d
   constexpr int DB = D / 32;  // 32-wide d blocks
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[L::kBytes];
   __bf16* smem = reinterpret_cast<__bf16*>(smem_raw);
   float* sm_l = reinterpret_cast<float*>(smem_raw + L::kElemsBf16 * 2);  // [2][BQ]
-  float* sm_d = sm_l + 2 * kBwdBQ;                                      // [2][BQ]
+  float* sm_d = sm_l + 2 * kKvBQ;                                      // [2][BQ]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -122,21 +103,21 @@ bwd_main_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int g16 = lane & 15;
   const int grp = lane >> 4;
 
-  const int rank = blockIdx.x / BH;
-  const int bh = blockIdx.x - rank * BH;
-  const int kblk = rank;  // causal: low key blocks see the most queries, issue them first
+  // workgroup id -> (head, key block); low key blocks meet the most queries
+  // under the causal mask, so they are issued first
+  const int kblk = blockIdx.x / BH;
+  const int bh = blockIdx.x - kblk * BH;
   const int64_t head = (int64_t)bh * N * D;
   const __bf16* qh = q + head;
   const __bf16* doh = dout + head;
   const float* lse_h = lse + (int64_t)bh * N;
   const float* del_h = delta + (int64_t)bh * N;
 
-  const int key_wg0 = kblk * kBwdBK;
+  const int key_wg0 = kblk * kKvBK;
   const int key_w0 = key_wg0 + wave * 32;  // first key of this wave
   const int key = key_w0 + l32;            // this lane's key (accumulator column)
 
-  // K and V of this workgroup: LDS copy of K (for dQ), and per-wave K^T / V^T
-  // fragments in registers (B operand: lane holds X[key][16 s + 8 half + e]).
+  // K^T and V^T fragments (B operand): lane holds X[key][16 s + 8 half + e].
   bf16x8 kf[KS], vf[KS];
   {
     const bf16x8 zero = {};
@@ -148,20 +129,10 @@ bwd_main_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       kf[s] = ok ? *reinterpret_cast<const bf16x8*>(krow + 16 * s) : zero;
       vf[s] = ok ? *reinterpret_cast<const bf16x8*>(vrow + 16 * s) : zero;
     }
-    __bf16* ks = smem + L::kOffK;
-    for (int c = tid; c < kBwdBK * D / 8; c += kBwdThreads) {
-      const int row = c / (D / 8);
-      const int col = (c % (D / 8)) * 8;
-      const int kk = key_wg0 + row;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (kk < N) val = *reinterpret_cast<const uint4*>(k + head + (int64_t)kk * D + col);
-      *reinterpret_cast<uint4*>(ks + row * L::kStrideK + col) = val;
-    }
   }
 
-  // query tiles this key block meets
-  const int n_qtiles = (N + kBwdBQ - 1) / kBwdBQ;
-  const int qt_begin = CAUSAL ? key_wg0 / kBwdBQ : 0;
+  const int n_qtiles = (N + kKvBQ - 1) / kKvBQ;
+  const int qt_begin = CAUSAL ? key_wg0 / kKvBQ : 0;
 
   uint4 rq[L::kChunksPerThread], rdo[L::kChunksPerThread];
   float rl = 0.f, rd = 0.f;
@@ -171,7 +142,7 @@ bwd_main_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       const int c = tid + r * kBwdThreads;
       const int row = c / (D / 8);
       const int col = (c % (D / 8)) * 8;
-      const int qq = qt * kBwdBQ + row;
+      const int qq = qt * kKvBQ + row;
       if (qq < N) {
         rq[r] = *reinterpret_cast<const uint4*>(qh + (int64_t)qq * D + col);
         rdo[r] = *reinterpret_cast<const uint4*>(doh + (int64_t)qq * D + col);
@@ -180,26 +151,26 @@ bwd_main_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         rdo[r] = make_uint4(0, 0, 0, 0);
       }
     }
-    if (tid < kBwdBQ) {
-      const int qq = qt * kBwdBQ + tid;
+    if (tid < kKvBQ) {
+      const int qq = qt * kKvBQ + tid;
       rl = qq < N ? lse_h[qq] * kLog2e : 0.f;
       rd = qq < N ? del_h[qq] : 0.f;
     }
   };
   auto store_tile = [&](int st) {
-    __bf16* qs = smem + L::kOffQ + st * L::kElemsQ;
-    __bf16* ds = smem + L::kOffDO + st * L::kElemsQ;
+    __bf16* qs = smem + L::kOffQ + st * L::kElems;
+    __bf16* ds = smem + L::kOffDO + st * L::kElems;
 #pragma unroll
     for (int r = 0; r < L::kChunksPerThread; ++r) {
       const int c = tid + r * kBwdThreads;
       const int row = c / (D / 8);
       const int col = (c % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(qs + row * L::kStrideQ + col) = rq[r];
-      *reinterpret_cast<uint4*>(ds + row * L::kStrideQ + col) = rdo[r];
+      *reinterpret_cast<uint4*>(qs + row * L::kStride + col) = rq[r];
+      *reinterpret_cast<uint4*>(ds + row * L::kStride + col) = rdo[r];
     }
-    if (tid < kBwdBQ) {
-      sm_l[st * kBwdBQ + tid] = rl;
-      sm_d[st * kBwdBQ + tid] = rd;
+    if (tid < kKvBQ) {
+      sm_l[st * kKvBQ + tid] = rl;
+      sm_d[st * kKvBQ + tid] = rd;
     }
   };
 
@@ -220,35 +191,32 @@ bwd_main_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const int st = (qt - qt_begin) & 1;
     if (qt + 1 < n_qtiles) load_tile(qt + 1);
 
-    const ATTN_LDS __bf16* qs = (const ATTN_LDS __bf16*)(smem + L::kOffQ + st * L::kElemsQ);
-    const ATTN_LDS __bf16* dos = (const ATTN_LDS __bf16*)(smem + L::kOffDO + st * L::kElemsQ);
-    const float* lq = sm_l + st * kBwdBQ;
-    const float* dq_d = sm_d + st * kBwdBQ;
-    ATTN_LDS __bf16* sts = (ATTN_LDS __bf16*)(smem + L::kOffS);
-
-    const int q0 = qt * kBwdBQ;
-    // All 64 queries of the tile precede every key of this wave: nothing to do.
-    const bool skip = CAUSAL && (q0 + kBwdBQ - 1 < key_w0);
+    const int q0 = qt * kKvBQ;
+    // wave-uniform: every query of the tile precedes every key of this wave
+    const bool skip = CAUSAL && (q0 + kKvBQ - 1 < key_w0);
     if (!skip) {
-      const bool need_mask = (q0 + kBwdBQ > N) || (key_w0 + 32 > N) ||
-                             (CAUSAL && q0 < key_w0 + 31);
+      const ATTN_LDS __bf16* qs = (const ATTN_LDS __bf16*)(smem + L::kOffQ + st * L::kElems);
+      const ATTN_LDS __bf16* dos = (const ATTN_LDS __bf16*)(smem + L::kOffDO + st * L::kElems);
+      const float* lq = sm_l + st * kKvBQ;
+      const float* dq_d = sm_d + st * kKvBQ;
+      const bool need_mask =
+          (q0 + kKvBQ > N) || (key_w0 + 32 > N) || (CAUSAL && q0 < key_w0 + 31);
+
       // ---- S = Q K^T and dP = dO V^T for two 32-query blocks
-      f32x16 sacc[2], pacc[2];
+      f32x16 sacc[2] = {f32x16{}, f32x16{}};
+      f32x16 pacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        sacc[qb] = f32x16{};
-        pacc[qb] = f32x16{};
-        const ATTN_LDS __bf16* qrow = qs + (qb * 32 + l32) * L::kStrideQ + half * 8;
-        const ATTN_LDS __bf16* drow = dos + (qb * 32 + l32) * L::kStrideQ + half * 8;
+      for (int s = 0; s < KS; ++s)
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(qrow + 16 * s);
+        for (int qb = 0; qb < 2; ++qb) {
+          const int off = (qb * 32 + l32) * L::kStride + half * 8 + 16 * s;
+          const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(qs + off);
           sacc[qb] = mfma_32x32x16(a, kf[s], sacc[qb]);
-          const bf16x8 b = *reinterpret_cast<const ATTN_LDS bf16x8*>(drow + 16 * s);
+          const bf16x8 b = *reinterpret_cast<const ATTN_LDS bf16x8*>(dos + off);
           pacc[qb] = mfma_32x32x16(b, vf[s], pacc[qb]);
         }
-      }
-      // ---- P = 2^{S scale log2e - L log2e}; dS = P (dP - D)
+
+      // ---- P = 2^{S scale log2e - L log2e};  dS = P (dP - D)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -270,7 +238,8 @@ bwd_main_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             pacc[qb][i] = p * (pacc[qb][i] - dv4[e]);
           }
         }
-      // ---- dV += P^T dO ; dK += dS^T Q   (A from the accumulators, B by transpose reads)
+
+      // ---- dV += P^T dO ; dK += dS^T Q
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -285,76 +254,22 @@ bwd_main_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
           for (int b = 0; b < DB; ++b) {
             const int col = b * 32 + (grp & 1) * 16 + 4 * (g16 & 3);
-            const bf16x8 dob = concat4(lds_read_tr4(dos + row * L::kStrideQ + col),
-                                       lds_read_tr4(dos + (row + 8) * L::kStrideQ + col));
+            const bf16x8 dob = concat4(lds_read_tr4(dos + row * L::kStride + col),
+                                       lds_read_tr4(dos + (row + 8) * L::kStride + col));
             dv_acc[b] = mfma_32x32x16(pa, dob, dv_acc[b]);
-            const bf16x8 qbv = concat4(lds_read_tr4(qs + row * L::kStrideQ + col),
-                                       lds_read_tr4(qs + (row + 8) * L::kStrideQ + col));
+            const bf16x8 qbv = concat4(lds_read_tr4(qs + row * L::kStride + col),
+                                       lds_read_tr4(qs + (row + 8) * L::kStride + col));
             dk_acc[b] = mfma_32x32x16(sa, qbv, dk_acc[b]);
           }
         }
-      // ---- stage dS^T (bf16) for the dQ product: sts[key][query]
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          bf16x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (__bf16)pacc[qb][r * 4 + e];
-          *reinterpret_cast<ATTN_LDS bf16x4*>(sts + (wave * 32 + l32) * L::kStrideS + qb * 32 +
-                                              r * 8 + half * 4) = w;
-        }
-    } else {
-      // this wave's keys contribute nothing to this query tile
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          *reinterpret_cast<ATTN_LDS bf16x4*>(sts + (wave * 32 + l32) * L::kStrideS + qb * 32 +
-                                              r * 8 + half * 4) = bf16x4{};
-    }
-    __syncthreads();
-
-    // ---- dQ[q0 .. q0+63][:] += scale * dS K over the 128 keys of the workgroup
-    {
-      const ATTN_LDS __bf16* ks = (const ATTN_LDS __bf16*)(smem + L::kOffK);
-      const int qb = wave & 1;
-      // causal: keys of this workgroup beyond the last query of the tile add nothing
-      const int key_lim = CAUSAL ? min(kBwdBK, q0 + kBwdBQ - key_wg0) : kBwdBK;
-      const int ksteps = (key_lim + 15) / 16;
-#pragma unroll
-      for (int bb = 0; bb < DB / 2 + (DB == 1); ++bb) {
-        const int b = (wave >> 1) + 2 * bb;
-        if (b >= DB) break;
-        f32x16 acc = f32x16{};
-        for (int ks16 = 0; ks16 < ksteps; ++ks16) {
-          const int krow = ks16 * 16 + half * 8 + (g16 >> 2);
-          // A = dS[query][keys]: transpose read of sts[key][query]
-          const int qcol = qb * 32 + (grp & 1) * 16 + 4 * (g16 & 3);
-          const bf16x8 a = concat4(lds_read_tr4(sts + krow * L::kStrideS + qcol),
-                                   lds_read_tr4(sts + (krow + 4) * L::kStrideS + qcol));
-          // B = K[keys][d]: transpose read of the K block
-          const int dcol = b * 32 + (grp & 1) * 16 + 4 * (g16 & 3);
-          const bf16x8 bk = concat4(lds_read_tr4(ks + krow * L::kStrideK + dcol),
-                                    lds_read_tr4(ks + (krow + 4) * L::kStrideK + dcol));
-          acc = mfma_32x32x16(a, bk, acc);
-        }
-        // acc lane: d column b*32 + l32, query rows (i/4)*8 + half*4 + i%4
-        const int dd = b * 32 + l32;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int qq = q0 + qb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-          if (qq < N) atomicAdd(dq_acc + head + (int64_t)qq * D + dd, acc[i] * scale);
-        }
-      }
     }
 
     if (qt + 1 < n_qtiles) store_tile(st ^ 1);
     __syncthreads();
   }
 
-  // ---- write dK = scale * acc and dV: lane holds d column b*32 + l32 and
-  //      key rows (i/4)*8 + half*4 + i%4 of this wave's 32 keys
+  // ---- dK = scale * acc, dV: lane holds d column b*32 + l32 and key rows
+  //      (i/4)*8 + half*4 + i%4 of this wave's 32 keys
 #pragma unroll
   for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -368,36 +283,205 @@ bwd_main_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch_main(const BwdArgs& a) {
-  using L = BwdLds<D>;
-  const int BH = a.B * a.H;
-  const int n_kblocks = (a.N + kBwdBK - 1) / kBwdBK;
-  auto kern = bwd_main_kernel<D, CAUSAL>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, L::kBytes);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(BH * n_kblocks)), dim3(kBwdThreads), L::kBytes,
-                     (hipStream_t)a.stream, (const __bf16*)a.q, (const __bf16*)a.k,
-                     (const __bf16*)a.v, (const __bf16*)a.dout, a.lse, a.delta, a.dq_acc,
-                     (__bf16*)a.dk, (__bf16*)a.dv, BH, a.N, n_kblocks, a.scale,
-                     a.scale * kLog2e);
-  return hipGetLastError();
-}
+// ---------------------------------------------------------------- phase 2
+constexpr int kDqBQ = 128;  // queries per workgroup (32 per wave)
+constexpr int kDqBK = 64;   // keys per K/V tile
 
 template <int D>
-hipError_t launch_phase(const BwdArgs& a, int phase) {
-  const int64_t rows = (int64_t)a.B * a.H * a.N;
-  if (phase == 0) {
-    hipLaunchKernelGGL(bwd_preprocess_kernel<D>, dim3((unsigned)((rows + 31) / 32)), dim3(256),
-                       0, (hipStream_t)a.stream, (const __bf16*)a.o, (const __bf16*)a.dout,
-                       a.delta, a.dq_acc, rows);
-    return hipGetLastError();
+struct DqLds {
+  static constexpr int kStrideK = D + 16;  // b128 row reads and transpose reads
+  static constexpr int kStrideV = D + 8;   // b128 row reads only
+  static constexpr int kElemsK = kDqBK * kStrideK;
+  static constexpr int kElemsV = kDqBK * kStrideV;
+  static constexpr int kStage = kElemsK + kElemsV;
+  static constexpr int kChunksPerThread = kDqBK * D / 8 / kBwdThreads;
+  static_assert(kDqBK * D / 8 % kBwdThreads == 0, "tile must split evenly over threads");
+};
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(kBwdThreads, 2)
+bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+              const __bf16* __restrict__ v, const __bf16* __restrict__ dout,
+              const float* __restrict__ lse, const float* __restrict__ delta,
+              __bf16* __restrict__ dq, int BH, int N, int n_qtiles, float scale,
+              float scale_log2) {
+  using L = DqLds<D>;
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * L::kStage];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int half = lane >> 5;
+  const int g16 = lane & 15;
+  const int grp = lane >> 4;
+
+  // workgroup id -> (head, query tile), heavy causal tiles first
+  const int rank = blockIdx.x / BH;
+  const int bh = blockIdx.x - rank * BH;
+  const int qt = CAUSAL ? (n_qtiles - 1 - rank) : rank;
+  const int64_t head = (int64_t)bh * N * D;
+  const __bf16* kh = k + head;
+  const __bf16* vh = v + head;
+
+  const int q_wave0 = qt * kDqBQ + wave * 32;
+  const int qry = q_wave0 + l32;
+  const bool qok = qry < N;
+
+  // Q^T and dO^T fragments (B operand): lane holds X[qry][16 s + 8 half + e]
+  bf16x8 qf[KS], df[KS];
+  {
+    const bf16x8 zero = {};
+    const int64_t roff = head + (int64_t)(qok ? qry : 0) * D + half * 8;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      qf[s] = qok ? *reinterpret_cast<const bf16x8*>(q + roff + 16 * s) : zero;
+      df[s] = qok ? *reinterpret_cast<const bf16x8*>(dout + roff + 16 * s) : zero;
+    }
   }
-  if (phase == 1) return a.causal ? launch_main<D, true>(a) : launch_main<D, false>(a);
-  const int64_t n8 = rows * D / 8;
-  hipLaunchKernelGGL(bwd_dq_convert_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0,
-                     (hipStream_t)a.stream, a.dq_acc, (__bf16*)a.dq, n8);
+  const float lq2 = qok ? lse[(int64_t)bh * N + qry] * kLog2e : 0.f;
+  const float dlt = qok ? delta[(int64_t)bh * N + qry] : 0.f;
+
+  const int kv_end = CAUSAL ? min(N, (qt + 1) * kDqBQ) : N;
+  const int n_tiles = (kv_end + kDqBK - 1) / kDqBK;
+
+  uint4 rk[L::kChunksPerThread], rv[L::kChunksPerThread];
+  auto load_tile = [&](int j) {
+#pragma unroll
+    for (int r = 0; r < L::kChunksPerThread; ++r) {
+      const int c = tid + r * kBwdThreads;
+      const int row = c / (D / 8);
+      const int col = (c % (D / 8)) * 8;
+      const int kk = j * kDqBK + row;
+      if (kk < N) {
+        rk[r] = *reinterpret_cast<const uint4*>(kh + (int64_t)kk * D + col);
+        rv[r] = *reinterpret_cast<const uint4*>(vh + (int64_t)kk * D + col);
+      } else {
+        rk[r] = make_uint4(0, 0, 0, 0);
+        rv[r] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto store_tile = [&](int st) {
+    __bf16* ks = smem + st * L::kStage;
+    __bf16* vs = ks + L::kElemsK;
+#pragma unroll
+    for (int r = 0; r < L::kChunksPerThread; ++r) {
+      const int c = tid + r * kBwdThreads;
+      const int row = c / (D / 8);
+      const int col = (c % (D / 8)) * 8;
+      *reinterpret_cast<uint4*>(ks + row * L::kStrideK + col) = rk[r];
+      *reinterpret_cast<uint4*>(vs + row * L::kStrideV + col) = rv[r];
+    }
+  };
+
+  f32x16 dq_acc[DB];
+#pragma unroll
+  for (int b = 0; b < DB; ++b) dq_acc[b] = f32x16{};
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int j = 0; j < n_tiles; ++j) {
+    const int st = j & 1;
+    if (j + 1 < n_tiles) load_tile(j + 1);
+    const int key0 = j * kDqBK;
+    const bool skip = CAUSAL && key0 > q_wave0 + 31;
+    if (!skip) {
+      const ATTN_LDS __bf16* ks = (const ATTN_LDS __bf16*)(smem + st * L::kStage);
+      const ATTN_LDS __bf16* vs = ks + L::kElemsK;
+      const bool need_mask = (key0 + kDqBK > N) || (CAUSAL && key0 + kDqBK - 1 > q_wave0);
+
+      // ---- S^T = K Q^T and dP^T = V dO^T for two 32-key halves
+      f32x16 sacc[2] = {f32x16{}, f32x16{}};
+      f32x16 pacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(
+              ks + (kb * 32 + l32) * L::kStrideK + half * 8 + 16 * s);
+          sacc[kb] = mfma_32x32x16(a, qf[s], sacc[kb]);
+          const bf16x8 b = *reinterpret_cast<const ATTN_LDS bf16x8*>(
+              vs + (kb * 32 + l32) * L::kStrideV + half * 8 + 16 * s);
+          pacc[kb] = mfma_32x32x16(b, df[s], pacc[kb]);
+        }
+
+      // ---- P^T = 2^{S^T scale log2e - L}; dS^T = P^T (dP^T - D), as bf16 B operand
+      bf16x8 sf[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float p = fast_exp2(fmaf(sacc[kb][i], scale_log2, -lq2));
+          if (need_mask) {
+            const int kk = key0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+            if (kk >= N || (CAUSAL && kk > qry)) p = 0.f;
+          }
+          sf[kb][i >> 3][i & 7] = (__bf16)(p * (pacc[kb][i] - dlt));
+        }
+
+      // ---- dQ^T += K^T dS^T
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int row = kb * 32 + t * 16 + half * 4 + (g16 >> 2);
+#pragma unroll
+          for (int b = 0; b < DB; ++b) {
+            const int col = b * 32 + (grp & 1) * 16 + 4 * (g16 & 3);
+            const bf16x8 ka = concat4(lds_read_tr4(ks + row * L::kStrideK + col),
+                                      lds_read_tr4(ks + (row + 8) * L::kStrideK + col));
+            dq_acc[b] = mfma_32x32x16(ka, sf[kb][t], dq_acc[b]);
+          }
+        }
+    }
+    if (j + 1 < n_tiles) store_tile(st ^ 1);
+    __syncthreads();
+  }
+
+  // ---- dQ = scale * acc: lane holds query qry, d rows b*32 + (i/4)*8 + half*4 + i%4
+  if (qok) {
+    __bf16* row = dq + head + (int64_t)qry * D;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(dq_acc[b][r * 4 + e] * scale);
+        *reinterpret_cast<bf16x4*>(row + b * 32 + r * 8 + half * 4) = w;
+      }
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+template <int D>
+hipError_t launch_phase(const BwdArgs& a, int phase) {
+  const int BH = a.B * a.H;
+  const hipStream_t s = (hipStream_t)a.stream;
+  if (phase == 0) {
+    const int64_t rows = (int64_t)BH * a.N;
+    hipLaunchKernelGGL(bwd_preprocess_kernel<D>, dim3((unsigned)((rows + 31) / 32)), dim3(256),
+                       0, s, (const __bf16*)a.o, (const __bf16*)a.dout, a.delta, rows);
+  } else if (phase == 1) {
+    const int nkb = (a.N + kKvBK - 1) / kKvBK;
+    auto kern = a.causal ? bwd_dkdv_kernel<D, true> : bwd_dkdv_kernel<D, false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(BH * nkb)), dim3(kBwdThreads), 0, s,
+                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
+                       (const __bf16*)a.dout, a.lse, a.delta, (__bf16*)a.dk, (__bf16*)a.dv, BH,
+                       a.N, a.scale, a.scale * kLog2e);
+  } else {
+    const int nqt = (a.N + kDqBQ - 1) / kDqBQ;
+    auto kern = a.causal ? bwd_dq_kernel<D, true> : bwd_dq_kernel<D, false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(BH * nqt)), dim3(kBwdThreads), 0, s,
+                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
+                       (const __bf16*)a.dout, a.lse, a.delta, (__bf16*)a.dq, BH, a.N, nqt,
+                       a.scale, a.scale * kLog2e);
+  }
   return hipGetLastError();
 }
 

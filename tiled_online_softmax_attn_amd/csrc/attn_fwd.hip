@@ -28,12 +28,15 @@
 #include "device_common.h"
 #include "attn_launch.h"
 
+#include <type_traits>
+
 namespace attn {
 namespace {
 
 constexpr int kFwdThreads = 256;
 constexpr int kFwdBQ = 128;  // queries per workgroup
 constexpr int kFwdBK = 64;   // keys per K/V tile
+constexpr float kRescaleSlack = 8.f;  // log2 units: P never exceeds 2^8
 
 template <int D>
 struct FwdLds {
@@ -131,8 +134,98 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   f32x16 oacc[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b) oacc[b] = f32x16{};
-  float m_run = -INFINITY;  // running max, in units of log2 (scores * scale * log2 e)
-  float l_run = 0.f;        // this lane's share of the running sum (its 32 keys per tile)
+  // Reference maximum of the exponentials, in log2 units (score * scale *
+  // log2 e).  It only moves when a row maximum exceeds it by more than
+  // kRescaleSlack, so P = 2^{s - m_ref} stays below 2^kRescaleSlack and the
+  // e^{m - m'} rescale of O and l runs on few tiles.  Any reference value
+  // gives the same O = (sum P V) / (sum P) and lse = m_ref + log2(l) in exact
+  // arithmetic.
+  float m_ref = -INFINITY;
+  float l_run = 0.f;  // this lane's share of the running sum (its 32 keys per tile)
+
+  const int g16 = lane & 15;
+  const int grp = lane >> 4;
+
+  // One K/V tile: S^T = K Q^T, online-softmax update, O^T += V^T P^T.
+  // MASK selects the code path for tiles that straddle the causal diagonal or
+  // the end of the sequence.
+  auto tile_step = [&](const int key0, const int st, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const ATTN_LDS __bf16* ks = (const ATTN_LDS __bf16*)(smem + st * L::kStage);
+    const ATTN_LDS __bf16* vs = ks + L::kElemsK;
+
+    // ---- S^T = K Q^T for the two 32-key halves (two independent MFMA chains)
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(
+            ks + (kb * 32 + l32) * L::kStrideK + half * 8 + 16 * s);
+        sacc[kb] = mfma_32x32x16(a, qf[s], sacc[kb]);
+      }
+
+    if constexpr (MASK) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = key0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+          if (key >= N || (CAUSAL && key > qry)) sacc[kb][i] = -INFINITY;
+        }
+    }
+
+    // ---- row maximum of this tile for the lane's query
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+    mx = max_across_halves(mx) * scale_log2;
+
+    // ---- move the reference maximum only when it is exceeded by the slack
+    if (wave_any(mx > m_ref + kRescaleSlack)) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = (MASK && m_new == -INFINITY) ? 1.f : fast_exp2(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[b][i] *= alpha;
+    }
+    const float m_off = (MASK && m_ref == -INFINITY) ? 0.f : m_ref;
+
+    // ---- P = 2^{s * scale * log2 e - m_ref}, rounded to bf16 as the B operand
+    float psum = 0.f;
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(fmaf(sacc[kb][i], scale_log2, -m_off));
+        psum += p;
+        pf[kb][i >> 3][i & 7] = (__bf16)p;
+      }
+    l_run += psum;
+
+    // ---- O^T += V^T P^T: for each 16-key step, DB independent accumulators
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int row = kb * 32 + t * 16 + half * 4 + (g16 >> 2);
+        bf16x8 va[DB];
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {
+          const int col = b * 32 + (grp & 1) * 16 + 4 * (g16 & 3);
+          va[b] = concat4(lds_read_tr4(vs + row * L::kStrideV + col),
+                          lds_read_tr4(vs + (row + 8) * L::kStrideV + col));
+        }
+#pragma unroll
+        for (int b = 0; b < DB; ++b) oacc[b] = mfma_32x32x16(va[b], pf[kb][t], oacc[b]);
+      }
+  };
 
   load_tile(0);
   store_tile(0);
@@ -141,92 +234,24 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   for (int j = 0; j < n_tiles; ++j) {
     const int st = j & 1;
     if (j + 1 < n_tiles) load_tile(j + 1);
-
     const int key0 = j * kFwdBK;
-    // Whole tile in this wave's future: nothing to add (wave-uniform).
+    // wave-uniform: the whole tile lies in this wave's future (nothing to add),
+    // or it crosses the diagonal / the sequence end (masked path)
     const bool skip = CAUSAL && key0 > q_wave0 + 31;
+    const bool need_mask = (key0 + kFwdBK > N) || (CAUSAL && key0 + kFwdBK - 1 > q_wave0);
     if (!skip) {
-      const ATTN_LDS __bf16* ks = (const ATTN_LDS __bf16*)(smem + st * L::kStage);
-      const ATTN_LDS __bf16* vs = ks + L::kElemsK;
-
-      // ---- S^T = K Q^T for two 32-key halves of the tile
-      f32x16 sacc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = f32x16{};
-        const ATTN_LDS __bf16* krow = ks + (kb * 32 + l32) * L::kStrideK + half * 8;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(krow + 16 * s);
-          sacc[kb] = mfma_32x32x16(a, qf[s], sacc[kb]);
-        }
-      }
-
-      // ---- mask: keys past N, and (causal) keys after the query
-      const bool need_mask = (key0 + kFwdBK > N) || (CAUSAL && key0 + kFwdBK - 1 > q_wave0);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = key0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-            if (key >= N || (CAUSAL && key > qry)) sacc[kb][i] = -INFINITY;
-          }
-      }
-
-      // ---- online softmax statistics (per lane = per query)
-      float mx = sacc[0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-      mx = max_across_halves(mx);
-      const float m_new = fmaxf(m_run, mx * scale_log2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      m_run = m_new;
-
-      float psum = 0.f;
-      bf16x8 pf[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(fmaf(sacc[kb][i], scale_log2, -m_use));
-          psum += p;
-          pf[kb][i >> 3][i & 7] = (__bf16)p;
-        }
-      l_run = l_run * alpha + psum;
-
-#pragma unroll
-      for (int b = 0; b < DB; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[b][i] *= alpha;
-
-      // ---- O^T += V^T P^T
-      const int g16 = lane & 15;
-      const int grp = lane >> 4;
-#pragma unroll
-      for (int b = 0; b < DB; ++b) {
-        const int col = b * 32 + (grp & 1) * 16 + 4 * (g16 & 3);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const int row = kb * 32 + t * 16 + half * 4 + (g16 >> 2);
-            const bf16x4 lo = lds_read_tr4(vs + row * L::kStrideV + col);
-            const bf16x4 hi = lds_read_tr4(vs + (row + 8) * L::kStrideV + col);
-            oacc[b] = mfma_32x32x16(concat4(lo, hi), pf[kb][t], oacc[b]);
-          }
-      }
+      if (need_mask)
+        tile_step(key0, st, std::true_type{});
+      else
+        tile_step(key0, st, std::false_type{});
     }
-
     if (j + 1 < n_tiles) store_tile(st ^ 1);
     __syncthreads();
   }
 
   // ---- epilogue: O = O / l, lse = ln2 * (m + log2 l)
   const float l_tot = sum_across_halves(l_run);
+  const float m_run = m_ref;
   if (qry < N) {
     const float inv = 1.f / l_tot;
     __bf16* orow = o + head + (int64_t)qry * D;

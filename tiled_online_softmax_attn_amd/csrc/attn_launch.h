@@ -30,8 +30,7 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;   // [B][H][N] fp32 workspace: D = rowsum(dO * O)
-  float* dq_acc;  // [B][H][N][d] fp32 workspace: dQ accumulator
+  float* delta;  // [B][H][N] fp32 workspace: D = rowsum(dO * O)
   int B, H, N, d;
   int causal;
   float scale;
@@ -40,11 +39,10 @@ struct BwdArgs {
 
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
-// phase 0 = preprocess, 1 = main, 2 = dQ convert
+// phase 0 = preprocess (D), 1 = dK and dV, 2 = dQ
 hipError_t launch_bwd_phase(const BwdArgs& a, int phase);
 
-// Workspace layout of the backward (offsets in bytes, 256-byte aligned).
+// Workspace of the backward: the D vector, rounded up to 256 bytes.
 size_t bwd_delta_bytes(int B, int H, int N);
-size_t bwd_dq_acc_bytes(int B, int H, int N, int d);
 
 }  // namespace attn

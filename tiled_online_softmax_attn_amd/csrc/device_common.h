@@ -56,6 +56,9 @@ __device__ __forceinline__ bf16x8 concat4(bf16x4 lo, bf16x4 hi) {
   return r;
 }
 
+// True on every lane when p holds on at least one active lane of the wave.
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
 // max of x over lanes l and l ^ 32.
 __device__ __forceinline__ float max_across_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
