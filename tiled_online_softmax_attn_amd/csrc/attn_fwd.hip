@@ -38,16 +38,18 @@ constexpr int kFwdBQ = 128;  // queries per workgroup
 constexpr int kFwdBK = 64;   // keys per K/V tile
 constexpr float kRescaleSlack = 8.f;  // log2 units: P never exceeds 2^8
 
+// K and V tiles of 64 keys, stored without padding and XOR-swizzled by
+// 16-byte chunk (tile_swizzle), double-buffered: [stage][K | V][64][D].
 template <int D>
 struct FwdLds {
-  static constexpr int kStrideK = D + 8;   // 16-byte row pad: conflict-free b128 row reads
-  static constexpr int kStrideV = D + 16;  // 32-byte row pad: conflict-free transpose reads
-  static constexpr int kElemsK = kFwdBK * kStrideK;
-  static constexpr int kElemsV = kFwdBK * kStrideV;
-  static constexpr int kStage = kElemsK + kElemsV;
-  static constexpr int kChunks = kFwdBK * D / 8;             // 16-byte chunks per tile
-  static constexpr int kChunksPerThread = kChunks / kFwdThreads;
-  static_assert(kChunks % kFwdThreads == 0, "tile must split evenly over threads");
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kTileBytes = kFwdBK * kRowBytes;
+  static constexpr int kStageBytes = 2 * kTileBytes;
+  static constexpr int kBytes = 2 * kStageBytes;
+  static constexpr int kRowsPerDma = 1024 / kRowBytes;                // rows per wave instruction
+  static constexpr int kDmaPerWave = kFwdBK / kRowsPerDma / (kFwdThreads / 64);
+  static constexpr int kChunksPerRow = D / 8;
+  static_assert(kFwdBK % (kRowsPerDma * (kFwdThreads / 64)) == 0, "tile must split over waves");
 };
 
 // Workgroup id -> (head, query tile).  Heavy causal tiles (late queries see
@@ -69,13 +71,15 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   using L = FwdLds<D>;
   constexpr int KS = D / 16;  // k-steps of the S^T MFMA
   constexpr int DB = D / 32;  // 32-wide d blocks of O^T
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * L::kStage];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[L::kBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int half = lane >> 5;
+  const int g16 = lane & 15;
+  const int grp = lane >> 4;
 
   int bh, qt;
   fwd_tile_coords(blockIdx.x, BH, n_qtiles, CAUSAL, bh, qt);
@@ -100,36 +104,39 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int kv_end = CAUSAL ? min(N, (qt + 1) * kFwdBQ) : N;
   const int n_tiles = (kv_end + kFwdBK - 1) / kFwdBK;
 
-  // global -> register staging of one K/V tile
-  uint4 rk[L::kChunksPerThread], rv[L::kChunksPerThread];
-  auto load_tile = [&](int j) {
+  // ---- direct global -> LDS copy of one K/V tile into a stage.  Wave w
+  // fills rows [w * kDmaPerWave * kRowsPerDma, ...); lane l of an instruction
+  // writes physical chunk l % kChunksPerRow of its row, so it fetches the
+  // logical chunk that the swizzle maps there.  Rows past the end of the
+  // sequence re-read row N-1 (finite values that the mask gives weight 0).
+  const int dma_row0 = lane / L::kChunksPerRow;
+  const int dma_chunk = lane % L::kChunksPerRow;
+  auto load_tile = [&](int j, int st) {
+    ATTN_LDS unsigned char* kdst = (ATTN_LDS unsigned char*)smem + st * L::kStageBytes;
 #pragma unroll
-    for (int r = 0; r < L::kChunksPerThread; ++r) {
-      const int c = tid + r * kFwdThreads;
-      const int row = c / (D / 8);
-      const int col = (c % (D / 8)) * 8;
-      const int key = j * kFwdBK + row;
-      if (key < N) {
-        rk[r] = *reinterpret_cast<const uint4*>(kh + (int64_t)key * D + col);
-        rv[r] = *reinterpret_cast<const uint4*>(vh + (int64_t)key * D + col);
-      } else {
-        rk[r] = make_uint4(0, 0, 0, 0);
-        rv[r] = make_uint4(0, 0, 0, 0);
-      }
+    for (int i = 0; i < L::kDmaPerWave; ++i) {
+      const int row = (wave * L::kDmaPerWave + i) * L::kRowsPerDma + dma_row0;
+      const int key = min(j * kFwdBK + row, N - 1);
+      const int col = (dma_chunk ^ tile_swizzle<D>(row)) * 8;
+      const int boff = (wave * L::kDmaPerWave + i) * 1024;
+      lds_dma16(kh + (int64_t)key * D + col, kdst + boff);
+      lds_dma16(vh + (int64_t)key * D + col, kdst + L::kTileBytes + boff);
     }
   };
-  auto store_tile = [&](int st) {
-    __bf16* ks = smem + st * L::kStage;
-    __bf16* vs = ks + L::kElemsK;
-#pragma unroll
-    for (int r = 0; r < L::kChunksPerThread; ++r) {
-      const int c = tid + r * kFwdThreads;
-      const int row = c / (D / 8);
-      const int col = (c % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(ks + row * L::kStrideK + col) = rk[r];
-      *reinterpret_cast<uint4*>(vs + row * L::kStrideV + col) = rv[r];
-    }
-  };
+
+  // ---- per-lane LDS read addresses (byte offsets inside a stage).
+  // K rows (A operand of S^T): row kb*32 + l32, logical chunk 2 s + half:
+  //   address = (rowbase | ((half ^ sw) << 4)) ^ (32 s), + kb * 32 rows.
+  const int k_base = (l32 * L::kRowBytes) | (((half ^ tile_swizzle<D>(l32)) & (L::kChunksPerRow - 1)) << 4);
+  // V transpose reads: rows kb*32 + t*16 + half*4 + g16/4 (+8 for the upper
+  // four keys), logical chunk 4 b + cpart, byte 8 (g16 & 1) of the chunk:
+  //   address = (rowbase | ((cpart ^ sw) << 4) | 8 (g16 & 1)) ^ (64 b).
+  const int v_row = half * 4 + (g16 >> 2);
+  const int cpart = 2 * (grp & 1) + ((g16 & 3) >> 1);
+  const int v_base_lo = L::kTileBytes + v_row * L::kRowBytes +
+                        (((cpart ^ tile_swizzle<D>(v_row)) & (L::kChunksPerRow - 1)) << 4) + 8 * (g16 & 1);
+  const int v_base_hi = L::kTileBytes + (v_row + 8) * L::kRowBytes +
+                        (((cpart ^ tile_swizzle<D>(v_row + 8)) & (L::kChunksPerRow - 1)) << 4) + 8 * (g16 & 1);
 
   f32x16 oacc[DB];
 #pragma unroll
@@ -143,27 +150,24 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   float m_ref = -INFINITY;
   float l_run = 0.f;  // this lane's share of the running sum (its 32 keys per tile)
 
-  const int g16 = lane & 15;
-  const int grp = lane >> 4;
-
   // One K/V tile: S^T = K Q^T, online-softmax update, O^T += V^T P^T.
   // MASK selects the code path for tiles that straddle the causal diagonal or
   // the end of the sequence.
   auto tile_step = [&](const int key0, const int st, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const ATTN_LDS __bf16* ks = (const ATTN_LDS __bf16*)(smem + st * L::kStage);
-    const ATTN_LDS __bf16* vs = ks + L::kElemsK;
+    const ATTN_LDS unsigned char* sb = (const ATTN_LDS unsigned char*)smem + st * L::kStageBytes;
 
     // ---- S^T = K Q^T for the two 32-key halves (two independent MFMA chains)
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
+    for (int s = 0; s < KS; ++s) {
+      const int a_off = k_base ^ (32 * s);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(
-            ks + (kb * 32 + l32) * L::kStrideK + half * 8 + 16 * s);
+        const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(sb + a_off + kb * 32 * L::kRowBytes);
         sacc[kb] = mfma_32x32x16(a, qf[s], sacc[kb]);
       }
+    }
 
     if constexpr (MASK) {
 #pragma unroll
@@ -211,29 +215,28 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 
     // ---- O^T += V^T P^T: for each 16-key step, DB independent accumulators
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int b = 0; b < DB; ++b) {
+      const int lo = v_base_lo ^ (64 * b);
+      const int hi = v_base_hi ^ (64 * b);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int row = kb * 32 + t * 16 + half * 4 + (g16 >> 2);
-        bf16x8 va[DB];
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int b = 0; b < DB; ++b) {
-          const int col = b * 32 + (grp & 1) * 16 + 4 * (g16 & 3);
-          va[b] = concat4(lds_read_tr4(vs + row * L::kStrideV + col),
-                          lds_read_tr4(vs + (row + 8) * L::kStrideV + col));
+        for (int t = 0; t < 2; ++t) {
+          const int roff = (kb * 32 + t * 16) * L::kRowBytes;
+          const bf16x8 va = concat4(lds_read_tr4((const ATTN_LDS __bf16*)(sb + lo + roff)),
+                                    lds_read_tr4((const ATTN_LDS __bf16*)(sb + hi + roff)));
+          oacc[b] = mfma_32x32x16(va, pf[kb][t], oacc[b]);
         }
-#pragma unroll
-        for (int b = 0; b < DB; ++b) oacc[b] = mfma_32x32x16(va[b], pf[kb][t], oacc[b]);
-      }
+    }
   };
 
-  load_tile(0);
-  store_tile(0);
+  load_tile(0, 0);
+  wait_vmem();
   __syncthreads();
 
   for (int j = 0; j < n_tiles; ++j) {
     const int st = j & 1;
-    if (j + 1 < n_tiles) load_tile(j + 1);
+    if (j + 1 < n_tiles) load_tile(j + 1, st ^ 1);
     const int key0 = j * kFwdBK;
     // wave-uniform: the whole tile lies in this wave's future (nothing to add),
     // or it crosses the diagonal / the sequence end (masked path)
@@ -245,7 +248,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       else
         tile_step(key0, st, std::false_type{});
     }
-    if (j + 1 < n_tiles) store_tile(st ^ 1);
+    wait_vmem();
     __syncthreads();
   }
 

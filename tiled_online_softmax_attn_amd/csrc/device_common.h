@@ -16,6 +16,15 @@
 //
 //   v_permlane32_swap(x, x) returns {x of lanes 0-31 in both halves,
 //     x of lanes 32-63 in both halves}.
+//
+//   global_load_lds_dwordx4 (direct global -> LDS): lane l's 16 bytes land at
+//     LDS address M0 + 16 l, so one wave instruction fills 1 KiB of LDS in
+//     lane order.  The instruction's immediate offset moves the global AND the
+//     LDS address, so it is kept at 0.
+//
+// LDS banks: 64 banks of 4 bytes.  A ds_read_b128 is served 8 lanes at a
+// time and a ds_read_b64_tr_b16 16 lanes at a time; both are conflict-free
+// when the lanes served together touch distinct 16-byte bank groups.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -71,6 +80,37 @@ __device__ __forceinline__ float sum_across_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
                                             __builtin_bit_cast(unsigned, x), false, false);
   return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// Asynchronous copy of 16 bytes per lane from global memory to LDS.  `lds`
+// must be the same for every lane of the wave (it is the base of the 1 KiB
+// the wave writes); lane l's bytes land at lds + 16 l.
+__device__ __forceinline__ void lds_dma16(const void* src, ATTN_LDS void* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src, lds, 16, 0,
+                                   0);
+}
+
+// Wait until every outstanding global load of this wave (including LDS DMA)
+// has completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// XOR swizzle of the 16-byte chunks of a row-major bf16 tile of D columns
+// stored without padding (rows of 2*D bytes).  Logical chunk c of row r sits
+// at physical chunk c ^ tile_swizzle<D>(r).  The choice makes the two read
+// patterns of the kernels conflict-free:
+//   * ds_read_b128 of one chunk by 8 lanes on 8 consecutive rows, and
+//   * ds_read_b64_tr_b16 by 16 lanes on 4 consecutive rows (first row a
+//     multiple of 4) and 2 adjacent chunks (first chunk even).
+// D = 128 (16 chunks, one row = all 64 banks): 4 (r & 3) + ((r >> 2) & 3).
+// D = 64 (8 chunks, two rows per 64 banks): bit-reverse of (r >> 1) & 7.
+template <int D>
+__device__ __forceinline__ int tile_swizzle(int r) {
+  if constexpr (D == 128) {
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  } else {
+    const int x = (r >> 1) & 7;
+    return ((x & 1) << 2) | (x & 2) | ((x >> 2) & 1);
+  }
 }
 
 }  // namespace attn
