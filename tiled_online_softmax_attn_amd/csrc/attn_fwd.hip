@@ -39,17 +39,19 @@ constexpr int kFwdBK = 64;   // keys per K/V tile
 constexpr float kRescaleSlack = 8.f;  // log2 units: P never exceeds 2^8
 
 // K and V tiles of 64 keys, stored without padding and XOR-swizzled by
-// 16-byte chunk (tile_swizzle), double-buffered: [stage][K | V][64][D].
+// 16-byte chunk (tile_swizzle).  K and V each have two buffers; K runs one
+// tile ahead of V (see the loop): [K0 | K1 | V0 | V1], each [64][D].
 template <int D>
 struct FwdLds {
   static constexpr int kRowBytes = 2 * D;
   static constexpr int kTileBytes = kFwdBK * kRowBytes;
-  static constexpr int kStageBytes = 2 * kTileBytes;
-  static constexpr int kBytes = 2 * kStageBytes;
+  static constexpr int kBytes = 4 * kTileBytes;
   static constexpr int kRowsPerDma = 1024 / kRowBytes;                // rows per wave instruction
   static constexpr int kDmaPerWave = kFwdBK / kRowsPerDma / (kFwdThreads / 64);
   static constexpr int kChunksPerRow = D / 8;
   static_assert(kFwdBK % (kRowsPerDma * (kFwdThreads / 64)) == 0, "tile must split over waves");
+  static constexpr int k_buf(int b) { return b * kTileBytes; }
+  static constexpr int v_buf(int b) { return (2 + b) * kTileBytes; }
 };
 
 // Workgroup id -> (head, query tile).  Heavy causal tiles (late queries see
@@ -71,6 +73,11 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   using L = FwdLds<D>;
   constexpr int KS = D / 16;  // k-steps of the S^T MFMA
   constexpr int DB = D / 32;  // 32-wide d blocks of O^T
+  // d = 128: S^T of tile j+1 is computed during the softmax of tile j (the
+  // MFMA work per tile is large enough to hide the exponentials).  d = 64:
+  // S^T of a tile is computed at the start of its own step, which keeps the
+  // register count low enough for more waves per SIMD.
+  constexpr bool kPipelineQK = (D == 128) && CAUSAL;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[L::kBytes];
 
   const int tid = threadIdx.x;
@@ -104,27 +111,25 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int kv_end = CAUSAL ? min(N, (qt + 1) * kFwdBQ) : N;
   const int n_tiles = (kv_end + kFwdBK - 1) / kFwdBK;
 
-  // ---- direct global -> LDS copy of one K/V tile into a stage.  Wave w
+  // ---- direct global -> LDS copy of one 64-key tile of K or V.  Wave w
   // fills rows [w * kDmaPerWave * kRowsPerDma, ...); lane l of an instruction
   // writes physical chunk l % kChunksPerRow of its row, so it fetches the
   // logical chunk that the swizzle maps there.  Rows past the end of the
   // sequence re-read row N-1 (finite values that the mask gives weight 0).
   const int dma_row0 = lane / L::kChunksPerRow;
   const int dma_chunk = lane % L::kChunksPerRow;
-  auto load_tile = [&](int j, int st) {
-    ATTN_LDS unsigned char* kdst = (ATTN_LDS unsigned char*)smem + st * L::kStageBytes;
+  auto load_tile = [&](const __bf16* src, int j, int buf_off) {
+    ATTN_LDS unsigned char* dst = (ATTN_LDS unsigned char*)smem + buf_off;
 #pragma unroll
     for (int i = 0; i < L::kDmaPerWave; ++i) {
       const int row = (wave * L::kDmaPerWave + i) * L::kRowsPerDma + dma_row0;
       const int key = min(j * kFwdBK + row, N - 1);
       const int col = (dma_chunk ^ tile_swizzle<D>(row)) * 8;
-      const int boff = (wave * L::kDmaPerWave + i) * 1024;
-      lds_dma16(kh + (int64_t)key * D + col, kdst + boff);
-      lds_dma16(vh + (int64_t)key * D + col, kdst + L::kTileBytes + boff);
+      lds_dma16(src + (int64_t)key * D + col, dst + (wave * L::kDmaPerWave + i) * 1024);
     }
   };
 
-  // ---- per-lane LDS read addresses (byte offsets inside a stage).
+  // ---- per-lane LDS read addresses (byte offsets inside a tile buffer).
   // K rows (A operand of S^T): row kb*32 + l32, logical chunk 2 s + half:
   //   address = (rowbase | ((half ^ sw) << 4)) ^ (32 s), + kb * 32 rows.
   const int k_base = (l32 * L::kRowBytes) | (((half ^ tile_swizzle<D>(l32)) & (L::kChunksPerRow - 1)) << 4);
@@ -133,10 +138,27 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   //   address = (rowbase | ((cpart ^ sw) << 4) | 8 (g16 & 1)) ^ (64 b).
   const int v_row = half * 4 + (g16 >> 2);
   const int cpart = 2 * (grp & 1) + ((g16 & 3) >> 1);
-  const int v_base_lo = L::kTileBytes + v_row * L::kRowBytes +
+  const int v_base_lo = v_row * L::kRowBytes +
                         (((cpart ^ tile_swizzle<D>(v_row)) & (L::kChunksPerRow - 1)) << 4) + 8 * (g16 & 1);
-  const int v_base_hi = L::kTileBytes + (v_row + 8) * L::kRowBytes +
+  const int v_base_hi = (v_row + 8) * L::kRowBytes +
                         (((cpart ^ tile_swizzle<D>(v_row + 8)) & (L::kChunksPerRow - 1)) << 4) + 8 * (g16 & 1);
+
+  // S^T = K Q^T for the two 32-key halves of the K tile in buffer `kb_off`
+  // (two independent MFMA chains).
+  auto qk = [&](f32x16 (&sacc)[2], int kb_off) {
+    const ATTN_LDS unsigned char* kbuf = (const ATTN_LDS unsigned char*)smem + kb_off;
+    sacc[0] = f32x16{};
+    sacc[1] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int a_off = k_base ^ (32 * s);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(kbuf + a_off + kb * 32 * L::kRowBytes);
+        sacc[kb] = mfma_32x32x16(a, qf[s], sacc[kb]);
+      }
+    }
+  };
 
   f32x16 oacc[DB];
 #pragma unroll
@@ -150,41 +172,32 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   float m_ref = -INFINITY;
   float l_run = 0.f;  // this lane's share of the running sum (its 32 keys per tile)
 
-  // One K/V tile: S^T = K Q^T, online-softmax update, O^T += V^T P^T.
-  // MASK selects the code path for tiles that straddle the causal diagonal or
-  // the end of the sequence.
-  auto tile_step = [&](const int key0, const int st, auto mask_tag) {
+  // Tile j of the softmax pipeline.  On entry `sc` holds S^T of tile j; the
+  // step issues S^T of tile j+1 into `sn` (when NEXT) so that those MFMAs run
+  // while the VALU evaluates the exponentials of tile j, then adds
+  // V_j^T P_j^T to O^T.  MASK selects the path for tiles that straddle the
+  // causal diagonal or the end of the sequence.
+  auto step = [&](const int j, f32x16 (&sc)[2], f32x16 (&sn)[2], auto mask_tag, auto next_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const ATTN_LDS unsigned char* sb = (const ATTN_LDS unsigned char*)smem + st * L::kStageBytes;
-
-    // ---- S^T = K Q^T for the two 32-key halves (two independent MFMA chains)
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const int a_off = k_base ^ (32 * s);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(sb + a_off + kb * 32 * L::kRowBytes);
-        sacc[kb] = mfma_32x32x16(a, qf[s], sacc[kb]);
-      }
-    }
-
+    constexpr bool NEXT = kPipelineQK && decltype(next_tag)::value;
+    const int key0 = j * kFwdBK;
+    if constexpr (!kPipelineQK) qk(sc, L::k_buf(j & 1));
     if constexpr (MASK) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = key0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-          if (key >= N || (CAUSAL && key > qry)) sacc[kb][i] = -INFINITY;
+          if (key >= N || (CAUSAL && key > qry)) sc[kb][i] = -INFINITY;
         }
     }
 
     // ---- row maximum of this tile for the lane's query
-    float mx = sacc[0][0];
+    float mx = sc[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb][i]);
     mx = max_across_halves(mx) * scale_log2;
 
     // ---- move the reference maximum only when it is exceeded by the slack
@@ -200,20 +213,55 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
     const float m_off = (MASK && m_ref == -INFINITY) ? 0.f : m_ref;
 
-    // ---- P = 2^{s * scale * log2 e - m_ref}, rounded to bf16 as the B operand
+    // ---- P = 2^{s * scale * log2 e - m_ref} (bf16 B operand) on the VALU,
+    // interleaved in issue order with S^T of the next tile on the MFMA unit:
+    // k-step s issues the two MFMAs of that step (its K fragments were read
+    // one step earlier) and then the exponentials of 32 / KS scores.
     float psum = 0.f;
     bf16x8 pf[2][2];
+    auto exp_part = [&](int part) {
+      constexpr int PER = 32 / KS;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(fmaf(sacc[kb][i], scale_log2, -m_off));
+      for (int u = 0; u < PER; ++u) {
+        const int e = part * PER + u;
+        const int kb = e >> 4, i = e & 15;
+        const float p = fast_exp2(fmaf(sc[kb][i], scale_log2, -m_off));
+        // keep the exponential at this point of the issue order (it would
+        // otherwise sink below the MFMAs it is meant to overlap with)
+        __asm__ volatile("" ::"v"(p));
         psum += p;
         pf[kb][i >> 3][i & 7] = (__bf16)p;
       }
+    };
+    if constexpr (NEXT) {
+      const ATTN_LDS unsigned char* kbuf = (const ATTN_LDS unsigned char*)smem + L::k_buf((j + 1) & 1);
+      sn[0] = f32x16{};
+      sn[1] = f32x16{};
+      bf16x8 a[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        a[0][kb] = *reinterpret_cast<const ATTN_LDS bf16x8*>(kbuf + k_base + kb * 32 * L::kRowBytes);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        if (s + 1 < KS) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            a[(s + 1) & 1][kb] = *reinterpret_cast<const ATTN_LDS bf16x8*>(
+                kbuf + (k_base ^ (32 * (s + 1))) + kb * 32 * L::kRowBytes);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) sn[kb] = mfma_32x32x16(a[s & 1][kb], qf[s], sn[kb]);
+        exp_part(s);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) exp_part(s);
+    }
     l_run += psum;
 
     // ---- O^T += V^T P^T: for each 16-key step, DB independent accumulators
+    const ATTN_LDS unsigned char* vbuf = (const ATTN_LDS unsigned char*)smem + L::v_buf(j & 1);
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
       const int lo = v_base_lo ^ (64 * b);
@@ -223,33 +271,62 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const int roff = (kb * 32 + t * 16) * L::kRowBytes;
-          const bf16x8 va = concat4(lds_read_tr4((const ATTN_LDS __bf16*)(sb + lo + roff)),
-                                    lds_read_tr4((const ATTN_LDS __bf16*)(sb + hi + roff)));
+          const bf16x8 va = concat4(lds_read_tr4((const ATTN_LDS __bf16*)(vbuf + lo + roff)),
+                                    lds_read_tr4((const ATTN_LDS __bf16*)(vbuf + hi + roff)));
           oacc[b] = mfma_32x32x16(va, pf[kb][t], oacc[b]);
         }
     }
   };
 
-  load_tile(0, 0);
-  wait_vmem();
-  __syncthreads();
+  // Last tile this wave computes: under the causal mask, later tiles lie
+  // wholly in the future of all 32 of its queries (wave-uniform).
+  const int last_tile = CAUSAL ? min(n_tiles - 1, (q_wave0 + 31) / kFwdBK) : n_tiles - 1;
 
-  for (int j = 0; j < n_tiles; ++j) {
-    const int st = j & 1;
-    if (j + 1 < n_tiles) load_tile(j + 1, st ^ 1);
-    const int key0 = j * kFwdBK;
-    // wave-uniform: the whole tile lies in this wave's future (nothing to add),
-    // or it crosses the diagonal / the sequence end (masked path)
-    const bool skip = CAUSAL && key0 > q_wave0 + 31;
-    const bool need_mask = (key0 + kFwdBK > N) || (CAUSAL && key0 + kFwdBK - 1 > q_wave0);
-    if (!skip) {
-      if (need_mask)
-        tile_step(key0, st, std::true_type{});
-      else
-        tile_step(key0, st, std::false_type{});
+  // One iteration of the workgroup loop.  Buffers, pipelined: in iteration j
+  // the K tile j+1 and the V tile j are read; the copies of K tile j+2 (into
+  // the buffer of K tile j, last read in iteration j-1) and V tile j+1 (into
+  // the buffer of V tile j-1) are in flight meanwhile.  Not pipelined: K and
+  // V tile j are read and the copies of K and V tile j+1 are in flight.  The
+  // barrier at the end of every iteration publishes the copies.
+  auto iteration = [&](const int j, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    if constexpr (kPipelineQK) {
+      if (j + 2 < n_tiles) load_tile(kh, j + 2, L::k_buf(j & 1));
+    } else {
+      if (j + 1 < n_tiles) load_tile(kh, j + 1, L::k_buf((j + 1) & 1));
+    }
+    if (j + 1 < n_tiles) load_tile(vh, j + 1, L::v_buf((j + 1) & 1));
+    if (j <= last_tile) {
+      const int key0 = j * kFwdBK;
+      const bool need_mask = (key0 + kFwdBK > N) || (CAUSAL && key0 + kFwdBK - 1 > q_wave0);
+      const bool next = j < last_tile;
+      if (need_mask) {
+        if (next) step(j, sc, sn, std::true_type{}, std::true_type{});
+        else step(j, sc, sn, std::true_type{}, std::false_type{});
+      } else {
+        if (next) step(j, sc, sn, std::false_type{}, std::true_type{});
+        else step(j, sc, sn, std::false_type{}, std::false_type{});
+      }
     }
     wait_vmem();
     __syncthreads();
+  };
+
+  // prologue: K tiles 0 and 1 and V tile 0 in LDS (and, pipelined, S^T of
+  // tile 0 in registers)
+  load_tile(kh, 0, L::k_buf(0));
+  load_tile(vh, 0, L::v_buf(0));
+  if (kPipelineQK && n_tiles > 1) load_tile(kh, 1, L::k_buf(1));
+  wait_vmem();
+  __syncthreads();
+  f32x16 s_even[2], s_odd[2];
+  if constexpr (kPipelineQK) {
+    qk(s_even, L::k_buf(0));
+    __syncthreads();  // K buffer 0 is refilled in iteration 0
+  }
+
+  for (int j = 0; j < n_tiles; j += 2) {
+    iteration(j, s_even, s_odd);
+    if (j + 1 < n_tiles) iteration(j + 1, s_odd, s_even);
   }
 
   // ---- epilogue: O = O / l, lse = ln2 * (m + log2 l)
