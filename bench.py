@@ -108,6 +108,63 @@ def cpu_baseline(w, q, k, v, do, budget_s: float):
                       f"head, S and P materialised), {el:.1f} s"}
 
 
+def kernel_key(name: str):
+    """Map a device kernel name to the bench's kernel keys (None if foreign)."""
+    if "attn_fwd_bf16_kernel" in name:
+        return "fwd"
+    if "bwd_preprocess_kernel" in name:
+        return "bwd_preprocess"
+    if "bwd_dkdv_kernel" in name:
+        return "bwd_dkdv"
+    if "bwd_dq_kernel" in name:
+        return "bwd_dq"
+    if "MulFunctor" in name:  # the --copy-mib reference kernel (x * 1)
+        return "copy"
+    return None
+
+
+def pmc_summary(dirs, copy_mib: float, workload: str) -> int:
+    """Turn rocprofv3 FETCH_SIZE / WRITE_SIZE passes (counter_collection.csv
+    files under `dirs`) into profiles/traffic.json.  The plain copy kernel
+    that `--copy-mib` runs (reads and writes copy_mib MiB) calibrates each
+    counter: bytes = counter_KiB * 1024 * (known / measured on the copy)."""
+    import csv
+    import glob
+    sums = {}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    key = kernel_key(r["Kernel_Name"])
+                    if key is None:
+                        continue
+                    ent = sums.setdefault((key, r["Counter_Name"]), [])
+                    ent.append(float(r["Counter_Value"]))
+    avg = {k: sum(v) / len(v) for k, v in sums.items()}
+    known_kib = copy_mib * 1024.0
+    fetch_cal = known_kib / avg[("copy", "FETCH_SIZE")]
+    write_cal = known_kib / avg[("copy", "WRITE_SIZE")]
+    out = {"calibration": {"copy_mib": copy_mib,
+                           "copy_fetch_kib": avg[("copy", "FETCH_SIZE")],
+                           "copy_write_kib": avg[("copy", "WRITE_SIZE")],
+                           "fetch_factor": fetch_cal, "write_factor": write_cal}}
+    per = {}
+    for kn in KERNELS:
+        if (kn, "FETCH_SIZE") not in avg or (kn, "WRITE_SIZE") not in avg:
+            continue
+        per[kn] = {"fetch_bytes": avg[(kn, "FETCH_SIZE")] * 1024 * fetch_cal,
+                   "write_bytes": avg[(kn, "WRITE_SIZE")] * 1024 * write_cal,
+                   "fetch_kib_raw": avg[(kn, "FETCH_SIZE")],
+                   "write_kib_raw": avg[(kn, "WRITE_SIZE")],
+                   "source_digest": source_digest(kn)}
+    out[workload] = per
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,7 +173,17 @@ def main():
     ap.add_argument("--workload", default=None, help="workload name (default: the headline)")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=float, default=0.0,
+                    help="run one plain device copy of this many MiB before timing "
+                         "(reference kernel for the HBM byte counters)")
+    ap.add_argument("--pmc-summary", nargs="+", default=None, metavar="DIR",
+                    help="summarise rocprofv3 FETCH_SIZE/WRITE_SIZE passes into "
+                         "profiles/traffic.json and exit (needs --copy-mib of the profiled run)")
     args = ap.parse_args()
+
+    if args.pmc_summary:
+        from attn_inputs import HEADLINE
+        sys.exit(pmc_summary(args.pmc_summary, args.copy_mib, args.workload or HEADLINE))
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         eprint("bench.py: this build runs on exactly one GPU; multi-GPU runs are not "
@@ -155,6 +222,14 @@ def main():
                              stream)
             if events is not None:
                 events[2 + ph].record(stream)
+
+    if args.copy_mib > 0:
+        n = int(args.copy_mib * 1024 * 1024 // 4)
+        src = torch.ones(n, device=dev, dtype=torch.float32)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)  # reads and writes copy_mib MiB
+        torch.cuda.synchronize()
+        del src, dst
 
     eprint(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
