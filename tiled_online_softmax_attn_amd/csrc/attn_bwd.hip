@@ -21,6 +21,10 @@
 // B=4, H=16, N=4096, d=128.  Both kernels write their results exactly once,
 // so the backward is deterministic.
 //
+// Q/dO (dK/dV kernel) and K/V (dQ kernel) tiles of 64 rows go straight from
+// global memory to LDS (SwzTile: unpadded, XOR-swizzled chunks, read both by
+// rows and through the transpose read without bank conflicts).
+//
 // Register layouts (v_mfma_f32_32x32x16_bf16; see device_common.h):
 //   bwd_dkdv: S = Q K^T and dP = dO V^T with K^T / V^T fragments resident in
 //     registers; every lane owns one key.  dV += P^T dO and dK += dS^T Q take
@@ -66,18 +70,19 @@ bwd_preprocess_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ d
 
 // ---------------------------------------------------------------- phase 1
 constexpr int kKvBK = 128;  // keys per workgroup (32 per wave)
-constexpr int kKvBQ = 64;   // queries per inner step
+constexpr int kKvBQ = 64;   // queries per inner step (one SwzTile)
 
+// Q and dO tiles of 64 queries (SwzTile layout), two buffers each, then the
+// tiles' L (log2 units) and D values: [Q0 | Q1 | dO0 | dO1 | L[2][64] | D[2][64]].
 template <int D>
 struct DkdvLds {
-  static constexpr int kStride = D + 16;  // Q and dO tiles [query][d]: conflict-free b128 and transpose reads
-  static constexpr int kElems = kKvBQ * kStride;
-  static constexpr int kOffQ = 0;                 // [2][BQ][stride]
-  static constexpr int kOffDO = 2 * kElems;       // [2][BQ][stride]
-  static constexpr int kElemsBf16 = 4 * kElems;
-  static constexpr int kBytes = kElemsBf16 * 2 + 2 * 2 * kKvBQ * 4;  // + L, D [2][BQ] fp32
-  static constexpr int kChunksPerThread = kKvBQ * D / 8 / kBwdThreads;
-  static_assert(kKvBQ * D / 8 % kBwdThreads == 0, "tile must split evenly over threads");
+  static constexpr int kTileBytes = SwzTile<D>::kBytes;
+  static constexpr int q_buf(int b) { return b * kTileBytes; }
+  static constexpr int do_buf(int b) { return (2 + b) * kTileBytes; }
+  static constexpr int kOffL = 4 * kTileBytes;
+  static constexpr int kOffD = kOffL + 2 * kKvBQ * 4;
+  static constexpr int kBytes = kOffD + 2 * kKvBQ * 4;
+  static_assert(kKvBQ == SwzTile<D>::kRows, "query tile is one SwzTile");
 };
 
 template <int D, bool CAUSAL>
@@ -88,20 +93,19 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 __bf16* __restrict__ dk, __bf16* __restrict__ dv, int BH, int N, float scale,
                 float scale_log2) {
   using L = DkdvLds<D>;
+  using Tile = SwzTile<D>;
   constexpr int KS = D / 16;  // k-steps over d
   constexpr int DB = D / 32;  // 32-wide d blocks
-  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[L::kBytes];
-  __bf16* smem = reinterpret_cast<__bf16*>(smem_raw);
-  float* sm_l = reinterpret_cast<float*>(smem_raw + L::kElemsBf16 * 2);  // [2][BQ]
-  float* sm_d = sm_l + 2 * kKvBQ;                                      // [2][BQ]
+  constexpr int RB = Tile::kRowBytes;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[L::kBytes];
+  float* sm_l = reinterpret_cast<float*>(smem + L::kOffL);  // [2][BQ]
+  float* sm_d = reinterpret_cast<float*>(smem + L::kOffD);  // [2][BQ]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int half = lane >> 5;
-  const int g16 = lane & 15;
-  const int grp = lane >> 4;
 
   // workgroup id -> (head, key block); low key blocks meet the most queries
   // under the causal mask, so they are issued first
@@ -134,45 +138,28 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int n_qtiles = (N + kKvBQ - 1) / kKvBQ;
   const int qt_begin = CAUSAL ? key_wg0 / kKvBQ : 0;
 
-  uint4 rq[L::kChunksPerThread], rdo[L::kChunksPerThread];
+  // Q and dO tiles go straight to LDS; L (in log2 units) and D pass through
+  // one register each on the first 64 threads.
   float rl = 0.f, rd = 0.f;
-  auto load_tile = [&](int qt) {
-#pragma unroll
-    for (int r = 0; r < L::kChunksPerThread; ++r) {
-      const int c = tid + r * kBwdThreads;
-      const int row = c / (D / 8);
-      const int col = (c % (D / 8)) * 8;
-      const int qq = qt * kKvBQ + row;
-      if (qq < N) {
-        rq[r] = *reinterpret_cast<const uint4*>(qh + (int64_t)qq * D + col);
-        rdo[r] = *reinterpret_cast<const uint4*>(doh + (int64_t)qq * D + col);
-      } else {
-        rq[r] = make_uint4(0, 0, 0, 0);
-        rdo[r] = make_uint4(0, 0, 0, 0);
-      }
-    }
+  auto load_tile = [&](int qt, int b) {
+    Tile::template load<kBwdThreads / 64>(qh, qt * kKvBQ, N, (ATTN_LDS unsigned char*)smem + L::q_buf(b), wave, lane);
+    Tile::template load<kBwdThreads / 64>(doh, qt * kKvBQ, N, (ATTN_LDS unsigned char*)smem + L::do_buf(b), wave, lane);
     if (tid < kKvBQ) {
       const int qq = qt * kKvBQ + tid;
       rl = qq < N ? lse_h[qq] * kLog2e : 0.f;
       rd = qq < N ? del_h[qq] : 0.f;
     }
   };
-  auto store_tile = [&](int st) {
-    __bf16* qs = smem + L::kOffQ + st * L::kElems;
-    __bf16* ds = smem + L::kOffDO + st * L::kElems;
-#pragma unroll
-    for (int r = 0; r < L::kChunksPerThread; ++r) {
-      const int c = tid + r * kBwdThreads;
-      const int row = c / (D / 8);
-      const int col = (c % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(qs + row * L::kStride + col) = rq[r];
-      *reinterpret_cast<uint4*>(ds + row * L::kStride + col) = rdo[r];
-    }
+  auto store_stats = [&](int b) {
     if (tid < kKvBQ) {
-      sm_l[st * kKvBQ + tid] = rl;
-      sm_d[st * kKvBQ + tid] = rd;
+      sm_l[b * kKvBQ + tid] = rl;
+      sm_d[b * kKvBQ + tid] = rd;
     }
   };
+
+  const int rd_base = Tile::row_read_base(l32, half);
+  const int tr_lo = Tile::tr_read_base(lane, false);
+  const int tr_hi = Tile::tr_read_base(lane, true);
 
   f32x16 dk_acc[DB], dv_acc[DB];
 #pragma unroll
@@ -182,21 +169,22 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   }
 
   if (qt_begin < n_qtiles) {
-    load_tile(qt_begin);
-    store_tile(0);
+    load_tile(qt_begin, 0);
+    store_stats(0);
   }
+  wait_vmem();
   __syncthreads();
 
   for (int qt = qt_begin; qt < n_qtiles; ++qt) {
     const int st = (qt - qt_begin) & 1;
-    if (qt + 1 < n_qtiles) load_tile(qt + 1);
+    if (qt + 1 < n_qtiles) load_tile(qt + 1, st ^ 1);
 
     const int q0 = qt * kKvBQ;
     // wave-uniform: every query of the tile precedes every key of this wave
     const bool skip = CAUSAL && (q0 + kKvBQ - 1 < key_w0);
     if (!skip) {
-      const ATTN_LDS __bf16* qs = (const ATTN_LDS __bf16*)(smem + L::kOffQ + st * L::kElems);
-      const ATTN_LDS __bf16* dos = (const ATTN_LDS __bf16*)(smem + L::kOffDO + st * L::kElems);
+      const ATTN_LDS unsigned char* qs = (const ATTN_LDS unsigned char*)smem + L::q_buf(st);
+      const ATTN_LDS unsigned char* dos = (const ATTN_LDS unsigned char*)smem + L::do_buf(st);
       const float* lq = sm_l + st * kKvBQ;
       const float* dq_d = sm_d + st * kKvBQ;
       const bool need_mask =
@@ -206,15 +194,16 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       f32x16 sacc[2] = {f32x16{}, f32x16{}};
       f32x16 pacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
+      for (int s = 0; s < KS; ++s) {
+        const int off = rd_base ^ (32 * s);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-          const int off = (qb * 32 + l32) * L::kStride + half * 8 + 16 * s;
-          const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(qs + off);
+          const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(qs + off + qb * 32 * RB);
           sacc[qb] = mfma_32x32x16(a, kf[s], sacc[qb]);
-          const bf16x8 b = *reinterpret_cast<const ATTN_LDS bf16x8*>(dos + off);
+          const bf16x8 b = *reinterpret_cast<const ATTN_LDS bf16x8*>(dos + off + qb * 32 * RB);
           pacc[qb] = mfma_32x32x16(b, vf[s], pacc[qb]);
         }
+      }
 
       // ---- P = 2^{S scale log2e - L log2e};  dS = P (dP - D)
 #pragma unroll
@@ -239,7 +228,7 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
           }
         }
 
-      // ---- dV += P^T dO ; dK += dS^T Q
+      // ---- dV += P^T dO ; dK += dS^T Q   (B operands by transpose reads)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -250,21 +239,23 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             pa[e] = (__bf16)sacc[qb][t * 8 + e];
             sa[e] = (__bf16)pacc[qb][t * 8 + e];
           }
-          const int row = qb * 32 + t * 16 + half * 4 + (g16 >> 2);
+          const int roff = (qb * 32 + t * 16) * RB;
 #pragma unroll
           for (int b = 0; b < DB; ++b) {
-            const int col = b * 32 + (grp & 1) * 16 + 4 * (g16 & 3);
-            const bf16x8 dob = concat4(lds_read_tr4(dos + row * L::kStride + col),
-                                       lds_read_tr4(dos + (row + 8) * L::kStride + col));
+            const int lo = (tr_lo ^ (64 * b)) + roff;
+            const int hi = (tr_hi ^ (64 * b)) + roff;
+            const bf16x8 dob = concat4(lds_read_tr4((const ATTN_LDS __bf16*)(dos + lo)),
+                                       lds_read_tr4((const ATTN_LDS __bf16*)(dos + hi)));
             dv_acc[b] = mfma_32x32x16(pa, dob, dv_acc[b]);
-            const bf16x8 qbv = concat4(lds_read_tr4(qs + row * L::kStride + col),
-                                       lds_read_tr4(qs + (row + 8) * L::kStride + col));
+            const bf16x8 qbv = concat4(lds_read_tr4((const ATTN_LDS __bf16*)(qs + lo)),
+                                       lds_read_tr4((const ATTN_LDS __bf16*)(qs + hi)));
             dk_acc[b] = mfma_32x32x16(sa, qbv, dk_acc[b]);
           }
         }
     }
 
-    if (qt + 1 < n_qtiles) store_tile(st ^ 1);
+    if (qt + 1 < n_qtiles) store_stats(st ^ 1);
+    wait_vmem();
     __syncthreads();
   }
 
@@ -285,17 +276,17 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 
 // ---------------------------------------------------------------- phase 2
 constexpr int kDqBQ = 128;  // queries per workgroup (32 per wave)
-constexpr int kDqBK = 64;   // keys per K/V tile
+constexpr int kDqBK = 64;   // keys per K/V tile (one SwzTile)
 
+// K and V tiles of 64 keys (SwzTile layout), two buffers each:
+// [K0 | K1 | V0 | V1].  K is read both by rows (S^T) and transposed (dQ^T).
 template <int D>
 struct DqLds {
-  static constexpr int kStrideK = D + 16;  // b128 row reads and transpose reads
-  static constexpr int kStrideV = D + 8;   // b128 row reads only
-  static constexpr int kElemsK = kDqBK * kStrideK;
-  static constexpr int kElemsV = kDqBK * kStrideV;
-  static constexpr int kStage = kElemsK + kElemsV;
-  static constexpr int kChunksPerThread = kDqBK * D / 8 / kBwdThreads;
-  static_assert(kDqBK * D / 8 % kBwdThreads == 0, "tile must split evenly over threads");
+  static constexpr int kTileBytes = SwzTile<D>::kBytes;
+  static constexpr int k_buf(int b) { return b * kTileBytes; }
+  static constexpr int v_buf(int b) { return (2 + b) * kTileBytes; }
+  static constexpr int kBytes = 4 * kTileBytes;
+  static_assert(kDqBK == SwzTile<D>::kRows, "key tile is one SwzTile");
 };
 
 template <int D, bool CAUSAL>
@@ -306,17 +297,17 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
               __bf16* __restrict__ dq, int BH, int N, int n_qtiles, float scale,
               float scale_log2) {
   using L = DqLds<D>;
+  using Tile = SwzTile<D>;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * L::kStage];
+  constexpr int RB = Tile::kRowBytes;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[L::kBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int half = lane >> 5;
-  const int g16 = lane & 15;
-  const int grp = lane >> 4;
 
   // workgroup id -> (head, query tile), heavy causal tiles first
   const int rank = blockIdx.x / BH;
@@ -347,68 +338,46 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int kv_end = CAUSAL ? min(N, (qt + 1) * kDqBQ) : N;
   const int n_tiles = (kv_end + kDqBK - 1) / kDqBK;
 
-  uint4 rk[L::kChunksPerThread], rv[L::kChunksPerThread];
-  auto load_tile = [&](int j) {
-#pragma unroll
-    for (int r = 0; r < L::kChunksPerThread; ++r) {
-      const int c = tid + r * kBwdThreads;
-      const int row = c / (D / 8);
-      const int col = (c % (D / 8)) * 8;
-      const int kk = j * kDqBK + row;
-      if (kk < N) {
-        rk[r] = *reinterpret_cast<const uint4*>(kh + (int64_t)kk * D + col);
-        rv[r] = *reinterpret_cast<const uint4*>(vh + (int64_t)kk * D + col);
-      } else {
-        rk[r] = make_uint4(0, 0, 0, 0);
-        rv[r] = make_uint4(0, 0, 0, 0);
-      }
-    }
+  auto load_tile = [&](int j, int b) {
+    Tile::template load<kBwdThreads / 64>(kh, j * kDqBK, N, (ATTN_LDS unsigned char*)smem + L::k_buf(b), wave, lane);
+    Tile::template load<kBwdThreads / 64>(vh, j * kDqBK, N, (ATTN_LDS unsigned char*)smem + L::v_buf(b), wave, lane);
   };
-  auto store_tile = [&](int st) {
-    __bf16* ks = smem + st * L::kStage;
-    __bf16* vs = ks + L::kElemsK;
-#pragma unroll
-    for (int r = 0; r < L::kChunksPerThread; ++r) {
-      const int c = tid + r * kBwdThreads;
-      const int row = c / (D / 8);
-      const int col = (c % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(ks + row * L::kStrideK + col) = rk[r];
-      *reinterpret_cast<uint4*>(vs + row * L::kStrideV + col) = rv[r];
-    }
-  };
+  const int rd_base = Tile::row_read_base(l32, half);
+  const int tr_lo = Tile::tr_read_base(lane, false);
+  const int tr_hi = Tile::tr_read_base(lane, true);
 
   f32x16 dq_acc[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b) dq_acc[b] = f32x16{};
 
-  load_tile(0);
-  store_tile(0);
+  load_tile(0, 0);
+  wait_vmem();
   __syncthreads();
 
   for (int j = 0; j < n_tiles; ++j) {
     const int st = j & 1;
-    if (j + 1 < n_tiles) load_tile(j + 1);
+    if (j + 1 < n_tiles) load_tile(j + 1, st ^ 1);
     const int key0 = j * kDqBK;
     const bool skip = CAUSAL && key0 > q_wave0 + 31;
     if (!skip) {
-      const ATTN_LDS __bf16* ks = (const ATTN_LDS __bf16*)(smem + st * L::kStage);
-      const ATTN_LDS __bf16* vs = ks + L::kElemsK;
+      const ATTN_LDS unsigned char* ks = (const ATTN_LDS unsigned char*)smem + L::k_buf(st);
+      const ATTN_LDS unsigned char* vs = (const ATTN_LDS unsigned char*)smem + L::v_buf(st);
       const bool need_mask = (key0 + kDqBK > N) || (CAUSAL && key0 + kDqBK - 1 > q_wave0);
 
       // ---- S^T = K Q^T and dP^T = V dO^T for two 32-key halves
       f32x16 sacc[2] = {f32x16{}, f32x16{}};
       f32x16 pacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
+      for (int s = 0; s < KS; ++s) {
+        const int off = rd_base ^ (32 * s);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(
-              ks + (kb * 32 + l32) * L::kStrideK + half * 8 + 16 * s);
+          const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(ks + off + kb * 32 * RB);
           sacc[kb] = mfma_32x32x16(a, qf[s], sacc[kb]);
-          const bf16x8 b = *reinterpret_cast<const ATTN_LDS bf16x8*>(
-              vs + (kb * 32 + l32) * L::kStrideV + half * 8 + 16 * s);
+          const bf16x8 b = *reinterpret_cast<const ATTN_LDS bf16x8*>(vs + off + kb * 32 * RB);
           pacc[kb] = mfma_32x32x16(b, df[s], pacc[kb]);
         }
+      }
 
       // ---- P^T = 2^{S^T scale log2e - L}; dS^T = P^T (dP^T - D), as bf16 B operand
       bf16x8 sf[2][2];
@@ -424,22 +393,23 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
           sf[kb][i >> 3][i & 7] = (__bf16)(p * (pacc[kb][i] - dlt));
         }
 
-      // ---- dQ^T += K^T dS^T
+      // ---- dQ^T += K^T dS^T (K^T by transpose reads of the K tile)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int b = 0; b < DB; ++b) {
+        const int lo = tr_lo ^ (64 * b);
+        const int hi = tr_hi ^ (64 * b);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int row = kb * 32 + t * 16 + half * 4 + (g16 >> 2);
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int b = 0; b < DB; ++b) {
-            const int col = b * 32 + (grp & 1) * 16 + 4 * (g16 & 3);
-            const bf16x8 ka = concat4(lds_read_tr4(ks + row * L::kStrideK + col),
-                                      lds_read_tr4(ks + (row + 8) * L::kStrideK + col));
+          for (int t = 0; t < 2; ++t) {
+            const int roff = (kb * 32 + t * 16) * RB;
+            const bf16x8 ka = concat4(lds_read_tr4((const ATTN_LDS __bf16*)(ks + lo + roff)),
+                                      lds_read_tr4((const ATTN_LDS __bf16*)(ks + hi + roff)));
             dq_acc[b] = mfma_32x32x16(ka, sf[kb][t], dq_acc[b]);
           }
-        }
+      }
     }
-    if (j + 1 < n_tiles) store_tile(st ^ 1);
+    wait_vmem();
     __syncthreads();
   }
 

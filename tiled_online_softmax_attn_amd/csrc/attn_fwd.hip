@@ -38,18 +38,14 @@ constexpr int kFwdBQ = 128;  // queries per workgroup
 constexpr int kFwdBK = 64;   // keys per K/V tile
 constexpr float kRescaleSlack = 8.f;  // log2 units: P never exceeds 2^8
 
-// K and V tiles of 64 keys, stored without padding and XOR-swizzled by
-// 16-byte chunk (tile_swizzle).  K and V each have two buffers; K runs one
-// tile ahead of V (see the loop): [K0 | K1 | V0 | V1], each [64][D].
+// K and V tiles of 64 keys (SwzTile layout).  K and V each have two
+// buffers: [K0 | K1 | V0 | V1].
 template <int D>
 struct FwdLds {
   static constexpr int kRowBytes = 2 * D;
-  static constexpr int kTileBytes = kFwdBK * kRowBytes;
+  static constexpr int kTileBytes = SwzTile<D>::kBytes;
   static constexpr int kBytes = 4 * kTileBytes;
-  static constexpr int kRowsPerDma = 1024 / kRowBytes;                // rows per wave instruction
-  static constexpr int kDmaPerWave = kFwdBK / kRowsPerDma / (kFwdThreads / 64);
-  static constexpr int kChunksPerRow = D / 8;
-  static_assert(kFwdBK % (kRowsPerDma * (kFwdThreads / 64)) == 0, "tile must split over waves");
+  static_assert(kFwdBK == SwzTile<D>::kRows, "K/V tile is one SwzTile");
   static constexpr int k_buf(int b) { return b * kTileBytes; }
   static constexpr int v_buf(int b) { return (2 + b) * kTileBytes; }
 };
@@ -85,8 +81,6 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int half = lane >> 5;
-  const int g16 = lane & 15;
-  const int grp = lane >> 4;
 
   int bh, qt;
   fwd_tile_coords(blockIdx.x, BH, n_qtiles, CAUSAL, bh, qt);
@@ -111,37 +105,15 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int kv_end = CAUSAL ? min(N, (qt + 1) * kFwdBQ) : N;
   const int n_tiles = (kv_end + kFwdBK - 1) / kFwdBK;
 
-  // ---- direct global -> LDS copy of one 64-key tile of K or V.  Wave w
-  // fills rows [w * kDmaPerWave * kRowsPerDma, ...); lane l of an instruction
-  // writes physical chunk l % kChunksPerRow of its row, so it fetches the
-  // logical chunk that the swizzle maps there.  Rows past the end of the
-  // sequence re-read row N-1 (finite values that the mask gives weight 0).
-  const int dma_row0 = lane / L::kChunksPerRow;
-  const int dma_chunk = lane % L::kChunksPerRow;
+  using Tile = SwzTile<D>;
   auto load_tile = [&](const __bf16* src, int j, int buf_off) {
-    ATTN_LDS unsigned char* dst = (ATTN_LDS unsigned char*)smem + buf_off;
-#pragma unroll
-    for (int i = 0; i < L::kDmaPerWave; ++i) {
-      const int row = (wave * L::kDmaPerWave + i) * L::kRowsPerDma + dma_row0;
-      const int key = min(j * kFwdBK + row, N - 1);
-      const int col = (dma_chunk ^ tile_swizzle<D>(row)) * 8;
-      lds_dma16(src + (int64_t)key * D + col, dst + (wave * L::kDmaPerWave + i) * 1024);
-    }
+    Tile::template load<kFwdThreads / 64>(src, j * kFwdBK, N,
+                                          (ATTN_LDS unsigned char*)smem + buf_off, wave, lane);
   };
-
-  // ---- per-lane LDS read addresses (byte offsets inside a tile buffer).
-  // K rows (A operand of S^T): row kb*32 + l32, logical chunk 2 s + half:
-  //   address = (rowbase | ((half ^ sw) << 4)) ^ (32 s), + kb * 32 rows.
-  const int k_base = (l32 * L::kRowBytes) | (((half ^ tile_swizzle<D>(l32)) & (L::kChunksPerRow - 1)) << 4);
-  // V transpose reads: rows kb*32 + t*16 + half*4 + g16/4 (+8 for the upper
-  // four keys), logical chunk 4 b + cpart, byte 8 (g16 & 1) of the chunk:
-  //   address = (rowbase | ((cpart ^ sw) << 4) | 8 (g16 & 1)) ^ (64 b).
-  const int v_row = half * 4 + (g16 >> 2);
-  const int cpart = 2 * (grp & 1) + ((g16 & 3) >> 1);
-  const int v_base_lo = v_row * L::kRowBytes +
-                        (((cpart ^ tile_swizzle<D>(v_row)) & (L::kChunksPerRow - 1)) << 4) + 8 * (g16 & 1);
-  const int v_base_hi = (v_row + 8) * L::kRowBytes +
-                        (((cpart ^ tile_swizzle<D>(v_row + 8)) & (L::kChunksPerRow - 1)) << 4) + 8 * (g16 & 1);
+  // per-lane LDS read offsets: K rows (A operand of S^T) and V transpose reads
+  const int k_base = Tile::row_read_base(l32, half);
+  const int v_base_lo = Tile::tr_read_base(lane, false);
+  const int v_base_hi = Tile::tr_read_base(lane, true);
 
   // S^T = K Q^T for the two 32-key halves of the K tile in buffer `kb_off`
   // (two independent MFMA chains).

@@ -113,4 +113,57 @@ __device__ __forceinline__ int tile_swizzle(int r) {
   }
 }
 
+// A 64-row tile of a row-major [rows][D] bf16 matrix held in LDS without
+// padding, its 16-byte chunks XOR-swizzled by row (tile_swizzle<D>).
+template <int D>
+struct SwzTile {
+  static constexpr int kRows = 64;
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kBytes = kRows * kRowBytes;
+  static constexpr int kRowsPerDma = 1024 / kRowBytes;  // rows one wave instruction fills
+  static constexpr int kChunksPerRow = D / 8;
+
+  // Copy rows [row0, row0 + 64) of `src` (row stride D elements) into `dst`
+  // using the NW waves of the workgroup.  Lane l of an instruction writes
+  // physical chunk l % kChunksPerRow of its row, so it fetches the logical
+  // chunk the swizzle maps there.  Rows at or past `nrows` re-read row
+  // nrows - 1 (finite values that the callers' masks give weight 0).
+  template <int NW>
+  static __device__ __forceinline__ void load(const __bf16* src, int row0, int nrows,
+                                              ATTN_LDS unsigned char* dst, int wave, int lane) {
+    constexpr int kPerWave = kRows / kRowsPerDma / NW;
+    static_assert(kRows % (kRowsPerDma * NW) == 0, "tile must split over the waves");
+    const int r_in = lane / kChunksPerRow;
+    const int chunk = lane % kChunksPerRow;
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int blk = wave * kPerWave + i;
+      const int row = blk * kRowsPerDma + r_in;
+      const int g = min(row0 + row, nrows - 1);
+      const int col = (chunk ^ tile_swizzle<D>(row)) * 8;
+      lds_dma16(src + (int64_t)g * D + col, dst + blk * 1024);
+    }
+  }
+
+  // Row reads (MFMA operand with one tile row per lane): lane reads row
+  // rb * 32 + l32, logical chunk 2 s + half.  Byte offset:
+  //   (row_read_base(l32, half) ^ (32 s)) + rb * 32 * kRowBytes.
+  static __device__ __forceinline__ int row_read_base(int l32, int half) {
+    return (l32 * kRowBytes) | (((half ^ tile_swizzle<D>(l32)) & (kChunksPerRow - 1)) << 4);
+  }
+
+  // Transpose reads (ds_read_b64_tr_b16): lane (group grp = lane / 16,
+  // g16 = lane % 16) points at row r0 + half * 4 + g16 / 4 (+ 8 for `hi`),
+  // columns 32 b + 16 (grp & 1) + 4 (g16 & 3), for r0 a multiple of 16.
+  // Byte offset: (tr_read_base(lane, hi) ^ (64 b)) + r0 * kRowBytes.
+  static __device__ __forceinline__ int tr_read_base(int lane, bool hi) {
+    const int g16 = lane & 15;
+    const int grp = lane >> 4;
+    const int row = (grp >> 1) * 4 + (g16 >> 2) + (hi ? 8 : 0);
+    const int cpart = 2 * (grp & 1) + ((g16 & 3) >> 1);
+    return row * kRowBytes + (((cpart ^ tile_swizzle<D>(row)) & (kChunksPerRow - 1)) << 4) +
+           8 * (g16 & 1);
+  }
+};
+
 }  // namespace attn
