@@ -36,6 +36,8 @@
 #include "device_common.h"
 #include "attn_launch.h"
 
+#include <type_traits>
+
 namespace attn {
 namespace {
 
@@ -190,68 +192,105 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       const bool need_mask =
           (q0 + kKvBQ > N) || (key_w0 + 32 > N) || (CAUSAL && q0 < key_w0 + 31);
 
-      // ---- S = Q K^T and dP = dO V^T for two 32-query blocks
+      // The tile's 64 queries are two 32-query blocks qb = 0, 1.  The issue
+      // order is software-pipelined across them so that MFMA and VALU work
+      // of the one wave overlap:
+      //   A  S, dP of block 0                      (MFMA)
+      //   B  S, dP of block 1   |  P, dS of block 0 (VALU)
+      //   C  dV, dK of block 0  |  P, dS of block 1
+      //   D  dV, dK of block 1
       f32x16 sacc[2] = {f32x16{}, f32x16{}};
       f32x16 pacc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int off = rd_base ^ (32 * s);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(qs + off + qb * 32 * RB);
-          sacc[qb] = mfma_32x32x16(a, kf[s], sacc[qb]);
-          const bf16x8 b = *reinterpret_cast<const ATTN_LDS bf16x8*>(dos + off + qb * 32 * RB);
-          pacc[qb] = mfma_32x32x16(b, vf[s], pacc[qb]);
-        }
-      }
+      bf16x8 pa[2][2], sa[2][2];
 
-      // ---- P = 2^{S scale log2e - L log2e};  dS = P (dP - D)
+      // S = Q K^T and dP = dO V^T, k-step s of block qb
+      auto sdp_step = [&](int qb, int s) {
+        const int off = (rd_base ^ (32 * s)) + qb * 32 * RB;
+        const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(qs + off);
+        sacc[qb] = mfma_32x32x16(a, kf[s], sacc[qb]);
+        const bf16x8 b = *reinterpret_cast<const ATTN_LDS bf16x8*>(dos + off);
+        pacc[qb] = mfma_32x32x16(b, vf[s], pacc[qb]);
+      };
+      // P = 2^{S scale log2e - L log2e} and dS = P (dP - D) for the 4 query
+      // rows qb*32 + r*8 + half*4 + e of the lane's key
+      auto soft_part = [&](int qb, int r, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        const int qrow0 = qb * 32 + r * 8 + half * 4;
+        const float4 l4 = *reinterpret_cast<const float4*>(lq + qrow0);
+        const float4 d4 = *reinterpret_cast<const float4*>(dq_d + qrow0);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int qrow0 = qb * 32 + r * 8 + half * 4;  // 4 consecutive query rows
-          const float4 l4 = *reinterpret_cast<const float4*>(lq + qrow0);
-          const float4 d4 = *reinterpret_cast<const float4*>(dq_d + qrow0);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-          const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = r * 4 + e;
-            float p = fast_exp2(fmaf(sacc[qb][i], scale_log2, -lv[e]));
-            if (need_mask) {
-              const int qq = q0 + qrow0 + e;
-              if (qq >= N || key >= N || (CAUSAL && key > qq)) p = 0.f;
-            }
-            sacc[qb][i] = p;
-            pacc[qb][i] = p * (pacc[qb][i] - dv4[e]);
+        for (int e = 0; e < 4; ++e) {
+          const int i = r * 4 + e;
+          float p = fast_exp2(fmaf(sacc[qb][i], scale_log2, -lv[e]));
+          if constexpr (MASK) {
+            const int qq = q0 + qrow0 + e;
+            if (qq >= N || key >= N || (CAUSAL && key > qq)) p = 0.f;
           }
+          // keep the exponential at this point of the issue order
+          __asm__ volatile("" ::"v"(p));
+          sacc[qb][i] = p;
+          pacc[qb][i] = p * (pacc[qb][i] - dv4[e]);
         }
-
-      // ---- dV += P^T dO ; dK += dS^T Q   (B operands by transpose reads)
+      };
+      // P^T and dS^T of block qb as bf16 A operands (16 queries per t)
+      auto to_bf16 = [&](int qb) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          bf16x8 pa, sa;
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            pa[e] = (__bf16)sacc[qb][t * 8 + e];
-            sa[e] = (__bf16)pacc[qb][t * 8 + e];
+            pa[qb][t][e] = (__bf16)sacc[qb][t * 8 + e];
+            sa[qb][t][e] = (__bf16)pacc[qb][t * 8 + e];
           }
-          const int roff = (qb * 32 + t * 16) * RB;
+      };
+      // dV += P^T dO and dK += dS^T Q for 16 queries (t) and 32 d columns (b)
+      auto dvdk_step = [&](int qb, int t, int b) {
+        const int roff = (qb * 32 + t * 16) * RB;
+        const int lo = (tr_lo ^ (64 * b)) + roff;
+        const int hi = (tr_hi ^ (64 * b)) + roff;
+        const bf16x8 dob = concat4(lds_read_tr4((const ATTN_LDS __bf16*)(dos + lo)),
+                                   lds_read_tr4((const ATTN_LDS __bf16*)(dos + hi)));
+        dv_acc[b] = mfma_32x32x16(pa[qb][t], dob, dv_acc[b]);
+        const bf16x8 qbv = concat4(lds_read_tr4((const ATTN_LDS __bf16*)(qs + lo)),
+                                   lds_read_tr4((const ATTN_LDS __bf16*)(qs + hi)));
+        dk_acc[b] = mfma_32x32x16(sa[qb][t], qbv, dk_acc[b]);
+      };
+
+      auto body = [&](auto mask_tag) {
+        // A
 #pragma unroll
-          for (int b = 0; b < DB; ++b) {
-            const int lo = (tr_lo ^ (64 * b)) + roff;
-            const int hi = (tr_hi ^ (64 * b)) + roff;
-            const bf16x8 dob = concat4(lds_read_tr4((const ATTN_LDS __bf16*)(dos + lo)),
-                                       lds_read_tr4((const ATTN_LDS __bf16*)(dos + hi)));
-            dv_acc[b] = mfma_32x32x16(pa, dob, dv_acc[b]);
-            const bf16x8 qbv = concat4(lds_read_tr4((const ATTN_LDS __bf16*)(qs + lo)),
-                                       lds_read_tr4((const ATTN_LDS __bf16*)(qs + hi)));
-            dk_acc[b] = mfma_32x32x16(sa, qbv, dk_acc[b]);
-          }
+        for (int s = 0; s < KS; ++s) sdp_step(0, s);
+        __builtin_amdgcn_sched_barrier(0);
+        // B: KS k-steps of block 1; softmax part r of block 0 after step r*KS/4
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          sdp_step(1, s);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (r * KS / 4 == s) soft_part(0, r, mask_tag);
+          __builtin_amdgcn_sched_barrier(0);
         }
+        to_bf16(0);
+        // C: 2*DB steps of block 0's dV/dK; softmax part r of block 1 after
+        // step r*2*DB/4
+#pragma unroll
+        for (int u = 0; u < 2 * DB; ++u) {
+          dvdk_step(0, u / DB, u % DB);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (r * 2 * DB / 4 == u) soft_part(1, r, mask_tag);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        to_bf16(1);
+        // D
+#pragma unroll
+        for (int u = 0; u < 2 * DB; ++u) dvdk_step(1, u / DB, u % DB);
+      };
+      if (need_mask)
+        body(std::true_type{});
+      else
+        body(std::false_type{});
     }
 
     if (qt + 1 < n_qtiles) store_stats(st ^ 1);
