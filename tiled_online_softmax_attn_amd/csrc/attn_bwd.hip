@@ -339,6 +339,7 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   using Tile = SwzTile<D>;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
+  constexpr bool kPipelineHalves = (D == 64);
   constexpr int RB = Tile::kRowBytes;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[L::kBytes];
 
@@ -403,49 +404,128 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       const ATTN_LDS unsigned char* vs = (const ATTN_LDS unsigned char*)smem + L::v_buf(st);
       const bool need_mask = (key0 + kDqBK > N) || (CAUSAL && key0 + kDqBK - 1 > q_wave0);
 
-      // ---- S^T = K Q^T and dP^T = V dO^T for two 32-key halves
-      f32x16 sacc[2] = {f32x16{}, f32x16{}};
-      f32x16 pacc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int off = rd_base ^ (32 * s);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(ks + off + kb * 32 * RB);
+      if constexpr (kPipelineHalves) {
+        // The tile's 64 keys are two 32-key halves kb = 0, 1.  At d = 64 they
+        // are software-pipelined like the dK/dV kernel's query blocks (at
+        // d = 128 the pipelined order needs more registers than two waves per
+        // SIMD allow, and the plain order measured as fast):
+        //   A  S^T, dP^T of half 0                       (MFMA)
+        //   B  S^T, dP^T of half 1 |  P^T, dS^T of half 0 (VALU)
+        //   C  dQ^T of half 0      |  P^T, dS^T of half 1
+        //   D  dQ^T of half 1
+        f32x16 sacc[2] = {f32x16{}, f32x16{}};
+        f32x16 pacc[2] = {f32x16{}, f32x16{}};
+        bf16x8 sf[2][2];
+
+        // S^T = K Q^T and dP^T = V dO^T, k-step s of half kb
+        auto sdp_step = [&](int kb, int s) {
+          const int off = (rd_base ^ (32 * s)) + kb * 32 * RB;
+          const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(ks + off);
           sacc[kb] = mfma_32x32x16(a, qf[s], sacc[kb]);
-          const bf16x8 b = *reinterpret_cast<const ATTN_LDS bf16x8*>(vs + off + kb * 32 * RB);
+          const bf16x8 b = *reinterpret_cast<const ATTN_LDS bf16x8*>(vs + off);
           pacc[kb] = mfma_32x32x16(b, df[s], pacc[kb]);
-        }
-      }
-
-      // ---- P^T = 2^{S^T scale log2e - L}; dS^T = P^T (dP^T - D), as bf16 B operand
-      bf16x8 sf[2][2];
+        };
+        // P^T = 2^{S^T scale log2e - L}, dS^T = P^T (dP^T - D) for accumulator
+        // entries 4 r .. 4 r + 3 of half kb, as bf16 B operand
+        auto soft_part = [&](int kb, int r, auto mask_tag) {
+          constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float p = fast_exp2(fmaf(sacc[kb][i], scale_log2, -lq2));
-          if (need_mask) {
-            const int kk = key0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-            if (kk >= N || (CAUSAL && kk > qry)) p = 0.f;
+          for (int e = 0; e < 4; ++e) {
+            const int i = r * 4 + e;
+            float p = fast_exp2(fmaf(sacc[kb][i], scale_log2, -lq2));
+            if constexpr (MASK) {
+              const int kk = key0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+              if (kk >= N || (CAUSAL && kk > qry)) p = 0.f;
+            }
+            // keep the exponential at this point of the issue order
+            __asm__ volatile("" ::"v"(p));
+            sf[kb][i >> 3][i & 7] = (__bf16)(p * (pacc[kb][i] - dlt));
           }
-          sf[kb][i >> 3][i & 7] = (__bf16)(p * (pacc[kb][i] - dlt));
+        };
+        // dQ^T += K^T dS^T for 16 keys (t) and 32 d rows (b) of half kb
+        auto dq_step = [&](int kb, int t, int b) {
+          const int roff = (kb * 32 + t * 16) * RB;
+          const bf16x8 ka = concat4(lds_read_tr4((const ATTN_LDS __bf16*)(ks + (tr_lo ^ (64 * b)) + roff)),
+                                    lds_read_tr4((const ATTN_LDS __bf16*)(ks + (tr_hi ^ (64 * b)) + roff)));
+          dq_acc[b] = mfma_32x32x16(ka, sf[kb][t], dq_acc[b]);
+        };
+
+        auto body = [&](auto mask_tag) {
+          // A
+#pragma unroll
+          for (int s = 0; s < KS; ++s) sdp_step(0, s);
+          __builtin_amdgcn_sched_barrier(0);
+          // B: softmax part r of half 0 after k-step r*KS/4 of half 1
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            sdp_step(1, s);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (r * KS / 4 == s) soft_part(0, r, mask_tag);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          // C: softmax part r of half 1 after dQ step r*2*DB/4 of half 0
+#pragma unroll
+          for (int u = 0; u < 2 * DB; ++u) {
+            dq_step(0, u / DB, u % DB);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (r * 2 * DB / 4 == u) soft_part(1, r, mask_tag);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          // D
+#pragma unroll
+          for (int u = 0; u < 2 * DB; ++u) dq_step(1, u / DB, u % DB);
+        };
+        if (need_mask)
+          body(std::true_type{});
+        else
+          body(std::false_type{});
+      } else {
+        // ---- S^T = K Q^T and dP^T = V dO^T for two 32-key halves
+        f32x16 sacc[2] = {f32x16{}, f32x16{}};
+        f32x16 pacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const int off = rd_base ^ (32 * s);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(ks + off + kb * 32 * RB);
+            sacc[kb] = mfma_32x32x16(a, qf[s], sacc[kb]);
+            const bf16x8 b = *reinterpret_cast<const ATTN_LDS bf16x8*>(vs + off + kb * 32 * RB);
+            pacc[kb] = mfma_32x32x16(b, df[s], pacc[kb]);
+          }
         }
 
-      // ---- dQ^T += K^T dS^T (K^T by transpose reads of the K tile)
-#pragma unroll
-      for (int b = 0; b < DB; ++b) {
-        const int lo = tr_lo ^ (64 * b);
-        const int hi = tr_hi ^ (64 * b);
+        // ---- P^T = 2^{S^T scale log2e - L}; dS^T = P^T (dP^T - D), as bf16 B operand
+        bf16x8 sf[2][2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const int roff = (kb * 32 + t * 16) * RB;
-            const bf16x8 ka = concat4(lds_read_tr4((const ATTN_LDS __bf16*)(ks + lo + roff)),
-                                      lds_read_tr4((const ATTN_LDS __bf16*)(ks + hi + roff)));
-            dq_acc[b] = mfma_32x32x16(ka, sf[kb][t], dq_acc[b]);
+          for (int i = 0; i < 16; ++i) {
+            float p = fast_exp2(fmaf(sacc[kb][i], scale_log2, -lq2));
+            if (need_mask) {
+              const int kk = key0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+              if (kk >= N || (CAUSAL && kk > qry)) p = 0.f;
+            }
+            sf[kb][i >> 3][i & 7] = (__bf16)(p * (pacc[kb][i] - dlt));
           }
+
+        // ---- dQ^T += K^T dS^T (K^T by transpose reads of the K tile)
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {
+          const int lo = tr_lo ^ (64 * b);
+          const int hi = tr_hi ^ (64 * b);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const int roff = (kb * 32 + t * 16) * RB;
+              const bf16x8 ka = concat4(lds_read_tr4((const ATTN_LDS __bf16*)(ks + lo + roff)),
+                                        lds_read_tr4((const ATTN_LDS __bf16*)(ks + hi + roff)));
+              dq_acc[b] = mfma_32x32x16(ka, sf[kb][t], dq_acc[b]);
+            }
+        }
       }
     }
     wait_vmem();
