@@ -199,33 +199,59 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       //   B  S, dP of block 1   |  P, dS of block 0 (VALU)
       //   C  dV, dK of block 0  |  P, dS of block 1
       //   D  dV, dK of block 1
+      // Every LDS operand is read one step before the MFMAs that use it, and
+      // each softmax part's L and D values one part ahead, so that with a
+      // single wave per SIMD the LDS latency stays off the critical path.
       f32x16 sacc[2] = {f32x16{}, f32x16{}};
       f32x16 pacc[2] = {f32x16{}, f32x16{}};
       bf16x8 pa[2][2], sa[2][2];
 
-      // S = Q K^T and dP = dO V^T, k-step s of block qb
-      auto sdp_step = [&](int qb, int s) {
+      struct RowFrag { bf16x8 q, d; };   // Q and dO rows: one k-step of one block
+      struct TrFrag { bf16x8 d, q; };    // dO and Q transposed: one (t, b) step
+      struct Stats { float4 l, d; };     // L and D of 4 query rows
+      // k-step s of S = Q K^T and dP = dO V^T for block qb
+      auto read_row = [&](int qb, int s) {
         const int off = (rd_base ^ (32 * s)) + qb * 32 * RB;
-        const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(qs + off);
-        sacc[qb] = mfma_32x32x16(a, kf[s], sacc[qb]);
-        const bf16x8 b = *reinterpret_cast<const ATTN_LDS bf16x8*>(dos + off);
-        pacc[qb] = mfma_32x32x16(b, vf[s], pacc[qb]);
+        return RowFrag{*reinterpret_cast<const ATTN_LDS bf16x8*>(qs + off),
+                       *reinterpret_cast<const ATTN_LDS bf16x8*>(dos + off)};
       };
-      // P = 2^{S scale log2e - L log2e} and dS = P (dP - D) for the 4 query
-      // rows qb*32 + r*8 + half*4 + e of the lane's key
-      auto soft_part = [&](int qb, int r, auto mask_tag) {
-        constexpr bool MASK = decltype(mask_tag)::value;
+      auto mma_sdp = [&](int qb, int s, const RowFrag& f) {
+        sacc[qb] = mfma_32x32x16(f.q, kf[s], sacc[qb]);
+        pacc[qb] = mfma_32x32x16(f.d, vf[s], pacc[qb]);
+      };
+      // step u = t * DB + b of dV += P^T dO and dK += dS^T Q for block qb
+      auto read_tr = [&](int qb, int u) {
+        const int t = u / DB, b = u % DB;
+        const int roff = (qb * 32 + t * 16) * RB;
+        const int lo = (tr_lo ^ (64 * b)) + roff;
+        const int hi = (tr_hi ^ (64 * b)) + roff;
+        return TrFrag{concat4(lds_read_tr4((const ATTN_LDS __bf16*)(dos + lo)),
+                              lds_read_tr4((const ATTN_LDS __bf16*)(dos + hi))),
+                      concat4(lds_read_tr4((const ATTN_LDS __bf16*)(qs + lo)),
+                              lds_read_tr4((const ATTN_LDS __bf16*)(qs + hi)))};
+      };
+      auto mma_dvdk = [&](int qb, int u, const TrFrag& f) {
+        const int t = u / DB, b = u % DB;
+        dv_acc[b] = mfma_32x32x16(pa[qb][t], f.d, dv_acc[b]);
+        dk_acc[b] = mfma_32x32x16(sa[qb][t], f.q, dk_acc[b]);
+      };
+      // L and D of query rows qb*32 + r*8 + half*4 + e, e = 0..3
+      auto read_stats = [&](int qb, int r) {
         const int qrow0 = qb * 32 + r * 8 + half * 4;
-        const float4 l4 = *reinterpret_cast<const float4*>(lq + qrow0);
-        const float4 d4 = *reinterpret_cast<const float4*>(dq_d + qrow0);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+        return Stats{*reinterpret_cast<const float4*>(lq + qrow0),
+                     *reinterpret_cast<const float4*>(dq_d + qrow0)};
+      };
+      // P = 2^{S scale log2e - L log2e} and dS = P (dP - D) for those rows
+      auto soft_part = [&](int qb, int r, const Stats& st4, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        const float lv[4] = {st4.l.x, st4.l.y, st4.l.z, st4.l.w};
+        const float dv4[4] = {st4.d.x, st4.d.y, st4.d.z, st4.d.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = r * 4 + e;
           float p = fast_exp2(fmaf(sacc[qb][i], scale_log2, -lv[e]));
           if constexpr (MASK) {
-            const int qq = q0 + qrow0 + e;
+            const int qq = q0 + qb * 32 + r * 8 + half * 4 + e;
             if (qq >= N || key >= N || (CAUSAL && key > qq)) p = 0.f;
           }
           // keep the exponential at this point of the issue order
@@ -244,48 +270,62 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             sa[qb][t][e] = (__bf16)pacc[qb][t * 8 + e];
           }
       };
-      // dV += P^T dO and dK += dS^T Q for 16 queries (t) and 32 d columns (b)
-      auto dvdk_step = [&](int qb, int t, int b) {
-        const int roff = (qb * 32 + t * 16) * RB;
-        const int lo = (tr_lo ^ (64 * b)) + roff;
-        const int hi = (tr_hi ^ (64 * b)) + roff;
-        const bf16x8 dob = concat4(lds_read_tr4((const ATTN_LDS __bf16*)(dos + lo)),
-                                   lds_read_tr4((const ATTN_LDS __bf16*)(dos + hi)));
-        dv_acc[b] = mfma_32x32x16(pa[qb][t], dob, dv_acc[b]);
-        const bf16x8 qbv = concat4(lds_read_tr4((const ATTN_LDS __bf16*)(qs + lo)),
-                                   lds_read_tr4((const ATTN_LDS __bf16*)(qs + hi)));
-        dk_acc[b] = mfma_32x32x16(sa[qb][t], qbv, dk_acc[b]);
-      };
 
       auto body = [&](auto mask_tag) {
-        // A
-#pragma unroll
-        for (int s = 0; s < KS; ++s) sdp_step(0, s);
-        __builtin_amdgcn_sched_barrier(0);
-        // B: KS k-steps of block 1; softmax part r of block 0 after step r*KS/4
+        constexpr int US = 2 * DB;  // dV/dK steps per block
+        RowFrag rf[2];
+        TrFrag tf[2];
+        Stats sv[2];
+        // A: S, dP of block 0; the last step prefetches block 1's first rows
+        rf[0] = read_row(0, 0);
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-          sdp_step(1, s);
+          rf[(s + 1) & 1] = (s + 1 < KS) ? read_row(0, s + 1) : read_row(1, 0);
+          if (s == KS - 1) sv[0] = read_stats(0, 0);
+          mma_sdp(0, s, rf[s & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // B: S, dP of block 1 | softmax part r of block 0 after step r*KS/4
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const int idx = (KS + s) & 1;
+          if (s + 1 < KS)
+            rf[idx ^ 1] = read_row(1, s + 1);
+          else
+            tf[0] = read_tr(0, 0);
+          mma_sdp(1, s, rf[idx]);
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (r * KS / 4 == s) soft_part(0, r, mask_tag);
+            if (r * KS / 4 == s) {
+              const Stats cur = sv[r & 1];
+              sv[(r + 1) & 1] = (r + 1 < 4) ? read_stats(0, r + 1) : read_stats(1, 0);
+              soft_part(0, r, cur, mask_tag);
+            }
           __builtin_amdgcn_sched_barrier(0);
         }
         to_bf16(0);
-        // C: 2*DB steps of block 0's dV/dK; softmax part r of block 1 after
-        // step r*2*DB/4
+        // C: dV, dK of block 0 | softmax part r of block 1 after step r*US/4
 #pragma unroll
-        for (int u = 0; u < 2 * DB; ++u) {
-          dvdk_step(0, u / DB, u % DB);
+        for (int u = 0; u < US; ++u) {
+          tf[(u + 1) & 1] = (u + 1 < US) ? read_tr(0, u + 1) : read_tr(1, 0);
+          mma_dvdk(0, u, tf[u & 1]);
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (r * 2 * DB / 4 == u) soft_part(1, r, mask_tag);
+            if (r * US / 4 == u) {
+              const Stats cur = sv[r & 1];
+              if (r + 1 < 4) sv[(r + 1) & 1] = read_stats(1, r + 1);
+              soft_part(1, r, cur, mask_tag);
+            }
           __builtin_amdgcn_sched_barrier(0);
         }
         to_bf16(1);
-        // D
+        // D: dV, dK of block 1
 #pragma unroll
-        for (int u = 0; u < 2 * DB; ++u) dvdk_step(1, u / DB, u % DB);
+        for (int u = 0; u < US; ++u) {
+          if (u + 1 < US) tf[(u + 1) & 1] = read_tr(1, u + 1);
+          mma_dvdk(1, u, tf[u & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       };
       if (need_mask)
         body(std::true_type{});
