@@ -522,19 +522,26 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         else
           body(std::false_type{});
       } else {
-        // ---- S^T = K Q^T and dP^T = V dO^T for two 32-key halves
+        // Plain order; every LDS operand is read one step ahead of its MFMAs.
+        // ---- S^T = K Q^T and dP^T = V dO^T, step u = s * 2 + kb
         f32x16 sacc[2] = {f32x16{}, f32x16{}};
         f32x16 pacc[2] = {f32x16{}, f32x16{}};
+        struct RowFrag { bf16x8 k, v; };
+        auto read_row = [&](int u) {
+          const int s = u >> 1, kb = u & 1;
+          const int off = (rd_base ^ (32 * s)) + kb * 32 * RB;
+          return RowFrag{*reinterpret_cast<const ATTN_LDS bf16x8*>(ks + off),
+                         *reinterpret_cast<const ATTN_LDS bf16x8*>(vs + off)};
+        };
+        RowFrag rf[2];
+        rf[0] = read_row(0);
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const int off = rd_base ^ (32 * s);
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(ks + off + kb * 32 * RB);
-            sacc[kb] = mfma_32x32x16(a, qf[s], sacc[kb]);
-            const bf16x8 b = *reinterpret_cast<const ATTN_LDS bf16x8*>(vs + off + kb * 32 * RB);
-            pacc[kb] = mfma_32x32x16(b, df[s], pacc[kb]);
-          }
+        for (int u = 0; u < 2 * KS; ++u) {
+          if (u + 1 < 2 * KS) rf[(u + 1) & 1] = read_row(u + 1);
+          const int s = u >> 1, kb = u & 1;
+          sacc[kb] = mfma_32x32x16(rf[u & 1].k, qf[s], sacc[kb]);
+          pacc[kb] = mfma_32x32x16(rf[u & 1].v, df[s], pacc[kb]);
+          __builtin_amdgcn_sched_barrier(0);
         }
 
         // ---- P^T = 2^{S^T scale log2e - L}; dS^T = P^T (dP^T - D), as bf16 B operand
@@ -551,20 +558,23 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             sf[kb][i >> 3][i & 7] = (__bf16)(p * (pacc[kb][i] - dlt));
           }
 
-        // ---- dQ^T += K^T dS^T (K^T by transpose reads of the K tile)
+        // ---- dQ^T += K^T dS^T, step u = (kb * 2 + t) * DB + b (K^T by
+        // transpose reads of the K tile)
+        auto read_kt = [&](int u) {
+          const int kt = u / DB, b = u % DB;
+          const int roff = kt * 16 * RB;
+          return concat4(lds_read_tr4((const ATTN_LDS __bf16*)(ks + (tr_lo ^ (64 * b)) + roff)),
+                         lds_read_tr4((const ATTN_LDS __bf16*)(ks + (tr_hi ^ (64 * b)) + roff)));
+        };
+        constexpr int US = 4 * DB;
+        bf16x8 ka[2];
+        ka[0] = read_kt(0);
 #pragma unroll
-        for (int b = 0; b < DB; ++b) {
-          const int lo = tr_lo ^ (64 * b);
-          const int hi = tr_hi ^ (64 * b);
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-              const int roff = (kb * 32 + t * 16) * RB;
-              const bf16x8 ka = concat4(lds_read_tr4((const ATTN_LDS __bf16*)(ks + lo + roff)),
-                                        lds_read_tr4((const ATTN_LDS __bf16*)(ks + hi + roff)));
-              dq_acc[b] = mfma_32x32x16(ka, sf[kb][t], dq_acc[b]);
-            }
+        for (int u = 0; u < US; ++u) {
+          if (u + 1 < US) ka[(u + 1) & 1] = read_kt(u + 1);
+          const int kt = u / DB, b = u % DB;
+          dq_acc[b] = mfma_32x32x16(ka[u & 1], sf[kt >> 1][kt & 1], dq_acc[b]);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }

@@ -232,21 +232,25 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
     l_run += psum;
 
-    // ---- O^T += V^T P^T: for each 16-key step, DB independent accumulators
+    // ---- O^T += V^T P^T: step u = (kb * 2 + t) * DB + b covers 16 keys and
+    // 32 d rows; consecutive steps go to different accumulators, and each
+    // step's V^T fragment is read one step ahead.
     const ATTN_LDS unsigned char* vbuf = (const ATTN_LDS unsigned char*)smem + L::v_buf(j & 1);
+    auto read_v = [&](int u) {
+      const int kt = u / DB, b = u % DB;
+      const int roff = kt * 16 * L::kRowBytes;  // kt = kb * 2 + t
+      return concat4(lds_read_tr4((const ATTN_LDS __bf16*)(vbuf + (v_base_lo ^ (64 * b)) + roff)),
+                     lds_read_tr4((const ATTN_LDS __bf16*)(vbuf + (v_base_hi ^ (64 * b)) + roff)));
+    };
+    constexpr int US = 4 * DB;
+    bf16x8 va[2];
+    va[0] = read_v(0);
 #pragma unroll
-    for (int b = 0; b < DB; ++b) {
-      const int lo = v_base_lo ^ (64 * b);
-      const int hi = v_base_hi ^ (64 * b);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int roff = (kb * 32 + t * 16) * L::kRowBytes;
-          const bf16x8 va = concat4(lds_read_tr4((const ATTN_LDS __bf16*)(vbuf + lo + roff)),
-                                    lds_read_tr4((const ATTN_LDS __bf16*)(vbuf + hi + roff)));
-          oacc[b] = mfma_32x32x16(va, pf[kb][t], oacc[b]);
-        }
+    for (int u = 0; u < US; ++u) {
+      if (u + 1 < US) va[(u + 1) & 1] = read_v(u + 1);
+      const int kt = u / DB, b = u % DB;
+      oacc[b] = mfma_32x32x16(va[u & 1], pf[kt >> 1][kt & 1], oacc[b]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
