@@ -271,59 +271,60 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
           }
       };
 
+      // The tile is one sequence of steps g: KS row steps of block 0 (A), KS
+      // of block 1 (B), 2*DB transposed steps of block 0 (C) and of block 1
+      // (D).  Both kinds read two bf16x8 fragments, so one ring of registers
+      // holds the fragments of the next kPrefetch steps.
+      constexpr int US = 2 * DB;
+      constexpr int NSTEPS = 2 * KS + 2 * US;
+      constexpr int kPrefetch = 3;
+      auto read_step = [&](int g) {
+        if (g < KS) { const RowFrag f = read_row(0, g); return TrFrag{f.q, f.d}; }
+        if (g < 2 * KS) { const RowFrag f = read_row(1, g - KS); return TrFrag{f.q, f.d}; }
+        if (g < 2 * KS + US) return read_tr(0, g - 2 * KS);
+        return read_tr(1, g - 2 * KS - US);
+      };
       auto body = [&](auto mask_tag) {
-        constexpr int US = 2 * DB;  // dV/dK steps per block
-        RowFrag rf[2];
-        TrFrag tf[2];
+        TrFrag ring[kPrefetch + 1];
         Stats sv[2];
-        // A: S, dP of block 0; the last step prefetches block 1's first rows
-        rf[0] = read_row(0, 0);
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          rf[(s + 1) & 1] = (s + 1 < KS) ? read_row(0, s + 1) : read_row(1, 0);
-          if (s == KS - 1) sv[0] = read_stats(0, 0);
-          mma_sdp(0, s, rf[s & 1]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        // B: S, dP of block 1 | softmax part r of block 0 after step r*KS/4
+        for (int g = 0; g < kPrefetch; ++g) ring[g] = read_step(g);
+#pragma clang loop unroll(full)
+        for (int g = 0; g < NSTEPS; ++g) {
+          if (g + kPrefetch < NSTEPS) ring[(g + kPrefetch) % (kPrefetch + 1)] = read_step(g + kPrefetch);
+          const TrFrag& f = ring[g % (kPrefetch + 1)];
+          if (g < KS) {
+            // A: S, dP of block 0
+            mma_sdp(0, g, RowFrag{f.d, f.q});
+            if (g == KS - 1) sv[0] = read_stats(0, 0);
+          } else if (g < 2 * KS) {
+            // B: S, dP of block 1 | softmax part r of block 0 after step r*KS/4
+            const int s = g - KS;
+            mma_sdp(1, s, RowFrag{f.d, f.q});
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const int idx = (KS + s) & 1;
-          if (s + 1 < KS)
-            rf[idx ^ 1] = read_row(1, s + 1);
-          else
-            tf[0] = read_tr(0, 0);
-          mma_sdp(1, s, rf[idx]);
+            for (int r = 0; r < 4; ++r)
+              if (r * KS / 4 == s) {
+                const Stats cur = sv[r & 1];
+                sv[(r + 1) & 1] = (r + 1 < 4) ? read_stats(0, r + 1) : read_stats(1, 0);
+                soft_part(0, r, cur, mask_tag);
+              }
+            if (s == KS - 1) to_bf16(0);
+          } else if (g < 2 * KS + US) {
+            // C: dV, dK of block 0 | softmax part r of block 1 after step r*US/4
+            const int u = g - 2 * KS;
+            mma_dvdk(0, u, f);
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (r * KS / 4 == s) {
-              const Stats cur = sv[r & 1];
-              sv[(r + 1) & 1] = (r + 1 < 4) ? read_stats(0, r + 1) : read_stats(1, 0);
-              soft_part(0, r, cur, mask_tag);
-            }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        to_bf16(0);
-        // C: dV, dK of block 0 | softmax part r of block 1 after step r*US/4
-#pragma unroll
-        for (int u = 0; u < US; ++u) {
-          tf[(u + 1) & 1] = (u + 1 < US) ? read_tr(0, u + 1) : read_tr(1, 0);
-          mma_dvdk(0, u, tf[u & 1]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (r * US / 4 == u) {
-              const Stats cur = sv[r & 1];
-              if (r + 1 < 4) sv[(r + 1) & 1] = read_stats(1, r + 1);
-              soft_part(1, r, cur, mask_tag);
-            }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        to_bf16(1);
-        // D: dV, dK of block 1
-#pragma unroll
-        for (int u = 0; u < US; ++u) {
-          if (u + 1 < US) tf[(u + 1) & 1] = read_tr(1, u + 1);
-          mma_dvdk(1, u, tf[u & 1]);
+            for (int r = 0; r < 4; ++r)
+              if (r * US / 4 == u) {
+                const Stats cur = sv[r & 1];
+                if (r + 1 < 4) sv[(r + 1) & 1] = read_stats(1, r + 1);
+                soft_part(1, r, cur, mask_tag);
+              }
+            if (u == US - 1) to_bf16(1);
+          } else {
+            // D: dV, dK of block 1
+            mma_dvdk(1, g - 2 * KS - US, f);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
       };
