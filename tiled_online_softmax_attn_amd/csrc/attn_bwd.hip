@@ -74,19 +74,6 @@ bwd_preprocess_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ d
 constexpr int kKvBK = 128;  // keys per workgroup (32 per wave)
 constexpr int kKvBQ = 64;   // queries per inner step (one SwzTile)
 
-// Q and dO tiles of 64 queries (SwzTile layout), two buffers each, then the
-// tiles' L (log2 units) and D values: [Q0 | Q1 | dO0 | dO1 | L[2][64] | D[2][64]].
-template <int D>
-struct DkdvLds {
-  static constexpr int kTileBytes = SwzTile<D>::kBytes;
-  static constexpr int q_buf(int b) { return b * kTileBytes; }
-  static constexpr int do_buf(int b) { return (2 + b) * kTileBytes; }
-  static constexpr int kOffL = 4 * kTileBytes;
-  static constexpr int kOffD = kOffL + 2 * kKvBQ * 4;
-  static constexpr int kBytes = kOffD + 2 * kKvBQ * 4;
-  static_assert(kKvBQ == SwzTile<D>::kRows, "query tile is one SwzTile");
-};
-
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(kBwdThreads, 1)
 bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
@@ -94,14 +81,18 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 const float* __restrict__ lse, const float* __restrict__ delta,
                 __bf16* __restrict__ dk, __bf16* __restrict__ dv, int BH, int N, float scale,
                 float scale_log2) {
-  using L = DkdvLds<D>;
   using Tile = SwzTile<D>;
+  static_assert(kKvBQ == Tile::kRows, "query tile is one SwzTile");
   constexpr int KS = D / 16;  // k-steps over d
   constexpr int DB = D / 32;  // 32-wide d blocks
   constexpr int RB = Tile::kRowBytes;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[L::kBytes];
-  float* sm_l = reinterpret_cast<float*>(smem + L::kOffL);  // [2][BQ]
-  float* sm_d = reinterpret_cast<float*>(smem + L::kOffD);  // [2][BQ]
+  // One LDS object per buffer: the compiler then knows that the copies into
+  // one buffer cannot alias reads of the other and does not wait for them.
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_q0[Tile::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_q1[Tile::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_do0[Tile::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_do1[Tile::kBytes];
+  __shared__ __attribute__((aligned(16))) float lds_stats[2][2][kKvBQ];  // [buffer][L, D][query]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -140,24 +131,33 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int n_qtiles = (N + kKvBQ - 1) / kKvBQ;
   const int qt_begin = CAUSAL ? key_wg0 / kKvBQ : 0;
 
-  // Q and dO tiles go straight to LDS; L (in log2 units) and D pass through
-  // one register each on the first 64 threads.
+  // Q and dO tiles go straight to LDS buffer B; L and D pass through one
+  // register each on the first 64 threads (L is scaled to log2 units only
+  // when stored, so that nothing waits for the load before then).
   float rl = 0.f, rd = 0.f;
-  auto load_tile = [&](int qt, int b) {
-    Tile::template load<kBwdThreads / 64>(qh, qt * kKvBQ, N, (ATTN_LDS unsigned char*)smem + L::q_buf(b), wave, lane);
-    Tile::template load<kBwdThreads / 64>(doh, qt * kKvBQ, N, (ATTN_LDS unsigned char*)smem + L::do_buf(b), wave, lane);
+  auto q_lds = [&](auto buf_tag) {
+    return (ATTN_LDS unsigned char*)(decltype(buf_tag)::value ? lds_q1 : lds_q0);
+  };
+  auto do_lds = [&](auto buf_tag) {
+    return (ATTN_LDS unsigned char*)(decltype(buf_tag)::value ? lds_do1 : lds_do0);
+  };
+  auto load_tile = [&](int qt, auto buf_tag) {
+    Tile::template load<kBwdThreads / 64>(qh, qt * kKvBQ, N, q_lds(buf_tag), wave, lane);
+    Tile::template load<kBwdThreads / 64>(doh, qt * kKvBQ, N, do_lds(buf_tag), wave, lane);
     if (tid < kKvBQ) {
       const int qq = qt * kKvBQ + tid;
-      rl = qq < N ? lse_h[qq] * kLog2e : 0.f;
+      rl = qq < N ? lse_h[qq] : 0.f;
       rd = qq < N ? del_h[qq] : 0.f;
     }
   };
-  auto store_stats = [&](int b) {
+  auto store_stats = [&](auto buf_tag) {
     if (tid < kKvBQ) {
-      sm_l[b * kKvBQ + tid] = rl;
-      sm_d[b * kKvBQ + tid] = rd;
+      lds_stats[decltype(buf_tag)::value][0][tid] = rl * kLog2e;
+      lds_stats[decltype(buf_tag)::value][1][tid] = rd;
     }
   };
+  using Buf0 = std::integral_constant<int, 0>;
+  using Buf1 = std::integral_constant<int, 1>;
 
   const int rd_base = Tile::row_read_base(l32, half);
   const int tr_lo = Tile::tr_read_base(lane, false);
@@ -171,30 +171,33 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   }
 
   if (qt_begin < n_qtiles) {
-    load_tile(qt_begin, 0);
-    store_stats(0);
+    load_tile(qt_begin, Buf0{});
+    store_stats(Buf0{});
   }
   wait_vmem();
   __syncthreads();
 
-  for (int qt = qt_begin; qt < n_qtiles; ++qt) {
-    const int st = (qt - qt_begin) & 1;
+  // One query tile; its Q / dO / L / D sit in buffer CUR, and the copies of
+  // the next tile go to the other buffer meanwhile.
+  auto tile = [&](const int qt, auto cur_tag) {
+    constexpr int CUR = decltype(cur_tag)::value;
+    using Next = std::integral_constant<int, 1 - CUR>;
     // Hold dK and dV in accumulation registers across the whole tile.
     // Without this the register allocator moves all 128 values out to
     // ordinary registers while S and dP occupy the accumulation registers
     // and back before dV += P^T dO, about 250 extra moves per tile.
 #pragma unroll
     for (int b = 0; b < DB; ++b) __asm__ volatile("" : "+a"(dk_acc[b]), "+a"(dv_acc[b]));
-    if (qt + 1 < n_qtiles) load_tile(qt + 1, st ^ 1);
+    if (qt + 1 < n_qtiles) load_tile(qt + 1, Next{});
 
     const int q0 = qt * kKvBQ;
     // wave-uniform: every query of the tile precedes every key of this wave
     const bool skip = CAUSAL && (q0 + kKvBQ - 1 < key_w0);
     if (!skip) {
-      const ATTN_LDS unsigned char* qs = (const ATTN_LDS unsigned char*)smem + L::q_buf(st);
-      const ATTN_LDS unsigned char* dos = (const ATTN_LDS unsigned char*)smem + L::do_buf(st);
-      const float* lq = sm_l + st * kKvBQ;
-      const float* dq_d = sm_d + st * kKvBQ;
+      const ATTN_LDS unsigned char* qs = q_lds(cur_tag);
+      const ATTN_LDS unsigned char* dos = do_lds(cur_tag);
+      const float* lq = lds_stats[CUR][0];
+      const float* dq_d = lds_stats[CUR][1];
       const bool need_mask =
           (q0 + kKvBQ > N) || (key_w0 + 32 > N) || (CAUSAL && q0 < key_w0 + 31);
 
@@ -340,9 +343,13 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         body(std::false_type{});
     }
 
-    if (qt + 1 < n_qtiles) store_stats(st ^ 1);
+    if (qt + 1 < n_qtiles) store_stats(Next{});
     wait_vmem();
     __syncthreads();
+  };
+  for (int qt = qt_begin; qt < n_qtiles; qt += 2) {
+    tile(qt, Buf0{});
+    if (qt + 1 < n_qtiles) tile(qt + 1, Buf1{});
   }
 
   // ---- dK = scale * acc, dV: lane holds d column b*32 + l32 and key rows
