@@ -371,17 +371,6 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 constexpr int kDqBQ = 128;  // queries per workgroup (32 per wave)
 constexpr int kDqBK = 64;   // keys per K/V tile (one SwzTile)
 
-// K and V tiles of 64 keys (SwzTile layout), two buffers each:
-// [K0 | K1 | V0 | V1].  K is read both by rows (S^T) and transposed (dQ^T).
-template <int D>
-struct DqLds {
-  static constexpr int kTileBytes = SwzTile<D>::kBytes;
-  static constexpr int k_buf(int b) { return b * kTileBytes; }
-  static constexpr int v_buf(int b) { return (2 + b) * kTileBytes; }
-  static constexpr int kBytes = 4 * kTileBytes;
-  static_assert(kDqBK == SwzTile<D>::kRows, "key tile is one SwzTile");
-};
-
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(kBwdThreads, 2)
 bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
@@ -389,13 +378,27 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
               const float* __restrict__ lse, const float* __restrict__ delta,
               __bf16* __restrict__ dq, int BH, int N, int n_qtiles, float scale,
               float scale_log2) {
-  using L = DqLds<D>;
   using Tile = SwzTile<D>;
+  static_assert(kDqBK == Tile::kRows, "key tile is one SwzTile");
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr bool kPipelineHalves = (D == 64);
   constexpr int RB = Tile::kRowBytes;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[L::kBytes];
+  // K and V tiles of 64 keys (SwzTile layout), two buffers each; K is read
+  // both by rows (S^T) and transposed (dQ^T).  One LDS object per buffer, so
+  // that the copies into one buffer do not make reads of the other wait.
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_k0[Tile::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_k1[Tile::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_v0[Tile::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_v1[Tile::kBytes];
+  auto k_lds = [&](auto buf_tag) {
+    return (ATTN_LDS unsigned char*)(decltype(buf_tag)::value ? lds_k1 : lds_k0);
+  };
+  auto v_lds = [&](auto buf_tag) {
+    return (ATTN_LDS unsigned char*)(decltype(buf_tag)::value ? lds_v1 : lds_v0);
+  };
+  using Buf0 = std::integral_constant<int, 0>;
+  using Buf1 = std::integral_constant<int, 1>;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -432,9 +435,9 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int kv_end = CAUSAL ? min(N, (qt + 1) * kDqBQ) : N;
   const int n_tiles = (kv_end + kDqBK - 1) / kDqBK;
 
-  auto load_tile = [&](int j, int b) {
-    Tile::template load<kBwdThreads / 64>(kh, j * kDqBK, N, (ATTN_LDS unsigned char*)smem + L::k_buf(b), wave, lane);
-    Tile::template load<kBwdThreads / 64>(vh, j * kDqBK, N, (ATTN_LDS unsigned char*)smem + L::v_buf(b), wave, lane);
+  auto load_tile = [&](int j, auto buf_tag) {
+    Tile::template load<kBwdThreads / 64>(kh, j * kDqBK, N, k_lds(buf_tag), wave, lane);
+    Tile::template load<kBwdThreads / 64>(vh, j * kDqBK, N, v_lds(buf_tag), wave, lane);
   };
   const int rd_base = Tile::row_read_base(l32, half);
   const int tr_lo = Tile::tr_read_base(lane, false);
@@ -444,18 +447,20 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
   for (int b = 0; b < DB; ++b) dq_acc[b] = f32x16{};
 
-  load_tile(0, 0);
+  load_tile(0, Buf0{});
   wait_vmem();
   __syncthreads();
 
-  for (int j = 0; j < n_tiles; ++j) {
-    const int st = j & 1;
-    if (j + 1 < n_tiles) load_tile(j + 1, st ^ 1);
+  // One K/V tile j, held in buffer CUR; the copies of tile j+1 go to the
+  // other buffer meanwhile.
+  auto tile = [&](const int j, auto cur_tag) {
+    using Next = std::integral_constant<int, 1 - decltype(cur_tag)::value>;
+    if (j + 1 < n_tiles) load_tile(j + 1, Next{});
     const int key0 = j * kDqBK;
     const bool skip = CAUSAL && key0 > q_wave0 + 31;
     if (!skip) {
-      const ATTN_LDS unsigned char* ks = (const ATTN_LDS unsigned char*)smem + L::k_buf(st);
-      const ATTN_LDS unsigned char* vs = (const ATTN_LDS unsigned char*)smem + L::v_buf(st);
+      const ATTN_LDS unsigned char* ks = k_lds(cur_tag);
+      const ATTN_LDS unsigned char* vs = v_lds(cur_tag);
       const bool need_mask = (key0 + kDqBK > N) || (CAUSAL && key0 + kDqBK - 1 > q_wave0);
 
       if constexpr (kPipelineHalves) {
@@ -594,6 +599,10 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
     wait_vmem();
     __syncthreads();
+  };
+  for (int j = 0; j < n_tiles; j += 2) {
+    tile(j, Buf0{});
+    if (j + 1 < n_tiles) tile(j + 1, Buf1{});
   }
 
   // ---- dQ = scale * acc: lane holds query qry, d rows b*32 + (i/4)*8 + half*4 + i%4

@@ -38,18 +38,6 @@ constexpr int kFwdBQ = 128;  // queries per workgroup
 constexpr int kFwdBK = 64;   // keys per K/V tile
 constexpr float kRescaleSlack = 8.f;  // log2 units: P never exceeds 2^8
 
-// K and V tiles of 64 keys (SwzTile layout).  K and V each have two
-// buffers: [K0 | K1 | V0 | V1].
-template <int D>
-struct FwdLds {
-  static constexpr int kRowBytes = 2 * D;
-  static constexpr int kTileBytes = SwzTile<D>::kBytes;
-  static constexpr int kBytes = 4 * kTileBytes;
-  static_assert(kFwdBK == SwzTile<D>::kRows, "K/V tile is one SwzTile");
-  static constexpr int k_buf(int b) { return b * kTileBytes; }
-  static constexpr int v_buf(int b) { return (2 + b) * kTileBytes; }
-};
-
 // Workgroup id -> (head, query tile).  Heavy causal tiles (late queries see
 // more keys) are issued first.  With B*H a multiple of 8 every query tile of
 // one head lands on the same XCD (ids are dealt round-robin over the 8 XCDs),
@@ -66,7 +54,9 @@ __global__ void __launch_bounds__(kFwdThreads, 2)
 attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      const __bf16* __restrict__ v, __bf16* __restrict__ o,
                      float* __restrict__ lse, int BH, int N, int n_qtiles, float scale_log2) {
-  using L = FwdLds<D>;
+  using Tile = SwzTile<D>;
+  static_assert(kFwdBK == Tile::kRows, "K/V tile is one SwzTile");
+  constexpr int RB = Tile::kRowBytes;
   constexpr int KS = D / 16;  // k-steps of the S^T MFMA
   constexpr int DB = D / 32;  // 32-wide d blocks of O^T
   // d = 128: S^T of tile j+1 is computed during the softmax of tile j (the
@@ -74,7 +64,22 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // S^T of a tile is computed at the start of its own step, which keeps the
   // register count low enough for more waves per SIMD.
   constexpr bool kPipelineQK = (D == 128) && CAUSAL;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[L::kBytes];
+  // K and V tiles of 64 keys (SwzTile layout), two buffers each.  One LDS
+  // object per buffer: the compiler then knows that the copies into one
+  // buffer cannot alias reads of another and does not wait for them.
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_k0[Tile::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_k1[Tile::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_v0[Tile::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_v1[Tile::kBytes];
+  // buffer P of K / V (P a compile-time 0 or 1)
+  auto k_lds = [&](auto par_tag) {
+    return (ATTN_LDS unsigned char*)(decltype(par_tag)::value ? lds_k1 : lds_k0);
+  };
+  auto v_lds = [&](auto par_tag) {
+    return (ATTN_LDS unsigned char*)(decltype(par_tag)::value ? lds_v1 : lds_v0);
+  };
+  using Par0 = std::integral_constant<int, 0>;
+  using Par1 = std::integral_constant<int, 1>;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -105,20 +110,17 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int kv_end = CAUSAL ? min(N, (qt + 1) * kFwdBQ) : N;
   const int n_tiles = (kv_end + kFwdBK - 1) / kFwdBK;
 
-  using Tile = SwzTile<D>;
-  auto load_tile = [&](const __bf16* src, int j, int buf_off) {
-    Tile::template load<kFwdThreads / 64>(src, j * kFwdBK, N,
-                                          (ATTN_LDS unsigned char*)smem + buf_off, wave, lane);
+  auto load_tile = [&](const __bf16* src, int j, ATTN_LDS unsigned char* dst) {
+    Tile::template load<kFwdThreads / 64>(src, j * kFwdBK, N, dst, wave, lane);
   };
   // per-lane LDS read offsets: K rows (A operand of S^T) and V transpose reads
   const int k_base = Tile::row_read_base(l32, half);
   const int v_base_lo = Tile::tr_read_base(lane, false);
   const int v_base_hi = Tile::tr_read_base(lane, true);
 
-  // S^T = K Q^T for the two 32-key halves of the K tile in buffer `kb_off`
-  // (two independent MFMA chains).
-  auto qk = [&](f32x16 (&sacc)[2], int kb_off) {
-    const ATTN_LDS unsigned char* kbuf = (const ATTN_LDS unsigned char*)smem + kb_off;
+  // S^T = K Q^T for the two 32-key halves of the K tile in `kbuf` (two
+  // independent MFMA chains).
+  auto qk = [&](f32x16 (&sacc)[2], const ATTN_LDS unsigned char* kbuf) {
     sacc[0] = f32x16{};
     sacc[1] = f32x16{};
 #pragma unroll
@@ -126,7 +128,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       const int a_off = k_base ^ (32 * s);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(kbuf + a_off + kb * 32 * L::kRowBytes);
+        const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(kbuf + a_off + kb * 32 * RB);
         sacc[kb] = mfma_32x32x16(a, qf[s], sacc[kb]);
       }
     }
@@ -149,11 +151,13 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // while the VALU evaluates the exponentials of tile j, then adds
   // V_j^T P_j^T to O^T.  MASK selects the path for tiles that straddle the
   // causal diagonal or the end of the sequence.
-  auto step = [&](const int j, f32x16 (&sc)[2], f32x16 (&sn)[2], auto mask_tag, auto next_tag) {
+  auto step = [&](const int j, auto par_tag, f32x16 (&sc)[2], f32x16 (&sn)[2], auto mask_tag,
+                  auto next_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
     constexpr bool NEXT = kPipelineQK && decltype(next_tag)::value;
+    using Other = std::integral_constant<int, 1 - decltype(par_tag)::value>;
     const int key0 = j * kFwdBK;
-    if constexpr (!kPipelineQK) qk(sc, L::k_buf(j & 1));
+    if constexpr (!kPipelineQK) qk(sc, k_lds(par_tag));
     if constexpr (MASK) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -206,20 +210,20 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       }
     };
     if constexpr (NEXT) {
-      const ATTN_LDS unsigned char* kbuf = (const ATTN_LDS unsigned char*)smem + L::k_buf((j + 1) & 1);
+      const ATTN_LDS unsigned char* kbuf = k_lds(Other{});
       sn[0] = f32x16{};
       sn[1] = f32x16{};
       bf16x8 a[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        a[0][kb] = *reinterpret_cast<const ATTN_LDS bf16x8*>(kbuf + k_base + kb * 32 * L::kRowBytes);
+        a[0][kb] = *reinterpret_cast<const ATTN_LDS bf16x8*>(kbuf + k_base + kb * 32 * RB);
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         if (s + 1 < KS) {
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
             a[(s + 1) & 1][kb] = *reinterpret_cast<const ATTN_LDS bf16x8*>(
-                kbuf + (k_base ^ (32 * (s + 1))) + kb * 32 * L::kRowBytes);
+                kbuf + (k_base ^ (32 * (s + 1))) + kb * 32 * RB);
         }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) sn[kb] = mfma_32x32x16(a[s & 1][kb], qf[s], sn[kb]);
@@ -235,10 +239,10 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     // ---- O^T += V^T P^T: step u = (kb * 2 + t) * DB + b covers 16 keys and
     // 32 d rows; consecutive steps go to different accumulators, and each
     // step's V^T fragment is read one step ahead.
-    const ATTN_LDS unsigned char* vbuf = (const ATTN_LDS unsigned char*)smem + L::v_buf(j & 1);
+    const ATTN_LDS unsigned char* vbuf = v_lds(par_tag);
     auto read_v = [&](int u) {
       const int kt = u / DB, b = u % DB;
-      const int roff = kt * 16 * L::kRowBytes;  // kt = kb * 2 + t
+      const int roff = kt * 16 * RB;  // kt = kb * 2 + t
       return concat4(lds_read_tr4((const ATTN_LDS __bf16*)(vbuf + (v_base_lo ^ (64 * b)) + roff)),
                      lds_read_tr4((const ATTN_LDS __bf16*)(vbuf + (v_base_hi ^ (64 * b)) + roff)));
     };
@@ -263,24 +267,26 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // the buffer of K tile j, last read in iteration j-1) and V tile j+1 (into
   // the buffer of V tile j-1) are in flight meanwhile.  Not pipelined: K and
   // V tile j are read and the copies of K and V tile j+1 are in flight.  The
-  // barrier at the end of every iteration publishes the copies.
-  auto iteration = [&](const int j, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+  // barrier at the end of every iteration publishes the copies.  par_tag is
+  // the parity of j, so that every buffer is a compile-time choice.
+  auto iteration = [&](const int j, auto par_tag, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    using Other = std::integral_constant<int, 1 - decltype(par_tag)::value>;
     if constexpr (kPipelineQK) {
-      if (j + 2 < n_tiles) load_tile(kh, j + 2, L::k_buf(j & 1));
+      if (j + 2 < n_tiles) load_tile(kh, j + 2, k_lds(par_tag));
     } else {
-      if (j + 1 < n_tiles) load_tile(kh, j + 1, L::k_buf((j + 1) & 1));
+      if (j + 1 < n_tiles) load_tile(kh, j + 1, k_lds(Other{}));
     }
-    if (j + 1 < n_tiles) load_tile(vh, j + 1, L::v_buf((j + 1) & 1));
+    if (j + 1 < n_tiles) load_tile(vh, j + 1, v_lds(Other{}));
     if (j <= last_tile) {
       const int key0 = j * kFwdBK;
       const bool need_mask = (key0 + kFwdBK > N) || (CAUSAL && key0 + kFwdBK - 1 > q_wave0);
       const bool next = j < last_tile;
       if (need_mask) {
-        if (next) step(j, sc, sn, std::true_type{}, std::true_type{});
-        else step(j, sc, sn, std::true_type{}, std::false_type{});
+        if (next) step(j, par_tag, sc, sn, std::true_type{}, std::true_type{});
+        else step(j, par_tag, sc, sn, std::true_type{}, std::false_type{});
       } else {
-        if (next) step(j, sc, sn, std::false_type{}, std::true_type{});
-        else step(j, sc, sn, std::false_type{}, std::false_type{});
+        if (next) step(j, par_tag, sc, sn, std::false_type{}, std::true_type{});
+        else step(j, par_tag, sc, sn, std::false_type{}, std::false_type{});
       }
     }
     wait_vmem();
@@ -289,20 +295,20 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 
   // prologue: K tiles 0 and 1 and V tile 0 in LDS (and, pipelined, S^T of
   // tile 0 in registers)
-  load_tile(kh, 0, L::k_buf(0));
-  load_tile(vh, 0, L::v_buf(0));
-  if (kPipelineQK && n_tiles > 1) load_tile(kh, 1, L::k_buf(1));
+  load_tile(kh, 0, k_lds(Par0{}));
+  load_tile(vh, 0, v_lds(Par0{}));
+  if (kPipelineQK && n_tiles > 1) load_tile(kh, 1, k_lds(Par1{}));
   wait_vmem();
   __syncthreads();
   f32x16 s_even[2], s_odd[2];
   if constexpr (kPipelineQK) {
-    qk(s_even, L::k_buf(0));
+    qk(s_even, k_lds(Par0{}));
     __syncthreads();  // K buffer 0 is refilled in iteration 0
   }
 
   for (int j = 0; j < n_tiles; j += 2) {
-    iteration(j, s_even, s_odd);
-    if (j + 1 < n_tiles) iteration(j + 1, s_odd, s_even);
+    iteration(j, Par0{}, s_even, s_odd);
+    if (j + 1 < n_tiles) iteration(j + 1, Par1{}, s_odd, s_even);
   }
 
   // ---- epilogue: O = O / l, lse = ln2 * (m + log2 l)
