@@ -209,11 +209,34 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         pf[kb][i >> 3][i & 7] = (__bf16)p;
       }
     };
+    // V^T fragment for O^T += V^T P^T step u = (kb * 2 + t) * DB + b, which
+    // covers 16 keys (kt = kb * 2 + t) and 32 d rows (b)
+    const ATTN_LDS unsigned char* vbuf = v_lds(par_tag);
+    auto read_v = [&](int u) {
+      const int kt = u / DB, b = u % DB;
+      const int roff = kt * 16 * RB;
+      return concat4(lds_read_tr4((const ATTN_LDS __bf16*)(vbuf + (v_base_lo ^ (64 * b)) + roff)),
+                     lds_read_tr4((const ATTN_LDS __bf16*)(vbuf + (v_base_hi ^ (64 * b)) + roff)));
+    };
+    auto pv = [&](int u, const bf16x8& vfrag) {
+      const int kt = u / DB, b = u % DB;
+      oacc[b] = mfma_32x32x16(vfrag, pf[kt >> 1][kt & 1], oacc[b]);
+    };
+    constexpr int US = 4 * DB;
     if constexpr (NEXT) {
+      // k-step s issues the two MFMAs of S^T of tile j+1 for that step, the
+      // exponentials of 32 / KS scores of tile j and, from s = 2 on, two
+      // steps of O^T += V^T P^T of tile j: PV step u needs the scores of its
+      // 16 keys, which exp parts 2 kt and 2 kt + 1 produce, and is issued at
+      // k-step 2 + u / 2 >= 2 kt + 2.  The last four PV steps follow the
+      // loop.  MFMA and VALU work are thus spread evenly over the step.
+      static_assert(KS == 8 && US == 16, "schedule written for d = 128");
+      constexpr int kPvStart = 2;
+      constexpr int kPvInLoop = 2 * (KS - kPvStart);
       const ATTN_LDS unsigned char* kbuf = k_lds(Other{});
       sn[0] = f32x16{};
       sn[1] = f32x16{};
-      bf16x8 a[2][2];
+      bf16x8 a[2][2], va[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
         a[0][kb] = *reinterpret_cast<const ATTN_LDS bf16x8*>(kbuf + k_base + kb * 32 * RB);
@@ -225,36 +248,45 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             a[(s + 1) & 1][kb] = *reinterpret_cast<const ATTN_LDS bf16x8*>(
                 kbuf + (k_base ^ (32 * (s + 1))) + kb * 32 * RB);
         }
+        // V fragments of the PV steps of k-step s + 1
+        if (s + 1 >= kPvStart && s + 1 < KS) {
+          const int u0 = 2 * (s + 1 - kPvStart);
+          va[(s + 1) & 1][0] = read_v(u0);
+          va[(s + 1) & 1][1] = read_v(u0 + 1);
+        }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) sn[kb] = mfma_32x32x16(a[s & 1][kb], qf[s], sn[kb]);
         exp_part(s);
+        if (s >= kPvStart) {
+          const int u0 = 2 * (s - kPvStart);
+          pv(u0, va[s & 1][0]);
+          pv(u0 + 1, va[s & 1][1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      l_run += psum;
+      bf16x8 vt[2];
+      vt[0] = read_v(kPvInLoop);
+#pragma unroll
+      for (int u = kPvInLoop; u < US; ++u) {
+        if (u + 1 < US) vt[(u + 1) & 1] = read_v(u + 1);
+        pv(u, vt[u & 1]);
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
 #pragma unroll
       for (int s = 0; s < KS; ++s) exp_part(s);
-    }
-    l_run += psum;
-
-    // ---- O^T += V^T P^T: step u = (kb * 2 + t) * DB + b covers 16 keys and
-    // 32 d rows; consecutive steps go to different accumulators, and each
-    // step's V^T fragment is read one step ahead.
-    const ATTN_LDS unsigned char* vbuf = v_lds(par_tag);
-    auto read_v = [&](int u) {
-      const int kt = u / DB, b = u % DB;
-      const int roff = kt * 16 * RB;  // kt = kb * 2 + t
-      return concat4(lds_read_tr4((const ATTN_LDS __bf16*)(vbuf + (v_base_lo ^ (64 * b)) + roff)),
-                     lds_read_tr4((const ATTN_LDS __bf16*)(vbuf + (v_base_hi ^ (64 * b)) + roff)));
-    };
-    constexpr int US = 4 * DB;
-    bf16x8 va[2];
-    va[0] = read_v(0);
+      l_run += psum;
+      // O^T += V^T P^T; consecutive steps go to different accumulators, and
+      // each step's V^T fragment is read one step ahead.
+      bf16x8 vt[2];
+      vt[0] = read_v(0);
 #pragma unroll
-    for (int u = 0; u < US; ++u) {
-      if (u + 1 < US) va[(u + 1) & 1] = read_v(u + 1);
-      const int kt = u / DB, b = u % DB;
-      oacc[b] = mfma_32x32x16(va[u & 1], pf[kt >> 1][kt & 1], oacc[b]);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int u = 0; u < US; ++u) {
+        if (u + 1 < US) vt[(u + 1) & 1] = read_v(u + 1);
+        pv(u, vt[u & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 
