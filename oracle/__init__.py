@@ -83,6 +83,9 @@ def _declare(lib):
     lib.oracle_attn_fwd_rows.restype = ctypes.c_int
     lib.oracle_attn_fwd_rows.argtypes = [_DP, _DP, _DP, i64, i64, ctypes.c_int,
                                          ctypes.c_double, _I64P, i64, _DP, _DP]
+    lib.oracle_attn_fwd_rect.restype = ctypes.c_int
+    lib.oracle_attn_fwd_rect.argtypes = [_DP, _DP, _DP, i64, i64, i64, ctypes.c_int,
+                                         ctypes.c_double, _DP, _DP]
     lib.oracle_attn_bwd_head.restype = ctypes.c_int
     lib.oracle_attn_bwd_head.argtypes = [_DP, _DP, _DP, _DP, i64, i64, ctypes.c_int,
                                          ctypes.c_double, _DP, _DP, _DP, _DP, _DP, _DP]
@@ -169,6 +172,25 @@ def attn_fwd_rows(q, k, v, causal: bool, scale: float, rows, lib=None):
                                   _ptr(o), _ptr(lse))
     _check(rc, "attn_fwd_rows")
     return o, lse
+
+
+def attn_fwd_rect(q, k, v, causal: bool, scale: float, lib=None):
+    """O and lse of Nq queries ([..., Nq, d]) against Nk keys and values
+    ([..., Nk, d]); the queries are the last Nq positions, so under the causal
+    mask query i sees keys 0 .. i + Nk - Nq."""
+    lib = lib or load()
+    qh, lead = _heads(q)
+    kh, _ = _heads(k)
+    vh, _ = _heads(v)
+    G, Nq, d = qh.shape
+    Nk = kh.shape[1]
+    o = np.empty_like(qh)
+    lse = np.empty((G, Nq), dtype=np.float64)
+    for g in range(G):
+        rc = lib.oracle_attn_fwd_rect(_ptr(qh[g]), _ptr(kh[g]), _ptr(vh[g]), Nq, Nk, d,
+                                      int(bool(causal)), float(scale), _ptr(o[g]), _ptr(lse[g]))
+        _check(rc, "attn_fwd_rect")
+    return o.reshape(lead + (Nq, d)), lse.reshape(lead + (Nq,))
 
 
 def attn_bwd(q, k, v, dout, causal: bool, scale: float, lib=None):

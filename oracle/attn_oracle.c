@@ -172,6 +172,59 @@ int oracle_attn_fwd_rows(const double* q, const double* k, const double* v,
   return failed ? -3 : 0;
 }
 
+/* Forward for Nq queries against Nk keys of one head (decode- and
+ * prefill-shaped attention over a key/value cache: PDC notes Lecture 4,
+ * section 4.9; CS336 L5 notes section 5.3).  The queries are the last Nq
+ * positions of the sequence, so query i sits at position i + Nk - Nq; under
+ * the causal mask it sees keys 0 .. i + Nk - Nq.  Nq = Nk is the square case
+ * of oracle_attn_fwd_head.  q: [Nq][d], k, v: [Nk][d]; o: [Nq][d], lse: [Nq].
+ * With causal, Nk >= Nq is required (every query then sees key 0).  Same
+ * definition as above: score row, safe softmax, P row times V. */
+int oracle_attn_fwd_rect(const double* q, const double* k, const double* v,
+                         int64_t Nq, int64_t Nk, int64_t d, int causal, double scale,
+                         double* o, double* lse) {
+  if (!q || !k || !v || !o || !lse) return -1;
+  if (Nq < 1 || Nk < 1 || d < 1 || (causal && Nk < Nq)) return -2;
+  const int64_t offset = Nk - Nq;
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)Nk);
+    double* p = (double*)malloc(sizeof(double) * (size_t)Nk);
+    if (!s || !p) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t i = 0; i < Nq; ++i) {
+        const double* qi = q + i * d;
+        for (int64_t j = 0; j < Nk; ++j) {
+          if (causal && j > i + offset) {
+            s[j] = -INFINITY;
+            continue;
+          }
+          const double* kj = k + j * d;
+          double dot = 0.0;
+          for (int64_t c = 0; c < d; ++c) dot += qi[c] * kj[c];
+          s[j] = dot * scale;
+        }
+        double m, l;
+        oracle_softmax_row(s, Nk, p, &m, &l);
+        lse[i] = log(l) + m;
+        double* oi = o + i * d;
+        for (int64_t c = 0; c < d; ++c) oi[c] = 0.0;
+        for (int64_t j = 0; j < Nk; ++j) {
+          const double* vj = v + j * d;
+          for (int64_t c = 0; c < d; ++c) oi[c] += p[j] * vj[c];
+        }
+      }
+    }
+    free(s);
+    free(p);
+  }
+  return failed ? -3 : 0;
+}
+
 /* Backward for one head (CS336 L5 notes section 8.4): the exact gradient of
  * sum(dO * O).  Inputs q, k, v, dout: [N][d].  Outputs dq, dk, dv: [N][d].
  * o_out [N][d], lse_out [N] and D_out [N], when not NULL, receive the

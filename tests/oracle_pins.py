@@ -22,6 +22,10 @@ What pins what:
   row maximum is subtracted.
 * backward - finite differences of the 50-digit forward; the D identity of
   CS336 L5 notes Exercise 9; sum_j dV_j = sum_i dO_i; sum_j dK_j = 0.
+* Nq queries against Nk keys (the last Nq positions, PDC notes Lecture 4
+  section 4.9 key/value cache): 50-digit brute force with the shifted causal
+  mask, Q = 0 closed form, and the blocked merge of per-chunk (O, lse) pairs
+  (CS149 L9 notes section 9) that split-key attention relies on.
 """
 from __future__ import annotations
 
@@ -59,6 +63,28 @@ def dec_forward(q, k, v, causal, scale, prec=50):
             w.append(s.exp())
         Z = sum(w, Decimal(0))
         O.append([sum((w[j] * v[j][c] for j in range(N)), Decimal(0)) / Z for c in range(d)])
+        lse.append(Z.ln())
+    return O, lse
+
+
+def dec_forward_rect(q, k, v, causal, scale, prec=50):
+    """Textbook attention of len(q) queries at the last positions of a
+    len(k)-key sequence, in Decimal: query i sees keys j <= i + Nk - Nq under
+    the causal mask.  Returns (O, lse) as nested lists of Decimal."""
+    getcontext().prec = prec
+    Nq, Nk, d = len(q), len(k), len(q[0])
+    sc = Decimal(scale)
+    O, lse = [], []
+    for i in range(Nq):
+        w = []
+        for j in range(Nk):
+            if causal and j > i + (Nk - Nq):
+                w.append(Decimal(0))
+                continue
+            s = sum((q[i][c] * k[j][c] for c in range(d)), Decimal(0)) * sc
+            w.append(s.exp())
+        Z = sum(w, Decimal(0))
+        O.append([sum((w[j] * v[j][c] for j in range(Nk)), Decimal(0)) / Z for c in range(d)])
         lse.append(Z.ln())
     return O, lse
 
@@ -325,8 +351,60 @@ def pin_bwd_invariants(lib):
         _assert_close(g["dk"].sum(0), np.zeros(6), 0, 1e-12 * np.abs(g["dk"]).sum(), "sum dK")
 
 
+# ---------------------------------------------------------------- Nq x Nk pins
+def pin_rect_brute_force(lib):
+    """Nq queries at the end of an Nk-key sequence: 50-digit brute force."""
+    rng = _rng(31)
+    for Nq, Nk, d, causal in [(3, 7, 3, True), (1, 6, 4, True), (4, 4, 2, True),
+                              (5, 9, 3, False), (2, 5, 4, True), (6, 6, 3, False)]:
+        q = rng.normal(0, 1.5, size=(Nq, d))
+        k, v = rng.normal(0, 1.5, size=(2, Nk, d))
+        scale = 1 / math.sqrt(d)
+        o, lse = oracle.attn_fwd_rect(q, k, v, causal, scale, lib=lib)
+        Od, Ld = dec_forward_rect(_to_dec(q), _to_dec(k), _to_dec(v), causal, scale)
+        _assert_close(o, np.array([[float(x) for x in r] for r in Od]), 1e-13, 1e-14, "rect brute O")
+        _assert_close(lse, np.array([float(x) for x in Ld]), 1e-14, 1e-14, "rect brute lse")
+
+
+def pin_rect_q_zero(lib):
+    """Q = 0: every visible key gets the same weight, so O_i is the mean of
+    the visible V rows and lse_i = ln(number of visible keys)."""
+    rng = _rng(32)
+    Nq, Nk, d = 5, 13, 4
+    k, v = rng.normal(size=(2, Nk, d))
+    q = np.zeros((Nq, d))
+    o, lse = oracle.attn_fwd_rect(q, k, v, False, 0.5, lib=lib)
+    _assert_close(o, np.tile(v.mean(0), (Nq, 1)), 1e-13, 1e-13, "rect Q=0 mean")
+    _assert_close(lse, np.full(Nq, math.log(Nk)), 1e-14, 0, "rect Q=0 lse")
+    o, lse = oracle.attn_fwd_rect(q, k, v, True, 0.5, lib=lib)
+    seen = np.arange(Nq) + (Nk - Nq) + 1
+    _assert_close(o, np.stack([v[:n].mean(0) for n in seen]), 1e-13, 1e-13, "rect Q=0 causal")
+    _assert_close(lse, np.log(seen), 1e-14, 1e-15, "rect Q=0 causal lse")
+
+
+def pin_rect_merge(lib):
+    """CS149 L9 notes section 9: attention over a split key range equals the
+    merge of the per-chunk results, lse = ln sum_c e^{lse_c} and
+    O = sum_c e^{lse_c - lse} O_c, for chunk sizes that do not divide Nk."""
+    rng = _rng(33)
+    Nq, Nk, d = 3, 23, 5
+    q = rng.normal(size=(Nq, d))
+    k, v = rng.normal(size=(2, Nk, d))
+    o, lse = oracle.attn_fwd_rect(q, k, v, False, 0.6, lib=lib)
+    edges = [0, 4, 11, 12, 23]
+    parts = [oracle.attn_fwd_rect(q, k[a:b], v[a:b], False, 0.6, lib=lib)
+             for a, b in zip(edges[:-1], edges[1:])]
+    m = np.max([lc for _, lc in parts], axis=0)
+    w = [np.exp(lc - m) for _, lc in parts]
+    lse_m = m + np.log(sum(w))
+    o_m = sum(wc[:, None] * oc for wc, (oc, _) in zip(w, parts)) / sum(w)[:, None]
+    _assert_close(lse_m, lse, 1e-14, 1e-14, "merged lse")
+    _assert_close(o_m, o, 1e-13, 1e-14, "merged O")
+
+
 FORWARD_PINS = [pin_worked_example, pin_blocked_identity, pin_streaming_and_blocked,
                 pin_rows_sum_to_one, pin_constant_v, pin_q_zero, pin_row0_and_single_key,
                 pin_brute_force, pin_large_logits, pin_rows_entry]
 BACKWARD_PINS = [pin_bwd_finite_differences, pin_bwd_D_identity, pin_bwd_invariants]
-ALL_PINS = FORWARD_PINS + BACKWARD_PINS
+RECT_PINS = [pin_rect_brute_force, pin_rect_q_zero, pin_rect_merge]
+ALL_PINS = FORWARD_PINS + BACKWARD_PINS + RECT_PINS

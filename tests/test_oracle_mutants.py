@@ -35,6 +35,10 @@ MUTANTS = {
     "D_uses_V": ("acc += dout[i * d + c] * O[i * d + c];", "acc += dout[i * d + c] * v[i * d + c];"),
     "dq_uses_V": ("dq[i * d + c] += g * k[j * d + c];", "dq[i * d + c] += g * v[j * d + c];"),
     "rows_wrong_index": ("const int64_t i = rows[r];", "const int64_t i = r;"),
+    "rect_mask_unshifted": ("if (causal && j > i + offset) {", "if (causal && j > i) {"),
+    "rect_scale_dropped": ("s[j] = dot * scale;", "s[j] = dot;"),
+    "rect_lse_log2": ("lse[i] = log(l) + m;", "lse[i] = log2(l) + m;"),
+    "rect_pv_key_offset": ("oi[c] += p[j] * vj[c];", "oi[c] += p[j] * vj[c] * (j + 1 < Nk);"),
 }
 
 
