@@ -84,3 +84,63 @@ def workload_inputs(w: Workload, with_dout: bool | None = None):
     if with_dout is None:
         with_dout = w.backward
     return make_inputs(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.qk_std, with_dout)
+
+
+@dataclass(frozen=True)
+class KvWorkload:
+    """Nq queries (the last Nq positions) against an Nk-token key/value
+    cache: decode (Nq = 1) and chunked prefill shapes."""
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    dtype: torch.dtype
+    causal: bool
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(self.d) ** 0.5
+
+    def kv_bytes(self) -> float:
+        """Bytes of K and V, each read once: the compulsory HBM traffic that
+        bounds decode."""
+        return 2.0 * self.B * self.H * self.Nk * self.d * torch.finfo(self.dtype).bits / 8
+
+    def flops(self) -> float:
+        """4*B*H*Nq*d times the number of visible (query, key) pairs per head."""
+        if self.causal:
+            off = self.Nk - self.Nq
+            pairs = sum(min(self.Nk, i + off + 1) for i in range(self.Nq))
+        else:
+            pairs = self.Nq * self.Nk
+        return 4.0 * self.B * self.H * pairs * self.d
+
+
+# Decode and chunked-prefill shapes for attn_fwd_kv.  The pages give no decode
+# shape; these are typical serving sizes (8 sequences of 8k tokens, 32 heads).
+KV_WORKLOADS = {
+    "decode_b8_h32_nq1_nk8192_d128": KvWorkload("decode_b8_h32_nq1_nk8192_d128", 8, 32, 1, 8192,
+                                                128, torch.bfloat16, True, 6),
+    "prefill_b2_h16_nq512_nk4096_d128": KvWorkload("prefill_b2_h16_nq512_nk4096_d128", 2, 16, 512,
+                                                   4096, 128, torch.bfloat16, True, 7),
+}
+
+
+def make_kv_inputs(B: int, H: int, Nq: int, Nk: int, d: int, dtype: torch.dtype = torch.bfloat16,
+                   seed: int = 0):
+    """CPU tensors q [B, H, Nq, d] and k, v [B, H, Nk, d]: a seeded CPU
+    generator draws Q, K, V in that order as float32 N(0, 1), then rounds to
+    ``dtype``."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    q = torch.randn((B, H, Nq, d), generator=g, dtype=torch.float32)
+    k = torch.randn((B, H, Nk, d), generator=g, dtype=torch.float32)
+    v = torch.randn((B, H, Nk, d), generator=g, dtype=torch.float32)
+    return q.to(dtype), k.to(dtype), v.to(dtype)
+
+
+def kv_workload_inputs(w: KvWorkload):
+    return make_kv_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, w.seed)

@@ -115,10 +115,43 @@ int attn_bwd_phase(int phase, const void* q, const void* k, const void* v, const
                    void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
                    int causal, float scale, int dtype, void* stream);
 
+/* Bytes of device workspace attn_fwd_kv needs for these sizes and this
+ * num_splits (0 = the library's choice, the same one attn_fwd_kv makes): fp32
+ * partial O and lse of every key chunk, each part rounded up to a multiple of
+ * 256.  Returns 0 for invalid sizes or an unsupported dtype. */
+size_t attn_fwd_kv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits,
+                                   int dtype);
+
+/* Forward of Nq queries against an Nk-token key/value cache: decode (Nq = 1)
+ * and chunked prefill (PDC notes Lecture 4, section 4.9; CS336 L5 notes
+ * section 5.3).  The queries are the last Nq positions of the sequence.
+ *   q          : [B][H][Nq][d] bf16, read only.
+ *   k, v       : [B][H][Nk][d] bf16, read only.
+ *   o          : [B][H][Nq][d] bf16, written.
+ *   lse        : [B][H][Nq] float32, written (natural log, as attn_fwd).
+ *   causal     : != 0 hides key j from query i when j > i + Nk - Nq, and then
+ *                requires Nk >= Nq; 0 lets every query see every key.
+ *   num_splits : number of key chunks streamed by separate workgroups and
+ *                merged with the blocked-softmax identity (CS149 L9 notes
+ *                section 9); 0 = chosen from the shape; values above
+ *                ceil(Nk / 64) are capped.  It changes rounding only.
+ *   workspace  : device scratch of at least attn_fwd_kv_workspace_bytes()
+ *                bytes with the same num_splits, caller-owned; contents on
+ *                entry are ignored.
+ *   dtype      : ATTN_DTYPE_BF16 only (ATTN_ERR_DTYPE otherwise).
+ * Nq = Nk computes what attn_fwd computes, by a different kernel.  Calls that
+ * share a workspace must not overlap in time.  Returns ATTN_OK or an error:
+ * those of attn_fwd, plus ATTN_ERR_SHAPE for Nq or Nk < 1, Nk < Nq with
+ * causal, or num_splits < 0, and ATTN_ERR_WORKSPACE. */
+int attn_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
+                int B, int H, int Nq, int Nk, int d, int causal, float scale, int dtype,
+                int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable text for a return code (never NULL). */
 const char* attn_status_str(int status);
 
-/* Library ABI version; bumped when a signature changes. */
+/* Library ABI version; bumped when an entry point is added or a signature
+ * changes (2: attn_fwd_kv and attn_fwd_kv_workspace_bytes). */
 int attn_abi_version(void);
 
 #ifdef __cplusplus

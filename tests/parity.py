@@ -105,3 +105,19 @@ def describe(err: dict) -> str:
 
 __all__ = ["compare", "gpu_forward", "gpu_backward", "sample_rows", "oracle_full_fwd",
            "oracle_rows_fwd", "to_np", "f32_scale", "log", "describe", "math"]
+
+
+def gpu_forward_kv(q, k, v, causal, scale, num_splits=0):
+    """q [B,H,Nq,d], k, v [B,H,Nk,d] CPU tensors; runs attn_fwd_kv on the GPU
+    with a poisoned workspace; returns CPU (o, lse)."""
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    o = torch.full_like(qd, float("nan"))
+    lse = torch.full((B, H, Nq), float("nan"), device=dev, dtype=torch.float32)
+    ws = torch.full((T.attn_fwd_kv_workspace_bytes(B, H, Nq, Nk, d, num_splits),), 0xFF,
+                    device=dev, dtype=torch.uint8)
+    T.attn_fwd_kv(qd, kd, vd, o, lse, causal, scale, num_splits, ws)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()

@@ -27,7 +27,8 @@ def _lib():
 
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted(["attn_fwd", "attn_bwd", "attn_bwd_phase",
-                                           "attn_bwd_workspace_bytes", "attn_status_str",
+                                           "attn_bwd_workspace_bytes", "attn_fwd_kv",
+                                           "attn_fwd_kv_workspace_bytes", "attn_status_str",
                                            "attn_abi_version"])
 
 
@@ -41,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = _lib()
-    assert lib.attn_abi_version() == 1
+    assert lib.attn_abi_version() == 2
     for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, 12345]:
         s = lib.attn_status_str(code)
         assert isinstance(s, bytes) and len(s) > 0
@@ -105,3 +106,46 @@ def test_bwd_phase_validation():
     bad = list(args)
     bad[9] = None  # workspace
     assert lib.attn_bwd_phase(1, *bad) == -7
+
+
+def test_kv_workspace_size():
+    """Partial O (d floats) and lse (one float) per split, head and query,
+    each part rounded up to 256 bytes; the automatic split count depends
+    only on the shape."""
+    lib = _lib()
+    for B, H, Nq, Nk, d, splits in ((1, 1, 1, 100, 64, 1), (2, 3, 7, 1000, 128, 5),
+                                    (8, 32, 1, 8192, 128, 0), (1, 2, 300, 300, 64, 0)):
+        n = lib.attn_fwd_kv_workspace_bytes(B, H, Nq, Nk, d, splits, 1)
+        tiles = (Nk + 63) // 64
+        if splits == 0:
+            assert n == lib.attn_fwd_kv_workspace_bytes(B, H, Nq, Nk, d, 0, 1)
+            assert n > 0
+            continue
+        per = -(-tiles // min(splits, tiles))
+        eff = -(-tiles // per)
+        rows = eff * B * H * Nq
+        r256 = lambda x: (x + 255) // 256 * 256
+        assert n == r256(rows * d * 4) + r256(rows * 4)
+    assert lib.attn_fwd_kv_workspace_bytes(1, 1, 0, 10, 64, 0, 1) == 0
+    assert lib.attn_fwd_kv_workspace_bytes(1, 1, 4, 10, 96, 0, 1) == 0
+    assert lib.attn_fwd_kv_workspace_bytes(1, 1, 4, 10, 64, -1, 1) == 0
+    assert lib.attn_fwd_kv_workspace_bytes(1, 1, 4, 10, 64, 0, 0) == 0  # fp32 unsupported
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(q=0), -1), (dict(lse=0), -1),
+    (dict(B=0), -2), (dict(Nq=0), -2), (dict(Nk=0), -2), (dict(splits=-1), -2),
+    (dict(Nq=20, Nk=10, causal=1), -2),
+    (dict(d=96), -4), (dict(dtype=0), -3), (dict(dtype=5), -3),
+    (dict(k=FAKE + 4), -5), (dict(scale=float("nan")), -6),
+    (dict(ws=0), -7), (dict(ws_bytes=8), -7), (dict(ws=FAKE + 8), -5),
+])
+def test_kv_validation(args, code):
+    lib = _lib()
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, Nq=4, Nk=100, d=64, causal=1,
+             scale=0.125, dtype=1, splits=0, ws=FAKE, ws_bytes=1 << 30)
+    a.update(args)
+    rc = lib.attn_fwd_kv(a["q"] or None, a["k"], a["v"], a["o"], a["lse"] or None, a["B"],
+                         a["H"], a["Nq"], a["Nk"], a["d"], a["causal"], a["scale"], a["dtype"],
+                         a["splits"], a["ws"] or None, a["ws_bytes"], None)
+    assert rc == code

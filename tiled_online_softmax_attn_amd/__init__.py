@@ -9,7 +9,8 @@ library raises ``AttnLibraryMissing``.
 
 Tensors: Q, K, V, O, dO, dQ, dK, dV are CUDA(HIP) tensors of shape
 [B, H, N, d], contiguous, all of one dtype (torch.bfloat16, or torch.float32
-for the forward only); lse is float32 [B, H, N].
+for the forward only); lse is float32 [B, H, N].  attn_fwd_kv takes Q and O
+of shape [B, H, Nq, d] and K, V of shape [B, H, Nk, d] (bf16).
 """
 from __future__ import annotations
 
@@ -27,7 +28,7 @@ STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR
           -4: "ATTN_ERR_HEADDIM", -5: "ATTN_ERR_ALIGN", -6: "ATTN_ERR_SCALE",
           -7: "ATTN_ERR_WORKSPACE", -8: "ATTN_ERR_HIP"}
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_phase", "attn_bwd_workspace_bytes",
-           "attn_status_str", "attn_abi_version")
+           "attn_fwd_kv", "attn_fwd_kv_workspace_bytes", "attn_status_str", "attn_abi_version")
 
 
 class AttnLibraryMissing(RuntimeError):
@@ -62,6 +63,11 @@ def lib() -> ctypes.CDLL:
                                      i, i, i, i, i, f, i, vp]
         L.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
+        L.attn_fwd_kv.restype = i
+        L.attn_fwd_kv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp,
+                                  ctypes.c_size_t, vp]
+        L.attn_fwd_kv_workspace_bytes.restype = ctypes.c_size_t
+        L.attn_fwd_kv_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
         L.attn_status_str.restype = ctypes.c_char_p
         L.attn_status_str.argtypes = [i]
         L.attn_abi_version.restype = i
@@ -153,6 +159,28 @@ def attn_bwd_phase(phase: int, q, k, v, o, dout, lse, dq, dk, dv, workspace, cau
         raise AttnError(rc, f"attn_bwd_phase({phase})")
 
 
+def attn_fwd_kv_workspace_bytes(B: int, H: int, Nq: int, Nk: int, d: int, num_splits: int = 0,
+                                dtype: torch.dtype = torch.bfloat16) -> int:
+    code = ATTN_DTYPE_BF16 if dtype == torch.bfloat16 else ATTN_DTYPE_F32
+    return int(lib().attn_fwd_kv_workspace_bytes(B, H, Nq, Nk, d, int(num_splits), code))
+
+
+def attn_fwd_kv(q, k, v, o, lse, causal: bool, scale: float, num_splits: int, workspace,
+                stream=None) -> None:
+    """Enqueue the forward of Nq queries (the last Nq positions) against Nk
+    cached keys and values; the key range is split into ``num_splits`` chunks
+    (0 = chosen by the library) whose partial results are merged."""
+    _check_contig(q, k, v, o, lse)
+    B, H, Nq, d = _shape(q)
+    Nk = int(k.shape[2])
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().attn_fwd_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
+                           int(bool(causal)), float(scale), _dtype_code(q), int(num_splits),
+                           _ptr(workspace), ws_bytes, _stream_handle(stream))
+    if rc != 0:
+        raise AttnError(rc, "attn_fwd_kv")
+
+
 # ------------------------------------------------------------ conveniences
 def flash_attention_forward(q, k, v, causal: bool = False, scale: float | None = None):
     """Allocate o and lse with torch and run attn_fwd; returns (o, lse)."""
@@ -162,6 +190,23 @@ def flash_attention_forward(q, k, v, causal: bool = False, scale: float | None =
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
     attn_fwd(q, k, v, o, lse, causal, scale)
+    return o, lse
+
+
+def flash_attention_kv(q, k, v, causal: bool = False, scale: float | None = None,
+                       num_splits: int = 0, workspace=None):
+    """Allocate o, lse (and a workspace if none is given) and run attn_fwd_kv;
+    returns (o, lse)."""
+    B, H, Nq, d = _shape(q)
+    Nk = int(k.shape[2])
+    if scale is None:
+        scale = d ** -0.5
+    if workspace is None:
+        workspace = torch.empty(attn_fwd_kv_workspace_bytes(B, H, Nq, Nk, d, num_splits, q.dtype),
+                                device=q.device, dtype=torch.uint8)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), device=q.device, dtype=torch.float32)
+    attn_fwd_kv(q, k, v, o, lse, causal, scale, num_splits, workspace)
     return o, lse
 
 

@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -48,7 +48,8 @@ const char* attn_status_str(int status) {
     case ATTN_ERR_HEADDIM: return "head dimension d must be 64 or 128";
     case ATTN_ERR_ALIGN: return "pointers must be 16-byte aligned";
     case ATTN_ERR_SCALE: return "scale must be finite";
-    case ATTN_ERR_WORKSPACE: return "workspace is NULL or smaller than attn_bwd_workspace_bytes()";
+    case ATTN_ERR_WORKSPACE:
+      return "workspace is NULL or smaller than the matching *_workspace_bytes()";
     case ATTN_ERR_HIP: return "the HIP runtime refused the kernel launch";
     default: return "unknown attn status";
   }
@@ -110,6 +111,47 @@ int attn_bwd_phase(int phase, const void* q, const void* k, const void* v, const
   if (phase < 0 || phase > 2) return ATTN_ERR_SHAPE;
   return bwd_common(phase, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H,
                     N, d, causal, scale, dtype, stream);
+}
+
+// Sizes of attn_fwd_kv: both sequence lengths >= 1, the causal alignment
+// needs Nk >= Nq, and the grid (B*H*ceil(Nq/128)*splits workgroups, at most
+// B*H*ceil(Nq/128)*ceil(Nk/64)) must fit a 32-bit count.
+static int check_kv_shape(int B, int H, int Nq, int Nk, int d, int causal, int num_splits) {
+  if (Nq < 1 || Nk < 1 || num_splits < 0) return ATTN_ERR_SHAPE;
+  if ((int64_t)Nq + (int64_t)Nk >= (int64_t)INT32_MAX) return ATTN_ERR_SHAPE;
+  if (causal && Nk < Nq) return ATTN_ERR_SHAPE;
+  int rc = check_shape(B, H, Nq > Nk ? Nq : Nk, d);
+  if (rc != ATTN_OK) return rc;
+  const int64_t wgs = (int64_t)B * H * (((int64_t)Nq + 127) / 128) * (((int64_t)Nk + 63) / 64);
+  if (wgs > (int64_t)INT32_MAX) return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
+size_t attn_fwd_kv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits,
+                                   int dtype) {
+  if (check_kv_shape(B, H, Nq, Nk, d, 0, num_splits) != ATTN_OK || dtype != ATTN_DTYPE_BF16)
+    return 0;
+  const attn::KvSplit sp = attn::kv_split_plan(B, H, Nq, Nk, d, num_splits);
+  return sp.o_part_bytes + sp.lse_part_bytes;
+}
+
+int attn_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                int Nq, int Nk, int d, int causal, float scale, int dtype, int num_splits,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+  int rc = check_kv_shape(B, H, Nq, Nk, d, causal, num_splits);
+  if (rc != ATTN_OK) return rc;
+  if (dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
+  const void* ptrs[] = {q, k, v, o, lse};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return ATTN_ERR_ALIGN;
+  if (!isfinite(scale)) return ATTN_ERR_SCALE;
+  const size_t need = attn_fwd_kv_workspace_bytes(B, H, Nq, Nk, d, num_splits, dtype);
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+  attn::FwdKvArgs a{q, k, v, o, lse, B, H, Nq, Nk, d, causal != 0, scale, num_splits,
+                    workspace, stream};
+  return attn::launch_fwd_kv(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 }  // extern "C"

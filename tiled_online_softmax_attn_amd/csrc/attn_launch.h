@@ -37,7 +37,35 @@ struct BwdArgs {
   void* stream;
 };
 
+// Nq queries (the last Nq positions) against Nk keys, the keys cut into
+// chunks processed by separate workgroups and merged (attn_fwd_kv).
+struct FwdKvArgs {
+  const void* q;  // [B][H][Nq][d] bf16
+  const void* k;  // [B][H][Nk][d] bf16
+  const void* v;  // [B][H][Nk][d] bf16
+  void* o;        // [B][H][Nq][d] bf16
+  float* lse;     // [B][H][Nq]
+  int B, H, Nq, Nk, d;
+  int causal;
+  float scale;
+  int num_splits;   // 0 = chosen from the shape
+  void* workspace;  // kv_split_plan(...).o_part_bytes + lse_part_bytes
+  void* stream;
+};
+
+// How attn_fwd_kv cuts the keys: `splits` chunks of `chunk` keys (a multiple
+// of the 64-key tile; the last chunk may be shorter), and the workspace it
+// needs for the partial results.
+struct KvSplit {
+  int splits;
+  int chunk;
+  size_t o_part_bytes;    // fp32 [splits][B*H][Nq][d], rounded up to 256
+  size_t lse_part_bytes;  // fp32 [splits][B*H][Nq], rounded up to 256
+};
+KvSplit kv_split_plan(int B, int H, int Nq, int Nk, int d, int num_splits);
+
 hipError_t launch_fwd(const FwdArgs& a);
+hipError_t launch_fwd_kv(const FwdKvArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
 // phase 0 = preprocess (D), 1 = dK and dV, 2 = dQ
 hipError_t launch_bwd_phase(const BwdArgs& a, int phase);
