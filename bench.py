@@ -7,6 +7,11 @@ preprocess D, dK/dV, dQ) on the causal B=4 H=16 N=4096 d=128 bf16
 workload.  Inputs are generated on the host from a fixed seed, copied to the
 GPU, and resident in HBM before the timed region starts.
 
+With `--workload` naming a key/value-cache shape (attn_inputs.KV_WORKLOADS,
+e.g. decode_b8_h32_nq1_nk8192_d128) a step is instead one attn_fwd_kv call
+(per-chunk partial kernel + merge kernel) and `value` is the K/V bytes read
+per second, the quantity that bounds decode.
+
 Prints ONE JSON line.  `value` is fwd+bwd TFLOP/s by the formula
 4*B*H*N^2*d (halved for causal) for the forward plus 2.5x that for the
 backward, over the K timed steps.  `roofline` describes the kernel with the
@@ -165,6 +170,94 @@ def pmc_summary(dirs, copy_mib: float, workload: str) -> int:
     return 0
 
 
+def cpu_baseline_kv(w, q, k, v, budget_s: float):
+    """The oracle's Nq x Nk forward on whole heads for about budget_s seconds;
+    rate in K/V bytes per second, like the GPU value."""
+    import numpy as np
+
+    import oracle
+    lib = oracle.load()
+    scale = float(np.float32(w.scale))
+    f64 = lambda t: t.to("cpu").double().numpy()
+    heads, t0 = 0, time.perf_counter()
+    for b in range(w.B):
+        for h in range(w.H):
+            oracle.attn_fwd_rect(f64(q[b, h]), f64(k[b, h]), f64(v[b, h]), w.causal, scale, lib=lib)
+            heads += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        else:
+            continue
+        break
+    el = time.perf_counter() - t0
+    eprint(f"[cpu_baseline] oracle: {heads} heads in {el:.1f} s")
+    return {"value": w.kv_bytes() / (w.B * w.H) * heads / el / 1e9, "unit": "GB/s",
+            "cores": oracle.num_threads(lib), "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} heads of {w.name} (fp64 forward per head), "
+                      f"{el:.1f} s"}
+
+
+def bench_kv(args, w):
+    """One step = attn_fwd_kv over the whole cache workload."""
+    import torch
+
+    import tiled_online_softmax_attn_amd as T
+    from attn_inputs import kv_workload_inputs
+
+    T.lib()
+    dev = torch.device("cuda:0")
+    eprint(f"[bench] generating inputs for {w.name}")
+    q, k, v = kv_workload_inputs(w)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.Nq), device=dev, dtype=torch.float32)
+    ws = torch.empty(T.attn_fwd_kv_workspace_bytes(w.B, w.H, w.Nq, w.Nk, w.d, 0, w.dtype),
+                     device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        T.attn_fwd_kv(qd, kd, vd, o, lse, w.causal, w.scale, 0, ws, stream)
+
+    eprint(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    eprint(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / args.steps
+    value = w.kv_bytes() * args.steps / wall / 1e9
+    # bytes of one call: K and V once, Q read and O, lse written; the fp32
+    # per-chunk partials are extra traffic of the split, not counted
+    elem = torch.finfo(w.dtype).bits // 8
+    algo = w.kv_bytes() + w.B * w.H * w.Nq * (2 * w.d * elem + 4)
+    achieved = algo / (call_ms * 1e-3) / 1e9
+    roofline = {"kernel": "fwd_kv (chunk partials + merge, one call)", "bound": "hbm",
+                "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    cpu = None if args.no_cpu_baseline else cpu_baseline_kv(w, q, k, v,
+                                                             args.cpu_baseline_seconds)
+    out = {
+        "metric": f"attention over a key/value cache, K/V bytes read per second, {w.name}",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q, K, V)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                   "causal": w.causal, "step": "attn_fwd_kv"},
+        "tflops": round(w.flops() / (call_ms * 1e-3) / 1e12, 2),
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -193,12 +286,15 @@ def main():
     import torch
 
     import tiled_online_softmax_attn_amd as T
-    from attn_inputs import HEADLINE, WORKLOADS, workload_inputs
+    from attn_inputs import HEADLINE, KV_WORKLOADS, WORKLOADS, workload_inputs
 
-    w = WORKLOADS[args.workload or HEADLINE]
     if not torch.cuda.is_available():
         eprint("bench.py needs a GPU")
         sys.exit(1)
+    if args.workload in KV_WORKLOADS:
+        bench_kv(args, KV_WORKLOADS[args.workload])
+        return
+    w = WORKLOADS[args.workload or HEADLINE]
     T.lib()
     dev = torch.device("cuda:0")
     eprint(f"[bench] generating inputs for {w.name}")
