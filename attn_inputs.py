@@ -144,3 +144,49 @@ def make_kv_inputs(B: int, H: int, Nq: int, Nk: int, d: int, dtype: torch.dtype 
 
 def kv_workload_inputs(w: KvWorkload):
     return make_kv_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, w.seed)
+
+
+@dataclass(frozen=True)
+class SoftmaxWorkload:
+    """Row softmax of an M x N matrix of scores (M rows of N keys)."""
+    name: str
+    M: int
+    N: int
+    dtype: torch.dtype
+    seed: int
+    std: float = 1.0
+
+    def hbm_bytes(self) -> float:
+        """Each element read once and written once: the compulsory traffic."""
+        return 2.0 * self.M * self.N * torch.finfo(self.dtype).bits / 8
+
+
+# Attention-score rows: 65536 query rows (B4 H16 N1024) of 4096 keys, the
+# score distribution of scale * q.k with unit-normal q and k (N(0, 1)).
+SOFTMAX_WORKLOADS = {
+    "softmax_m65536_n4096_bf16": SoftmaxWorkload("softmax_m65536_n4096_bf16", 65536, 4096,
+                                                 torch.bfloat16, 8),
+}
+
+
+def make_softmax_inputs(M: int, N: int, dtype: torch.dtype = torch.bfloat16, seed: int = 0,
+                        std: float = 1.0, mask: str = "none"):
+    """CPU tensor [M, N]: a seeded CPU generator draws float32 N(0, std^2),
+    then rounds to ``dtype``.  mask="causal" sets entry (r, j) to -inf for
+    j > r mod N, the score rows of a causal head (row r = query r mod N)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    x = torch.randn((M, N), generator=g, dtype=torch.float32)
+    if std != 1.0:
+        x = x * std
+    if mask == "causal":
+        r = torch.arange(M).unsqueeze(1) % N
+        j = torch.arange(N).unsqueeze(0)
+        x = x.masked_fill(j > r, float("-inf"))
+    elif mask != "none":
+        raise ValueError(mask)
+    return x.to(dtype)
+
+
+def softmax_workload_inputs(w: SoftmaxWorkload):
+    return make_softmax_inputs(w.M, w.N, w.dtype, w.seed, w.std)

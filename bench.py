@@ -10,7 +10,10 @@ GPU, and resident in HBM before the timed region starts.
 With `--workload` naming a key/value-cache shape (attn_inputs.KV_WORKLOADS,
 e.g. decode_b8_h32_nq1_nk8192_d128) a step is instead one attn_fwd_kv call
 (per-chunk partial kernel + merge kernel) and `value` is the K/V bytes read
-per second, the quantity that bounds decode.
+per second, the quantity that bounds decode.  With a row-softmax shape
+(attn_inputs.SOFTMAX_WORKLOADS, softmax_m65536_n4096_bf16) a step is one
+attn_softmax_rows call and `value` is the bytes it must move (one read and
+one write of every element) per second.
 
 Prints ONE JSON line.  `value` is fwd+bwd TFLOP/s by the formula
 4*B*H*N^2*d (halved for causal) for the forward plus 2.5x that for the
@@ -33,10 +36,11 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-KERNELS = ("fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq")
+KERNELS = ("fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "softmax_rows")
 CSRC = os.path.join(ROOT, "tiled_online_softmax_attn_amd", "csrc")
 KERNEL_SOURCES = {"fwd": "attn_fwd.hip", "bwd_preprocess": "attn_bwd.hip",
-                  "bwd_dkdv": "attn_bwd.hip", "bwd_dq": "attn_bwd.hip"}
+                  "bwd_dkdv": "attn_bwd.hip", "bwd_dq": "attn_bwd.hip",
+                  "softmax_rows": "softmax_rows.hip"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -123,6 +127,8 @@ def kernel_key(name: str):
         return "bwd_dkdv"
     if "bwd_dq_kernel" in name:
         return "bwd_dq"
+    if "softmax_rows" in name:
+        return "softmax_rows"
     if "MulFunctor" in name:  # the --copy-mib reference kernel (x * 1)
         return "copy"
     return None
@@ -149,11 +155,15 @@ def pmc_summary(dirs, copy_mib: float, workload: str) -> int:
     known_kib = copy_mib * 1024.0
     fetch_cal = known_kib / avg[("copy", "FETCH_SIZE")]
     write_cal = known_kib / avg[("copy", "WRITE_SIZE")]
-    out = {"calibration": {"copy_mib": copy_mib,
+    try:  # other workloads' entries are kept
+        with open(TRAFFIC_FILE) as fh:
+            out = json.load(fh)
+    except (OSError, ValueError):
+        out = {}
+    per = {"calibration": {"copy_mib": copy_mib,
                            "copy_fetch_kib": avg[("copy", "FETCH_SIZE")],
                            "copy_write_kib": avg[("copy", "WRITE_SIZE")],
                            "fetch_factor": fetch_cal, "write_factor": write_cal}}
-    per = {}
     for kn in KERNELS:
         if (kn, "FETCH_SIZE") not in avg or (kn, "WRITE_SIZE") not in avg:
             continue
@@ -258,6 +268,92 @@ def bench_kv(args, w):
     print(json.dumps(out), flush=True)
 
 
+def copy_reference(copy_mib: float) -> None:
+    """One plain device copy of copy_mib MiB (x * 1), the known-size kernel
+    that calibrates the HBM byte counters."""
+    if copy_mib <= 0:
+        return
+    import torch
+    n = int(copy_mib * 1024 * 1024 // 4)
+    src = torch.ones(n, device="cuda:0", dtype=torch.float32)
+    dst = torch.empty_like(src)
+    torch.mul(src, 1.0, out=dst)  # reads and writes copy_mib MiB
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def cpu_baseline_softmax(w, x, budget_s: float):
+    """The oracle's row softmax, row by row, for about budget_s seconds; rate
+    in bytes (one read + one write of each element) per second."""
+    import oracle
+    lib = oracle.load()
+    rows, t0 = 0, time.perf_counter()
+    while rows < w.M and time.perf_counter() - t0 < budget_s:
+        oracle.softmax_row(x[rows].double().numpy(), lib=lib)
+        rows += 1
+    el = time.perf_counter() - t0
+    eprint(f"[cpu_baseline] oracle: {rows} rows in {el:.1f} s")
+    return {"value": w.hbm_bytes() / w.M * rows / el / 1e9, "unit": "GB/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"{rows} of {w.M} rows of {w.name} (fp64 safe softmax per row), "
+                      f"{el:.1f} s"}
+
+
+def bench_softmax(args, w):
+    """One step = attn_softmax_rows over the whole M x N matrix."""
+    import torch
+
+    import tiled_online_softmax_attn_amd as T
+    from attn_inputs import softmax_workload_inputs
+
+    T.lib()
+    dev = torch.device("cuda:0")
+    eprint(f"[bench] generating inputs for {w.name}")
+    x = softmax_workload_inputs(w)
+    xd = x.to(dev)
+    y = torch.empty_like(xd)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        T.attn_softmax_rows(xd, y, stream)
+
+    copy_reference(args.copy_mib)
+
+    eprint(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    eprint(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / args.steps
+    value = w.hbm_bytes() * args.steps / wall / 1e9
+    achieved = w.hbm_bytes() / (call_ms * 1e-3) / 1e9
+    tr = measured_traffic("softmax_rows", w.name)
+    roofline = {"kernel": "softmax_rows", "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": None if tr is None else round(tr), "algorithmic_bytes": w.hbm_bytes(),
+                "avg_launch_us": round(call_ms * 1e3, 2)}
+    cpu = None if args.no_cpu_baseline else cpu_baseline_softmax(w, x, args.cpu_baseline_seconds)
+    out = {
+        "metric": f"fused row softmax, HBM bytes (one read + one write) per second, {w.name}",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 scores)",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "step": "attn_softmax_rows"},
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -286,13 +382,16 @@ def main():
     import torch
 
     import tiled_online_softmax_attn_amd as T
-    from attn_inputs import HEADLINE, KV_WORKLOADS, WORKLOADS, workload_inputs
+    from attn_inputs import HEADLINE, KV_WORKLOADS, SOFTMAX_WORKLOADS, WORKLOADS, workload_inputs
 
     if not torch.cuda.is_available():
         eprint("bench.py needs a GPU")
         sys.exit(1)
     if args.workload in KV_WORKLOADS:
         bench_kv(args, KV_WORKLOADS[args.workload])
+        return
+    if args.workload in SOFTMAX_WORKLOADS:
+        bench_softmax(args, SOFTMAX_WORKLOADS[args.workload])
         return
     w = WORKLOADS[args.workload or HEADLINE]
     T.lib()
@@ -319,13 +418,7 @@ def main():
             if events is not None:
                 events[2 + ph].record(stream)
 
-    if args.copy_mib > 0:
-        n = int(args.copy_mib * 1024 * 1024 // 4)
-        src = torch.ones(n, device=dev, dtype=torch.float32)
-        dst = torch.empty_like(src)
-        torch.mul(src, 1.0, out=dst)  # reads and writes copy_mib MiB
-        torch.cuda.synchronize()
-        del src, dst
+    copy_reference(args.copy_mib)
 
     eprint(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):

@@ -147,11 +147,24 @@ int attn_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse
                 int B, int H, int Nq, int Nk, int d, int causal, float scale, int dtype,
                 int num_splits, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Row-wise softmax of an M x N row-major matrix x (PDC notes Lecture 5,
+ * section 5.20, fused softmax; CS149 L9 notes section 8):
+ *   y_ij = e^{x_ij - max_j x_ij} / sum_j e^{x_ij - max_j x_ij}.
+ *   x, y   : device pointers to M*N elements of `dtype` (fp32 or bf16), rows
+ *            contiguous; y may equal x (in place), otherwise they must not
+ *            overlap.  Entries equal to -inf get probability 0; a row needs at
+ *            least one finite entry.
+ * Each row is read from HBM once and written once (twice read for rows of
+ * more than 16384 elements).  Returns ATTN_OK, ATTN_ERR_NULL, ATTN_ERR_SHAPE
+ * (M or N < 1, or M above 2^40), ATTN_ERR_DTYPE, ATTN_ERR_ALIGN
+ * (x or y not 16-byte aligned) or ATTN_ERR_HIP. */
+int attn_softmax_rows(const void* x, void* y, long long M, int N, int dtype, void* stream);
+
 /* Static, human-readable text for a return code (never NULL). */
 const char* attn_status_str(int status);
 
 /* Library ABI version; bumped when an entry point is added or a signature
- * changes (2: attn_fwd_kv and attn_fwd_kv_workspace_bytes). */
+ * changes (2: attn_fwd_kv and attn_fwd_kv_workspace_bytes; 3: attn_softmax_rows). */
 int attn_abi_version(void);
 
 #ifdef __cplusplus

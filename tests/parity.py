@@ -121,3 +121,23 @@ def gpu_forward_kv(q, k, v, causal, scale, num_splits=0):
     T.attn_fwd_kv(qd, kd, vd, o, lse, causal, scale, num_splits, ws)
     torch.cuda.synchronize()
     return o.cpu(), lse.cpu()
+
+
+def gpu_softmax(x, inplace=False):
+    """x [M, N] CPU tensor; runs attn_softmax_rows on the GPU (into a
+    NaN-poisoned output, or in place); returns the CPU result."""
+    xd = x.to(torch.device("cuda:0"))
+    if inplace:
+        y = xd
+    else:
+        y = torch.full_like(xd, float("nan"))
+    T.attn_softmax_rows(xd, y)
+    torch.cuda.synchronize()
+    return y.cpu()
+
+
+def oracle_softmax_rows(x: np.ndarray, rows=None) -> np.ndarray:
+    """fp64 oracle softmax of the given rows of x [M, N] (all by default)."""
+    rows = range(x.shape[0]) if rows is None else rows
+    return np.stack([oracle.softmax_row(np.ascontiguousarray(x[r], dtype=np.float64))[0]
+                     for r in rows])

@@ -28,8 +28,8 @@ def _lib():
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted(["attn_fwd", "attn_bwd", "attn_bwd_phase",
                                            "attn_bwd_workspace_bytes", "attn_fwd_kv",
-                                           "attn_fwd_kv_workspace_bytes", "attn_status_str",
-                                           "attn_abi_version"])
+                                           "attn_fwd_kv_workspace_bytes", "attn_softmax_rows",
+                                           "attn_status_str", "attn_abi_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = _lib()
-    assert lib.attn_abi_version() == 2
+    assert lib.attn_abi_version() == 3
     for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, 12345]:
         s = lib.attn_status_str(code)
         assert isinstance(s, bytes) and len(s) > 0
@@ -149,3 +149,15 @@ def test_kv_validation(args, code):
                          a["H"], a["Nq"], a["Nk"], a["d"], a["causal"], a["scale"], a["dtype"],
                          a["splits"], a["ws"] or None, a["ws_bytes"], None)
     assert rc == code
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(x=0), -1), (dict(y=0), -1), (dict(M=0), -2), (dict(N=0), -2), (dict(M=(1 << 40) + 1), -2),
+    (dict(dtype=2), -3), (dict(x=FAKE + 4), -5), (dict(y=FAKE + 2), -5),
+])
+def test_softmax_rows_validation(args, code):
+    lib = _lib()
+    a = dict(x=FAKE, y=FAKE, M=4, N=100, dtype=1)
+    a.update(args)
+    assert lib.attn_softmax_rows(a["x"] or None, a["y"] or None, a["M"], a["N"], a["dtype"],
+                                 None) == code

@@ -28,7 +28,8 @@ STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR
           -4: "ATTN_ERR_HEADDIM", -5: "ATTN_ERR_ALIGN", -6: "ATTN_ERR_SCALE",
           -7: "ATTN_ERR_WORKSPACE", -8: "ATTN_ERR_HIP"}
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_phase", "attn_bwd_workspace_bytes",
-           "attn_fwd_kv", "attn_fwd_kv_workspace_bytes", "attn_status_str", "attn_abi_version")
+           "attn_fwd_kv", "attn_fwd_kv_workspace_bytes", "attn_softmax_rows", "attn_status_str",
+           "attn_abi_version")
 
 
 class AttnLibraryMissing(RuntimeError):
@@ -68,6 +69,8 @@ def lib() -> ctypes.CDLL:
                                   ctypes.c_size_t, vp]
         L.attn_fwd_kv_workspace_bytes.restype = ctypes.c_size_t
         L.attn_fwd_kv_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+        L.attn_softmax_rows.restype = i
+        L.attn_softmax_rows.argtypes = [vp, vp, ctypes.c_longlong, i, i, vp]
         L.attn_status_str.restype = ctypes.c_char_p
         L.attn_status_str.argtypes = [i]
         L.attn_abi_version.restype = i
@@ -179,6 +182,19 @@ def attn_fwd_kv(q, k, v, o, lse, causal: bool, scale: float, num_splits: int, wo
                            _ptr(workspace), ws_bytes, _stream_handle(stream))
     if rc != 0:
         raise AttnError(rc, "attn_fwd_kv")
+
+
+def attn_softmax_rows(x, y, stream=None) -> None:
+    """Enqueue y = row-wise softmax of x (both contiguous, same shape and
+    dtype, fp32 or bf16; the last dimension is the row; y may be x)."""
+    _check_contig(x, y)
+    if x.shape != y.shape or x.dtype != y.dtype:
+        raise ValueError("x and y must have the same shape and dtype")
+    N = int(x.shape[-1]) if x.dim() > 0 else 1
+    M = x.numel() // max(N, 1)
+    rc = lib().attn_softmax_rows(_ptr(x), _ptr(y), M, N, _dtype_code(x), _stream_handle(stream))
+    if rc != 0:
+        raise AttnError(rc, "attn_softmax_rows")
 
 
 # ------------------------------------------------------------ conveniences

@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -152,6 +152,16 @@ int attn_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse
   attn::FwdKvArgs a{q, k, v, o, lse, B, H, Nq, Nk, d, causal != 0, scale, num_splits,
                     workspace, stream};
   return attn::launch_fwd_kv(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_softmax_rows(const void* x, void* y, long long M, int N, int dtype, void* stream) {
+  if (!x || !y) return ATTN_ERR_NULL;
+  if (M < 1 || N < 1) return ATTN_ERR_SHAPE;
+  if (M > (1LL << 40)) return ATTN_ERR_SHAPE;  // M * N elements must stay addressable
+  if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
+  if (!aligned16(x) || !aligned16(y)) return ATTN_ERR_ALIGN;
+  attn::SoftmaxArgs a{x, y, (int64_t)M, N, dtype == ATTN_DTYPE_BF16, stream};
+  return attn::launch_softmax_rows(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 }  // extern "C"

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace attn {
 
@@ -63,6 +64,17 @@ struct KvSplit {
   size_t lse_part_bytes;  // fp32 [splits][B*H][Nq], rounded up to 256
 };
 KvSplit kv_split_plan(int B, int H, int Nq, int Nk, int d, int num_splits);
+
+// Row-wise softmax of an M x N row-major matrix (attn_softmax_rows).
+struct SoftmaxArgs {
+  const void* x;
+  void* y;
+  int64_t M;
+  int N;
+  bool bf16;
+  void* stream;
+};
+hipError_t launch_softmax_rows(const SoftmaxArgs& a);
 
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_fwd_kv(const FwdKvArgs& a);

@@ -1,0 +1,194 @@
+// softmax_rows.hip - standalone fused row softmax for gfx950 (fp32 or bf16).
+//
+// y_ij = e^{x_ij - m_i} / l_i with m_i = max_j x_ij and l_i = sum_j e^{x_ij - m_i}
+// (CS149 Lecture 9 notes "Efficiently Evaluating DNNs on GPUs", section 8).
+// Fused as PDC notes Lecture 5, section 5.20 describes: each row is read from
+// HBM once, kept on chip (in registers) while the maximum, the exponentials
+// and their sum are formed with tree reductions, and written once.  Adjacent
+// threads load adjacent 16-byte pieces of the row (continuous addressing) and
+// every thread holds several of them (algorithm cascading).  Rows longer than
+// the registers of one workgroup take two passes: the first keeps a running
+// (m, l) per thread and merges them with the blocked-softmax identity (CS149
+// L9 notes section 9), the second writes the result.  Exponentials are
+// v_exp_f32 in base 2 with log2(e) folded into one FMA.
+#include <algorithm>
+
+#include "device_common.h"
+#include "attn_launch.h"
+
+namespace attn {
+namespace {
+
+template <typename T> struct Vec;  // one 16-byte piece of a row
+template <> struct Vec<float> {
+  static constexpr int kN = 4;
+  typedef float type __attribute__((ext_vector_type(4)));
+};
+template <> struct Vec<__bf16> {
+  static constexpr int kN = 8;
+  typedef __bf16 type __attribute__((ext_vector_type(8)));
+};
+
+// Reductions over the TPR threads of one row (a wave, or the whole
+// workgroup through LDS).
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+template <int TPR, bool MAX>
+__device__ __forceinline__ float row_reduce(float x, float* red) {
+  x = MAX ? wave_max(x) : wave_sum(x);
+  if constexpr (TPR > 64) {
+    const int wave = threadIdx.x >> 6;
+    constexpr int NW = TPR / 64;
+    __syncthreads();  // red[] is free (earlier readers are done)
+    if ((threadIdx.x & 63) == 0) red[wave] = x;
+    __syncthreads();
+    x = red[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) x = MAX ? fmaxf(x, red[w]) : x + red[w];
+  }
+  return x;
+}
+
+// One row per TPR threads (TPR = 64: a wave, 4 rows per workgroup; TPR =
+// 256: the workgroup); each thread holds P pieces of 16 bytes.  VECROWS: the
+// row length is a multiple of the piece, so rows are 16-byte aligned and read
+// with 16-byte loads; otherwise element by element.
+template <typename T, int TPR, int P, bool VECROWS>
+__global__ void __launch_bounds__(256)
+softmax_rows_kernel(const T* x, T* y, int64_t M, int N) {
+  constexpr int V = Vec<T>::kN;
+  constexpr int RPG = 256 / TPR;  // rows per workgroup
+  typedef typename Vec<T>::type VT;
+  __shared__ float red[4];
+  const int t = threadIdx.x % TPR;
+  // grid-stride over groups of RPG rows (the grid is capped at kMaxGroups)
+  for (int64_t g = blockIdx.x; g * RPG < M; g += gridDim.x) {
+    const int64_t row = g * RPG + threadIdx.x / TPR;
+    const bool live = row < M;  // uniform per row
+    const T* xr = x + (live ? row : 0) * (int64_t)N;
+    T* yr = y + (live ? row : 0) * (int64_t)N;
+    float v[P][V];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int c0 = (p * TPR + t) * V;
+      if (VECROWS && c0 + V <= N) {
+        const VT w = *reinterpret_cast<const VT*>(xr + c0);
+#pragma unroll
+        for (int e = 0; e < V; ++e) v[p][e] = (float)w[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < V; ++e) v[p][e] = c0 + e < N ? (float)xr[c0 + e] : -INFINITY;
+      }
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int e = 0; e < V; ++e) m = fmaxf(m, v[p][e]);
+    m = row_reduce<TPR, true>(m, red);
+    const float mo = m * kLog2e;
+    float l = 0.f;
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        v[p][e] = fast_exp2(fmaf(v[p][e], kLog2e, -mo));
+        l += v[p][e];
+      }
+    l = row_reduce<TPR, false>(l, red);
+    const float inv = 1.f / l;
+    if (live) {
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const int c0 = (p * TPR + t) * V;
+        if (VECROWS && c0 + V <= N) {
+          VT w;
+#pragma unroll
+          for (int e = 0; e < V; ++e) w[e] = (T)(v[p][e] * inv);
+          *reinterpret_cast<VT*>(yr + c0) = w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < V; ++e)
+            if (c0 + e < N) yr[c0 + e] = (T)(v[p][e] * inv);
+        }
+      }
+    }
+  }
+}
+
+// Rows too long for the registers: one workgroup per row, two passes.
+template <typename T>
+__global__ void __launch_bounds__(256)
+softmax_rows_long_kernel(const T* x, T* y, int64_t M, int N) {
+  __shared__ float red[4];
+  for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
+    const T* xr = x + row * (int64_t)N;
+    T* yr = y + row * (int64_t)N;
+    // pass 1: running maximum and sum of this thread's elements (log2 units)
+    float m = -INFINITY, l = 0.f;
+    for (int c = threadIdx.x; c < N; c += 256) {
+      const float s = (float)xr[c] * kLog2e;
+      if (s == -INFINITY) continue;  // weight 0
+      if (s > m) {
+        l = l * fast_exp2(m - s) + 1.f;
+        m = s;
+      } else {
+        l += fast_exp2(s - m);
+      }
+    }
+    // merge the threads' (m, l): m = max m_t, l = sum_t e^{m_t - m} l_t
+    const float mr = row_reduce<256, true>(m, red);
+    const float lr = row_reduce<256, false>(m == -INFINITY ? 0.f : l * fast_exp2(m - mr), red);
+    const float inv = 1.f / lr;
+    // pass 2
+    for (int c = threadIdx.x; c < N; c += 256)
+      yr[c] = (T)(fast_exp2(fmaf((float)xr[c], kLog2e, -mr)) * inv);
+  }
+}
+
+// Workgroups per launch at most; larger inputs are covered by grid striding
+// (keeps the work-item count of a dispatch well inside 32 bits).  A long row
+// is at least 32 KB of work per workgroup, so 8192 of them (four per slot of
+// a full chip) already balance.
+constexpr int64_t kMaxGroups = 1 << 20;
+constexpr int64_t kMaxLongGroups = 8192;
+
+template <typename T, int TPR, int P>
+hipError_t launch_rows(const SoftmaxArgs& a) {
+  constexpr int V = Vec<T>::kN;
+  const int64_t groups = std::min<int64_t>((a.M + (256 / TPR) - 1) / (256 / TPR), kMaxGroups);
+  const bool vec = a.N % V == 0;
+  auto kern = vec ? softmax_rows_kernel<T, TPR, P, true> : softmax_rows_kernel<T, TPR, P, false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)groups), dim3(256), 0, (hipStream_t)a.stream,
+                     (const T*)a.x, (T*)a.y, a.M, a.N);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_softmax_t(const SoftmaxArgs& a) {
+  constexpr int V = Vec<T>::kN;
+  const int pieces = (a.N + V - 1) / V;  // 16-byte pieces per row
+  if (pieces <= 64 * 4) return launch_rows<T, 64, 4>(a);
+  if (pieces <= 256 * 2) return launch_rows<T, 256, 2>(a);
+  if (pieces <= 256 * 4) return launch_rows<T, 256, 4>(a);
+  if (pieces <= 256 * (32 / V) * 2) return launch_rows<T, 256, 64 / V>(a);
+  hipLaunchKernelGGL(softmax_rows_long_kernel<T>, dim3((unsigned)std::min(a.M, kMaxLongGroups)), dim3(256), 0,
+                     (hipStream_t)a.stream, (const T*)a.x, (T*)a.y, a.M, a.N);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_softmax_rows(const SoftmaxArgs& a) {
+  return a.bf16 ? launch_softmax_t<__bf16>(a) : launch_softmax_t<float>(a);
+}
+
+}  // namespace attn
