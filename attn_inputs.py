@@ -60,6 +60,15 @@ WORKLOADS = {
 
 HEADLINE = "b4_h16_n4096_d128_causal"
 
+# The headline shape at the other head dimensions the kernels take (forward
+# and backward); the pages fix no workload for them.
+HEADDIM_WORKLOADS = {
+    "b4_h16_n4096_d96_causal": Workload("b4_h16_n4096_d96_causal", 4, 16, 4096, 96,
+                                        torch.bfloat16, True, 9, backward=True),
+    "b4_h16_n4096_d32_causal": Workload("b4_h16_n4096_d32_causal", 4, 16, 4096, 32,
+                                        torch.bfloat16, True, 10, backward=True),
+}
+
 
 def make_inputs(B: int, H: int, N: int, d: int, dtype: torch.dtype = torch.bfloat16,
                 seed: int = 0, qk_std: float = 1.0, with_dout: bool = False):

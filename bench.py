@@ -36,7 +36,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-KERNELS = ("fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "softmax_rows")
+KERNELS = ("fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq")  # one step, in launch order
+COUNTED_KERNELS = KERNELS + ("softmax_rows",)  # kernels the HBM byte counters cover
 CSRC = os.path.join(ROOT, "tiled_online_softmax_attn_amd", "csrc")
 KERNEL_SOURCES = {"fwd": "attn_fwd.hip", "bwd_preprocess": "attn_bwd.hip",
                   "bwd_dkdv": "attn_bwd.hip", "bwd_dq": "attn_bwd.hip",
@@ -164,7 +165,7 @@ def pmc_summary(dirs, copy_mib: float, workload: str) -> int:
                            "copy_fetch_kib": avg[("copy", "FETCH_SIZE")],
                            "copy_write_kib": avg[("copy", "WRITE_SIZE")],
                            "fetch_factor": fetch_cal, "write_factor": write_cal}}
-    for kn in KERNELS:
+    for kn in COUNTED_KERNELS:
         if (kn, "FETCH_SIZE") not in avg or (kn, "WRITE_SIZE") not in avg:
             continue
         per[kn] = {"fetch_bytes": avg[(kn, "FETCH_SIZE")] * 1024 * fetch_cal,
@@ -382,7 +383,8 @@ def main():
     import torch
 
     import tiled_online_softmax_attn_amd as T
-    from attn_inputs import HEADLINE, KV_WORKLOADS, SOFTMAX_WORKLOADS, WORKLOADS, workload_inputs
+    from attn_inputs import (HEADDIM_WORKLOADS, HEADLINE, KV_WORKLOADS, SOFTMAX_WORKLOADS,
+                             WORKLOADS, workload_inputs)
 
     if not torch.cuda.is_available():
         eprint("bench.py needs a GPU")
@@ -393,7 +395,7 @@ def main():
     if args.workload in SOFTMAX_WORKLOADS:
         bench_softmax(args, SOFTMAX_WORKLOADS[args.workload])
         return
-    w = WORKLOADS[args.workload or HEADLINE]
+    w = {**WORKLOADS, **HEADDIM_WORKLOADS}[args.workload or HEADLINE]
     T.lib()
     dev = torch.device("cuda:0")
     eprint(f"[bench] generating inputs for {w.name}")

@@ -55,7 +55,8 @@ def test_workspace_size():
     need = B * H * N * 4
     assert need <= n <= need + 256
     assert lib.attn_bwd_workspace_bytes(0, 1, 1, 64, 1) == 0
-    assert lib.attn_bwd_workspace_bytes(1, 1, 1, 96, 1) == 0
+    assert lib.attn_bwd_workspace_bytes(1, 1, 1, 80, 1) == 0
+    assert lib.attn_bwd_workspace_bytes(1, 1, 1, 256, 1) == 0
     assert lib.attn_bwd_workspace_bytes(1, 1, 1, 64, 0) == 0  # fp32 backward unsupported
 
 
@@ -66,7 +67,7 @@ FAKE = 1 << 20  # a 16-byte aligned non-null address, never dereferenced on erro
 @pytest.mark.parametrize("args,code", [
     (dict(q=0), -1), (dict(lse=0), -1),
     (dict(B=0), -2), (dict(H=-1), -2), (dict(N=0), -2),
-    (dict(d=96), -4), (dict(d=32), -4),
+    (dict(d=80), -4), (dict(d=16), -4), (dict(d=256), -4), (dict(d=0), -4),
     (dict(dtype=7), -3),
     (dict(q=FAKE + 8), -5), (dict(o=FAKE + 2), -5),
     (dict(scale=float("inf")), -6), (dict(scale=float("nan")), -6),
@@ -127,7 +128,7 @@ def test_kv_workspace_size():
         r256 = lambda x: (x + 255) // 256 * 256
         assert n == r256(rows * d * 4) + r256(rows * 4)
     assert lib.attn_fwd_kv_workspace_bytes(1, 1, 0, 10, 64, 0, 1) == 0
-    assert lib.attn_fwd_kv_workspace_bytes(1, 1, 4, 10, 96, 0, 1) == 0
+    assert lib.attn_fwd_kv_workspace_bytes(1, 1, 4, 10, 80, 0, 1) == 0
     assert lib.attn_fwd_kv_workspace_bytes(1, 1, 4, 10, 64, -1, 1) == 0
     assert lib.attn_fwd_kv_workspace_bytes(1, 1, 4, 10, 64, 0, 0) == 0  # fp32 unsupported
 
@@ -136,7 +137,7 @@ def test_kv_workspace_size():
     (dict(q=0), -1), (dict(lse=0), -1),
     (dict(B=0), -2), (dict(Nq=0), -2), (dict(Nk=0), -2), (dict(splits=-1), -2),
     (dict(Nq=20, Nk=10, causal=1), -2),
-    (dict(d=96), -4), (dict(dtype=0), -3), (dict(dtype=5), -3),
+    (dict(d=48), -4), (dict(dtype=0), -3), (dict(dtype=5), -3),
     (dict(k=FAKE + 4), -5), (dict(scale=float("nan")), -6),
     (dict(ws=0), -7), (dict(ws_bytes=8), -7), (dict(ws=FAKE + 8), -5),
 ])

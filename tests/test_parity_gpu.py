@@ -4,9 +4,9 @@ same seeded inputs.  Every test here needs an MI355X and the built library.
 Coverage:
 * the five workloads at their real shapes (full oracle where it finishes in
   seconds, sampled query rows at the large shapes; the backward workload on
-  two full heads);
-* ragged N (tails that span several tiles), N = 1, both masks, d = 64 / 128,
-  fp32 and bf16;
+  two full heads), and the B4 H16 N4096 causal shape at d = 96 and 32;
+* ragged N (tails that span several tiles), N = 1, both masks,
+  d = 32 / 64 / 96 / 128, fp32 and bf16;
 * closed forms with exactly representable inputs (Q = 0);
 * the dV / dK sum invariants of the backward at full size;
 * determinism of the forward.
@@ -16,7 +16,7 @@ import pytest
 import torch
 
 import oracle
-from attn_inputs import WORKLOADS, make_inputs, workload_inputs
+from attn_inputs import HEADDIM_WORKLOADS, WORKLOADS, make_inputs, workload_inputs
 from tests.parity import (compare, describe, f32_scale, gpu_backward, gpu_forward, log,
                           oracle_full_fwd, oracle_rows_fwd, sample_rows, to_np)
 
@@ -56,7 +56,7 @@ def test_h8_n1024_workloads(name):
 
 
 @pytest.mark.parametrize("N", [1, 17, 100, 255, 257, 1000])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_ragged_forward(N, d, causal, dtype):
@@ -65,7 +65,7 @@ def test_ragged_forward(N, d, causal, dtype):
 
 
 @pytest.mark.parametrize("N", [1, 17, 100, 257, 1000])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_ragged_backward(N, d, causal):
     q, k, v, do = make_inputs(1, 2, N, d, torch.bfloat16, seed=200 + N + d, with_dout=True)
@@ -107,9 +107,11 @@ def test_forward_is_deterministic():
     ("b4_h16_n4096_d128_causal", [(0, 0), (1, 7), (3, 15)]),
     ("h32_n16384_d128_causal_bigqk", [(0, 0), (0, 13), (0, 31)]),
     ("b2_h16_n4096_d64_causal_fwdbwd", [(0, 0), (1, 15)]),
+    ("b4_h16_n4096_d96_causal", [(0, 0), (3, 15)]),
+    ("b4_h16_n4096_d32_causal", [(0, 0), (2, 9)]),
 ])
 def test_full_size_forward_sampled_rows(name, heads):
-    w = WORKLOADS[name]
+    w = {**WORKLOADS, **HEADDIM_WORKLOADS}[name]
     log(f"[fwd] {name}: generating inputs")
     q, k, v = workload_inputs(w, with_dout=False)
     o, lse = gpu_forward(q, k, v, w.causal, w.scale)
@@ -122,8 +124,13 @@ def test_full_size_forward_sampled_rows(name, heads):
         log(f"    b{b} h{h} rows={len(rows)} O {describe(eo)} | lse {describe(el)}")
 
 
-def test_fwdbwd_workload_backward():
-    w = WORKLOADS["b2_h16_n4096_d64_causal_fwdbwd"]
+@pytest.mark.parametrize("name,heads", [
+    ("b2_h16_n4096_d64_causal_fwdbwd", [(0, 0), (1, 11)]),
+    ("b4_h16_n4096_d96_causal", [(2, 5)]),
+    ("b4_h16_n4096_d32_causal", [(1, 3)]),
+])
+def test_fwdbwd_workload_backward(name, heads):
+    w = {**WORKLOADS, **HEADDIM_WORKLOADS}[name]
     log(f"[bwd] {w.name}: generating inputs")
     q, k, v, do = workload_inputs(w)
     o, lse = gpu_forward(q, k, v, w.causal, w.scale)
@@ -133,11 +140,11 @@ def test_fwdbwd_workload_backward():
     # invariants on every head: sum_j dV_j = sum_i dO_i, sum_j dK_j = 0
     sdv = dv.double().sum(2)
     sdo = do.double().sum(2)
-    assert torch.allclose(sdv, sdo, atol=2e-2 * 4096 ** 0.5, rtol=1e-2)
+    assert torch.allclose(sdv, sdo, atol=2e-2 * w.N ** 0.5, rtol=1e-2)
     sdk = dk.double().sum(2)
-    assert (sdk.abs() <= 2e-2 * 4096 ** 0.5 + 1e-2 * dk.double().abs().sum(2)).all()
-    # element-by-element against the oracle on two whole heads
-    for b, h in [(0, 0), (1, 11)]:
+    assert (sdk.abs() <= 2e-2 * w.N ** 0.5 + 1e-2 * dk.double().abs().sum(2)).all()
+    # element-by-element against the oracle on whole heads
+    for b, h in heads:
         log(f"    oracle backward b{b} h{h}")
         ref = oracle.attn_bwd(to_np(q[b, h]), to_np(k[b, h]), to_np(v[b, h]), to_np(do[b, h]),
                               True, f32_scale(w.scale))

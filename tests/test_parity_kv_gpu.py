@@ -41,7 +41,7 @@ def _check(q, k, v, causal, splits, tag):
 
 
 @pytest.mark.parametrize("Nk", [1, 63, 64, 65, 1000, 4097])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_decode_shapes(Nk, d, causal):
     q, k, v = make_kv_inputs(2, 3, 1, Nk, d, seed=100 + Nk + d)
@@ -50,7 +50,7 @@ def test_decode_shapes(Nk, d, causal):
 
 @pytest.mark.parametrize("Nq,Nk", [(7, 100), (64, 64), (128, 1000), (200, 333), (130, 2049),
                                    (300, 300)])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_prefill_shapes(Nq, Nk, d, causal):
     q, k, v = make_kv_inputs(1, 2, Nq, Nk, d, seed=200 + Nq + Nk + d)

@@ -17,7 +17,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // int64 offsets and the workgroup count in a 32-bit grid.
 int check_shape(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
-  if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
+  if (!attn::head_dim_supported(d)) return ATTN_ERR_HEADDIM;
   const int64_t bh = (int64_t)B * (int64_t)H;
   if (bh > (int64_t)1 << 31) return ATTN_ERR_SHAPE;
   const int64_t tiles = bh * (((int64_t)N + 63) / 64);
@@ -45,7 +45,7 @@ const char* attn_status_str(int status) {
     case ATTN_ERR_NULL: return "a required pointer is NULL";
     case ATTN_ERR_SHAPE: return "B, H and N must be >= 1 and the sizes must fit 64-bit offsets";
     case ATTN_ERR_DTYPE: return "dtype not supported by this entry point";
-    case ATTN_ERR_HEADDIM: return "head dimension d must be 64 or 128";
+    case ATTN_ERR_HEADDIM: return "head dimension d must be 32, 64, 96 or 128";
     case ATTN_ERR_ALIGN: return "pointers must be 16-byte aligned";
     case ATTN_ERR_SCALE: return "scale must be finite";
     case ATTN_ERR_WORKSPACE:

@@ -44,22 +44,23 @@ namespace {
 constexpr int kBwdThreads = 256;
 
 // ---------------------------------------------------------------- phase 0
-// D_i = sum_k dO_ik O_ik; 8 threads per row, each over d/8 consecutive columns.
+// D_i = sum_k dO_ik O_ik; 8 threads per row, thread `part` over the 8-column
+// chunks part, part + 8, ... of the row (adjacent threads, adjacent chunks).
 template <int D>
 __global__ void __launch_bounds__(256)
 bwd_preprocess_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ dout,
                       float* __restrict__ delta, int64_t rows) {
-  constexpr int PER = D / 8;
+  constexpr int CH = D / 8;  // chunks per row
   const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
   const int part = threadIdx.x & 7;
   float acc = 0.f;
   if (row < rows) {
-    const __bf16* orow = o + row * D + part * PER;
-    const __bf16* drow = dout + row * D + part * PER;
+    const __bf16* orow = o + row * D;
+    const __bf16* drow = dout + row * D;
 #pragma unroll
-    for (int c = 0; c < PER; c += 8) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(orow + c);
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(drow + c);
+    for (int c = part; c < CH; c += 8) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(orow + c * 8);
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(drow + c * 8);
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
     }
@@ -81,7 +82,7 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 const float* __restrict__ lse, const float* __restrict__ delta,
                 __bf16* __restrict__ dk, __bf16* __restrict__ dv, int BH, int N, float scale,
                 float scale_log2) {
-  using Tile = SwzTile<D>;
+  using Tile = SwzTile<tile_width(D), D>;
   static_assert(kKvBQ == Tile::kRows, "query tile is one SwzTile");
   constexpr int KS = D / 16;  // k-steps over d
   constexpr int DB = D / 32;  // 32-wide d blocks
@@ -378,11 +379,11 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
               const float* __restrict__ lse, const float* __restrict__ delta,
               __bf16* __restrict__ dq, int BH, int N, int n_qtiles, float scale,
               float scale_log2) {
-  using Tile = SwzTile<D>;
+  using Tile = SwzTile<tile_width(D), D>;
   static_assert(kDqBK == Tile::kRows, "key tile is one SwzTile");
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr bool kPipelineHalves = (D == 64);
+  constexpr bool kPipelineHalves = (D <= 64);
   constexpr int RB = Tile::kRowBytes;
   // K and V tiles of 64 keys (SwzTile layout), two buffers each; K is read
   // both by rows (S^T) and transposed (dQ^T).  One LDS object per buffer, so
@@ -650,7 +651,13 @@ hipError_t launch_phase(const BwdArgs& a, int phase) {
 }  // namespace
 
 hipError_t launch_bwd_phase(const BwdArgs& a, int phase) {
-  return a.d == 128 ? launch_phase<128>(a, phase) : launch_phase<64>(a, phase);
+  switch (a.d) {
+    case 32: return launch_phase<32>(a, phase);
+    case 64: return launch_phase<64>(a, phase);
+    case 96: return launch_phase<96>(a, phase);
+    case 128: return launch_phase<128>(a, phase);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_bwd(const BwdArgs& a) {

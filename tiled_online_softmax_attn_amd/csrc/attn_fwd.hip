@@ -49,21 +49,25 @@ __device__ __forceinline__ void fwd_tile_coords(int bid, int BH, int n_qtiles, b
   qt = causal ? (n_qtiles - 1 - rank) : rank;
 }
 
-template <int D, bool CAUSAL>
+// One code path serves both masks: query i sees keys j with j - i <= off,
+// off = 0 under the causal mask and off = N without it (every key visible).
+// A separate unmasked instantiation spilled registers at d = 96 and 128.
+template <int D>
 __global__ void __launch_bounds__(kFwdThreads, 2)
 attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      const __bf16* __restrict__ v, __bf16* __restrict__ o,
-                     float* __restrict__ lse, int BH, int N, int n_qtiles, float scale_log2) {
-  using Tile = SwzTile<D>;
+                     float* __restrict__ lse, int BH, int N, int n_qtiles, int off,
+                     float scale_log2) {
+  using Tile = SwzTile<tile_width(D), D>;
   static_assert(kFwdBK == Tile::kRows, "K/V tile is one SwzTile");
   constexpr int RB = Tile::kRowBytes;
   constexpr int KS = D / 16;  // k-steps of the S^T MFMA
   constexpr int DB = D / 32;  // 32-wide d blocks of O^T
   // d = 128: S^T of tile j+1 is computed during the softmax of tile j (the
-  // MFMA work per tile is large enough to hide the exponentials).  d = 64:
+  // MFMA work per tile is large enough to hide the exponentials).  Other d:
   // S^T of a tile is computed at the start of its own step, which keeps the
-  // register count low enough for more waves per SIMD.
-  constexpr bool kPipelineQK = (D == 128) && CAUSAL;
+  // register count low (d = 64: low enough for more waves per SIMD).
+  constexpr bool kPipelineQK = (D == 128);
   // K and V tiles of 64 keys (SwzTile layout), two buffers each.  One LDS
   // object per buffer: the compiler then knows that the copies into one
   // buffer cannot alias reads of another and does not wait for them.
@@ -88,7 +92,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int half = lane >> 5;
 
   int bh, qt;
-  fwd_tile_coords(blockIdx.x, BH, n_qtiles, CAUSAL, bh, qt);
+  fwd_tile_coords(blockIdx.x, BH, n_qtiles, true, bh, qt);
   const int64_t head = (int64_t)bh * N * D;
   const __bf16* qh = q + head;
   const __bf16* kh = k + head;
@@ -107,7 +111,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       qf[s] = (qry < N) ? *reinterpret_cast<const bf16x8*>(qrow + 16 * s) : zero;
   }
 
-  const int kv_end = CAUSAL ? min(N, (qt + 1) * kFwdBQ) : N;
+  const int kv_end = (int)min((int64_t)N, (int64_t)(qt + 1) * kFwdBQ + off);
   const int n_tiles = (kv_end + kFwdBK - 1) / kFwdBK;
 
   auto load_tile = [&](const __bf16* src, int j, ATTN_LDS unsigned char* dst) {
@@ -164,7 +168,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = key0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-          if (key >= N || (CAUSAL && key > qry)) sc[kb][i] = -INFINITY;
+          if (key >= N || key - qry > off) sc[kb][i] = -INFINITY;
         }
     }
 
@@ -195,8 +199,10 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     // one step earlier) and then the exponentials of 32 / KS scores.
     float psum = 0.f;
     bf16x8 pf[2][2];
+    // the 32 scores of the lane in kExpParts equal parts
+    constexpr int kExpParts = (32 % KS == 0) ? KS : 8;
     auto exp_part = [&](int part) {
-      constexpr int PER = 32 / KS;
+      constexpr int PER = 32 / kExpParts;
 #pragma unroll
       for (int u = 0; u < PER; ++u) {
         const int e = part * PER + u;
@@ -275,7 +281,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       }
     } else {
 #pragma unroll
-      for (int s = 0; s < KS; ++s) exp_part(s);
+      for (int part = 0; part < kExpParts; ++part) exp_part(part);
       l_run += psum;
       // O^T += V^T P^T; consecutive steps go to different accumulators, and
       // each step's V^T fragment is read one step ahead.
@@ -292,7 +298,8 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 
   // Last tile this wave computes: under the causal mask, later tiles lie
   // wholly in the future of all 32 of its queries (wave-uniform).
-  const int last_tile = CAUSAL ? min(n_tiles - 1, (q_wave0 + 31) / kFwdBK) : n_tiles - 1;
+  const int last_tile =
+      (int)min((int64_t)n_tiles - 1, ((int64_t)q_wave0 + 31 + off) / kFwdBK);
 
   // One iteration of the workgroup loop.  Buffers, pipelined: in iteration j
   // the K tile j+1 and the V tile j are read; the copies of K tile j+2 (into
@@ -311,7 +318,8 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     if (j + 1 < n_tiles) load_tile(vh, j + 1, v_lds(Other{}));
     if (j <= last_tile) {
       const int key0 = j * kFwdBK;
-      const bool need_mask = (key0 + kFwdBK > N) || (CAUSAL && key0 + kFwdBK - 1 > q_wave0);
+      const bool need_mask =
+          (key0 + kFwdBK > N) || ((int64_t)key0 + kFwdBK - 1 > (int64_t)q_wave0 + off);
       const bool next = j < last_tile;
       if (need_mask) {
         if (next) step(j, par_tag, sc, sn, std::true_type{}, std::true_type{});
@@ -453,14 +461,14 @@ attn_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D>
 hipError_t launch_bf16(const FwdArgs& a) {
   const int n_qtiles = (a.N + kFwdBQ - 1) / kFwdBQ;
   const int BH = a.B * a.H;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)(BH * n_qtiles)),
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D>), dim3((unsigned)(BH * n_qtiles)),
                      dim3(kFwdThreads), 0, (hipStream_t)a.stream, (const __bf16*)a.q,
                      (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse, BH, a.N,
-                     n_qtiles, a.scale * kLog2e);
+                     n_qtiles, a.causal ? 0 : a.N, a.scale * kLog2e);
   return hipGetLastError();
 }
 
@@ -475,16 +483,23 @@ hipError_t launch_f32(const FwdArgs& a) {
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_fwd_d(const FwdArgs& a) {
+  const bool c = a.causal != 0;
+  if (a.bf16) return launch_bf16<D>(a);
+  return c ? launch_f32<D, true>(a) : launch_f32<D, false>(a);
+}
+
 }  // namespace
 
 hipError_t launch_fwd(const FwdArgs& a) {
-  const bool c = a.causal != 0;
-  if (a.bf16) {
-    if (a.d == 128) return c ? launch_bf16<128, true>(a) : launch_bf16<128, false>(a);
-    return c ? launch_bf16<64, true>(a) : launch_bf16<64, false>(a);
+  switch (a.d) {
+    case 32: return launch_fwd_d<32>(a);
+    case 64: return launch_fwd_d<64>(a);
+    case 96: return launch_fwd_d<96>(a);
+    case 128: return launch_fwd_d<128>(a);
+    default: return hipErrorInvalidValue;
   }
-  if (a.d == 128) return c ? launch_f32<128, true>(a) : launch_f32<128, false>(a);
-  return c ? launch_f32<64, true>(a) : launch_f32<64, false>(a);
 }
 
 }  // namespace attn

@@ -42,7 +42,7 @@ attn_fwd_kv_partial_kernel(const __bf16* __restrict__ q, const __bf16* __restric
                            const __bf16* __restrict__ v, float* __restrict__ o_part,
                            float* __restrict__ lse_part, int BH, int Nq, int Nk, int off,
                            int n_qtiles, int chunk, float scale_log2) {
-  using Tile = SwzTile<D>;
+  using Tile = SwzTile<tile_width(D), D>;
   static_assert(kKvBK == Tile::kRows, "K/V tile is one SwzTile");
   constexpr int RB = Tile::kRowBytes;
   constexpr int KS = D / 16;  // k-steps of the S^T MFMA
@@ -232,7 +232,7 @@ __global__ void __launch_bounds__(256)
 attn_fwd_kv_merge_kernel(const float* __restrict__ o_part, const float* __restrict__ lse_part,
                          __bf16* __restrict__ o, float* __restrict__ lse, int64_t rows,
                          int splits) {
-  constexpr int PER = D / 64;  // columns per lane
+  constexpr int PER = (D + 63) / 64;  // columns per lane: lane, lane + 64, ...
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
@@ -246,13 +246,15 @@ attn_fwd_kv_merge_kernel(const float* __restrict__ o_part, const float* __restri
     const float lc = lse_part[c * rows + row];
     const float w = lc == -INFINITY ? 0.f : fast_exp2((lc - m) * kLog2e);
     wsum += w;
-    const float* src = o_part + (c * rows + row) * D + lane * PER;
+    const float* src = o_part + (c * rows + row) * D + lane;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, src[e], acc[e]);
+    for (int e = 0; e < PER; ++e)
+      if (e * 64 + lane < D) acc[e] = fmaf(w, src[e * 64], acc[e]);
   }
   const float inv = 1.f / wsum;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) o[row * D + lane * PER + e] = (__bf16)(acc[e] * inv);
+  for (int e = 0; e < PER; ++e)
+    if (e * 64 + lane < D) o[row * D + e * 64 + lane] = (__bf16)(acc[e] * inv);
   if (lane == 0) lse[row] = m + kLn2 * fast_log2(wsum);
 }
 
@@ -301,7 +303,13 @@ KvSplit kv_split_plan(int B, int H, int Nq, int Nk, int d, int num_splits) {
 
 hipError_t launch_fwd_kv(const FwdKvArgs& a) {
   const KvSplit sp = kv_split_plan(a.B, a.H, a.Nq, a.Nk, a.d, a.num_splits);
-  return a.d == 128 ? launch_kv<128>(a, sp) : launch_kv<64>(a, sp);
+  switch (a.d) {
+    case 32: return launch_kv<32>(a, sp);
+    case 64: return launch_kv<64>(a, sp);
+    case 96: return launch_kv<96>(a, sp);
+    case 128: return launch_kv<128>(a, sp);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace attn

@@ -8,6 +8,10 @@
 
 namespace attn {
 
+// Head dimensions every kernel is built for (bf16 and fp32 forward, backward,
+// key/value-cache forward).
+constexpr bool head_dim_supported(int d) { return d == 32 || d == 64 || d == 96 || d == 128; }
+
 struct FwdArgs {
   const void* q;
   const void* k;

@@ -113,21 +113,32 @@ __device__ __forceinline__ int tile_swizzle(int r) {
   }
 }
 
-// A 64-row tile of a row-major [rows][D] bf16 matrix held in LDS without
-// padding, its 16-byte chunks XOR-swizzled by row (tile_swizzle<D>).
-template <int D>
+// Width of the LDS layout that holds a row of head dimension d: d = 32 rows
+// sit in the 64-wide layout and d = 96 rows in the 128-wide one, their upper
+// chunks never written nor read.  The MFMA loops run over d itself (d / 16
+// k-steps, d / 32 output blocks), so the padding costs LDS space only.
+constexpr int tile_width(int d) { return d <= 64 ? 64 : 128; }
+
+// A 64-row tile of a row-major [rows][D] bf16 matrix held in LDS in rows of
+// LD columns without padding between rows, its 16-byte chunks XOR-swizzled by
+// row (tile_swizzle<LD>).  Columns D .. LD - 1 of the layout are unused.
+template <int LD, int D = LD>
 struct SwzTile {
+  static_assert(LD == 64 || LD == 128, "layout widths with a swizzle");
+  static_assert(D % 32 == 0 && D <= LD, "d must be a multiple of 32 within the layout");
   static constexpr int kRows = 64;
-  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kRowBytes = 2 * LD;
   static constexpr int kBytes = kRows * kRowBytes;
   static constexpr int kRowsPerDma = 1024 / kRowBytes;  // rows one wave instruction fills
-  static constexpr int kChunksPerRow = D / 8;
+  static constexpr int kChunksPerRow = LD / 8;
+  static constexpr int kDataChunks = D / 8;             // chunks that hold data
 
   // Copy rows [row0, row0 + 64) of `src` (row stride D elements) into `dst`
   // using the NW waves of the workgroup.  Lane l of an instruction writes
   // physical chunk l % kChunksPerRow of its row, so it fetches the logical
-  // chunk the swizzle maps there.  Rows at or past `nrows` re-read row
-  // nrows - 1 (finite values that the callers' masks give weight 0).
+  // chunk the swizzle maps there; lanes whose logical chunk lies past column
+  // D issue nothing.  Rows at or past `nrows` re-read row nrows - 1 (finite
+  // values that the callers' masks give weight 0).
   template <int NW>
   static __device__ __forceinline__ void load(const __bf16* src, int row0, int nrows,
                                               ATTN_LDS unsigned char* dst, int wave, int lane) {
@@ -140,8 +151,9 @@ struct SwzTile {
       const int blk = wave * kPerWave + i;
       const int row = blk * kRowsPerDma + r_in;
       const int g = min(row0 + row, nrows - 1);
-      const int col = (chunk ^ tile_swizzle<D>(row)) * 8;
-      lds_dma16(src + (int64_t)g * D + col, dst + blk * 1024);
+      const int logical = chunk ^ tile_swizzle<LD>(row);
+      if (kDataChunks == kChunksPerRow || logical < kDataChunks)
+        lds_dma16(src + (int64_t)g * D + logical * 8, dst + blk * 1024);
     }
   }
 
@@ -149,7 +161,7 @@ struct SwzTile {
   // rb * 32 + l32, logical chunk 2 s + half.  Byte offset:
   //   (row_read_base(l32, half) ^ (32 s)) + rb * 32 * kRowBytes.
   static __device__ __forceinline__ int row_read_base(int l32, int half) {
-    return (l32 * kRowBytes) | (((half ^ tile_swizzle<D>(l32)) & (kChunksPerRow - 1)) << 4);
+    return (l32 * kRowBytes) | (((half ^ tile_swizzle<LD>(l32)) & (kChunksPerRow - 1)) << 4);
   }
 
   // Transpose reads (ds_read_b64_tr_b16): lane (group grp = lane / 16,
@@ -161,7 +173,7 @@ struct SwzTile {
     const int grp = lane >> 4;
     const int row = (grp >> 1) * 4 + (g16 >> 2) + (hi ? 8 : 0);
     const int cpart = 2 * (grp & 1) + ((g16 & 3) >> 1);
-    return row * kRowBytes + (((cpart ^ tile_swizzle<D>(row)) & (kChunksPerRow - 1)) << 4) +
+    return row * kRowBytes + (((cpart ^ tile_swizzle<LD>(row)) & (kChunksPerRow - 1)) << 4) +
            8 * (g16 & 1);
   }
 };
