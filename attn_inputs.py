@@ -61,8 +61,10 @@ WORKLOADS = {
 HEADLINE = "b4_h16_n4096_d128_causal"
 
 # The headline shape at the other head dimensions the kernels take (forward
-# and backward); the pages fix no workload for them.
+# and backward; d = 256 forward only); the pages fix no workload for them.
 HEADDIM_WORKLOADS = {
+    "b4_h16_n4096_d256_causal": Workload("b4_h16_n4096_d256_causal", 4, 16, 4096, 256,
+                                         torch.bfloat16, True, 11),
     "b4_h16_n4096_d96_causal": Workload("b4_h16_n4096_d96_causal", 4, 16, 4096, 96,
                                         torch.bfloat16, True, 9, backward=True),
     "b4_h16_n4096_d32_causal": Workload("b4_h16_n4096_d32_causal", 4, 16, 4096, 32,

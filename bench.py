@@ -90,7 +90,7 @@ def algorithmic(w, kernel: str):
     return BHN * w.d * 2 * 2 + BHN * 4, "byte", "hbm"
 
 
-def cpu_baseline(w, q, k, v, do, budget_s: float):
+def cpu_baseline(w, q, k, v, do, budget_s: float, backward: bool = True):
     import numpy as np
 
     import oracle
@@ -98,12 +98,13 @@ def cpu_baseline(w, q, k, v, do, budget_s: float):
     scale = float(np.float32(w.scale))
     f64 = lambda t: t.to("cpu").double().numpy()
     heads, t0 = 0, time.perf_counter()
-    per_head = (w.fwd_flops() + w.bwd_flops()) / (w.B * w.H)
+    per_head = (w.fwd_flops() + (w.bwd_flops() if backward else 0.0)) / (w.B * w.H)
     for b in range(w.B):
         for h in range(w.H):
             qh, kh, vh, dh = f64(q[b, h]), f64(k[b, h]), f64(v[b, h]), f64(do[b, h])
             oracle.attn_fwd(qh, kh, vh, w.causal, scale, lib=lib)
-            oracle.attn_bwd(qh, kh, vh, dh, w.causal, scale, lib=lib)
+            if backward:
+                oracle.attn_bwd(qh, kh, vh, dh, w.causal, scale, lib=lib)
             heads += 1
             eprint(f"[cpu_baseline] oracle head {heads}: {time.perf_counter() - t0:.1f} s")
             if time.perf_counter() - t0 >= budget_s:
@@ -114,8 +115,9 @@ def cpu_baseline(w, q, k, v, do, budget_s: float):
     el = time.perf_counter() - t0
     return {"value": per_head * heads / el / 1e12, "unit": "TFLOP/s",
             "cores": oracle.num_threads(lib), "kind": "oracle",
-            "sample": f"{heads} of {w.B * w.H} heads of {w.name} (fp64 forward + backward per "
-                      f"head, S and P materialised), {el:.1f} s"}
+            "sample": f"{heads} of {w.B * w.H} heads of {w.name} (fp64 forward"
+                      f"{' + backward' if backward else ''} per head, S and P materialised), "
+                      f"{el:.1f} s"}
 
 
 def kernel_key(name: str):
@@ -396,6 +398,9 @@ def main():
         bench_softmax(args, SOFTMAX_WORKLOADS[args.workload])
         return
     w = {**WORKLOADS, **HEADDIM_WORKLOADS}[args.workload or HEADLINE]
+    # the backward is built for d <= 128; at d = 256 a step is the forward
+    backward = w.d <= 128
+    run_kernels = KERNELS if backward else KERNELS[:1]
     T.lib()
     dev = torch.device("cuda:0")
     eprint(f"[bench] generating inputs for {w.name}")
@@ -405,7 +410,8 @@ def main():
     o = torch.empty_like(qd)
     lse = torch.empty((B, H, N), device=dev, dtype=torch.float32)
     dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
-    ws = torch.empty(T.attn_bwd_workspace_bytes(B, H, N, d, w.dtype), device=dev, dtype=torch.uint8)
+    ws = torch.empty(max(1, T.attn_bwd_workspace_bytes(B, H, N, d, w.dtype)), device=dev,
+                     dtype=torch.uint8)
     stream = torch.cuda.current_stream()
 
     def step(events=None):
@@ -414,6 +420,8 @@ def main():
         T.attn_fwd(qd, kd, vd, o, lse, w.causal, w.scale, stream)
         if events is not None:
             events[1].record(stream)
+        if not backward:
+            return
         for ph in range(3):
             T.attn_bwd_phase(ph, qd, kd, vd, o, dod, lse, dq, dk, dv, ws, w.causal, w.scale,
                              stream)
@@ -427,7 +435,8 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(run_kernels) + 1)]
+           for _ in range(args.steps)]
     eprint(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -436,17 +445,17 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    per_kernel_ms = {kn: 0.0 for kn in KERNELS}
+    per_kernel_ms = {kn: 0.0 for kn in run_kernels}
     for e in evs:
-        for i, kn in enumerate(KERNELS):
+        for i, kn in enumerate(run_kernels):
             per_kernel_ms[kn] += e[i].elapsed_time(e[i + 1])
     event_total_ms = evs[0][0].elapsed_time(evs[-1][-1])
     ms_per_step = wall * 1e3 / args.steps
-    flops_step = w.fwd_flops() + w.bwd_flops()
+    flops_step = w.fwd_flops() + (w.bwd_flops() if backward else 0.0)
     value = flops_step * args.steps / wall / 1e12
 
     kernels = {}
-    for kn in KERNELS:
+    for kn in run_kernels:
         avg_ms = per_kernel_ms[kn] / args.steps
         amount, unit, bound = algorithmic(w, kn)
         if unit == "flop":
@@ -456,7 +465,7 @@ def main():
         kernels[kn] = {"avg_ms": round(avg_ms, 5), "bound": bound, "achieved": round(achieved, 2),
                        "peak": peak, "unit": u, "frac": round(achieved / peak, 4),
                        "traffic": measured_traffic(kn, w.name)}
-    dominant = max(KERNELS, key=lambda kn: per_kernel_ms[kn])
+    dominant = max(run_kernels, key=lambda kn: per_kernel_ms[kn])
     dk_ = kernels[dominant]
     roofline = {"kernel": dominant, "bound": dk_["bound"], "achieved": dk_["achieved"],
                 "peak": dk_["peak"], "unit": dk_["unit"], "frac": dk_["frac"],
@@ -465,12 +474,16 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         eprint("[bench] timing the oracle on the host")
-        cpu = cpu_baseline(w, q, k, v, do, args.cpu_baseline_seconds)
+        cpu = cpu_baseline(w, q, k, v, do, args.cpu_baseline_seconds, backward)
 
     fwd_ms = kernels["fwd"]["avg_ms"]
-    bwd_ms = sum(kernels[kn]["avg_ms"] for kn in KERNELS[1:])
+    bwd_ms = sum(kernels[kn]["avg_ms"] for kn in run_kernels[1:])
+    if w.name == HEADLINE:
+        metric = "fused attention fwd/bwd TFLOP/s + % bf16 MFMA peak, causal B4 H16 N4096 d128"
+    else:
+        metric = f"fused attention {'fwd/bwd' if backward else 'fwd'} TFLOP/s, {w.name}"
     out = {
-        "metric": "fused attention fwd/bwd TFLOP/s + % bf16 MFMA peak, causal B4 H16 N4096 d128",
+        "metric": metric,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -483,10 +496,10 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16 Q, K, V, dO)",
         "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
-                   "step": "forward + backward"},
+                   "step": "forward + backward" if backward else "forward"},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_tflops": round(w.fwd_flops() / (fwd_ms * 1e-3) / 1e12, 2),
-        "bwd_tflops": round(w.bwd_flops() / (bwd_ms * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(w.bwd_flops() / (bwd_ms * 1e-3) / 1e12, 2) if backward else None,
         "event_ms_per_step": round(event_total_ms / args.steps, 4),
         "roofline": roofline,
         "kernels": kernels,

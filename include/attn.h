@@ -24,8 +24,8 @@
  *   j from query i when j > i (the diagonal is visible).  `scale` multiplies
  *   Q K^T before the softmax; pass 1/sqrt(d) for the usual scaling.
  * - N may be any value >= 1 (no tile multiple is required); d must be 32, 64,
- *   96 or 128.  bf16 is supported by every entry point; fp32 by the forward
- *   only.
+ *   96, 128 or 256 (the backward: 32, 64, 96 or 128).  bf16 is supported by
+ *   every entry point; fp32 by the forward only.
  * - The caller owns every buffer (including the backward workspace).  The
  *   library never allocates, frees or synchronises; it enqueues kernels on
  *   `stream` (a hipStream_t, NULL = the default stream) and returns.  Results
@@ -57,7 +57,7 @@ typedef enum {
   ATTN_ERR_NULL = -1,      /* a required pointer is NULL */
   ATTN_ERR_SHAPE = -2,     /* B, H or N < 1, or sizes overflow 64-bit offsets */
   ATTN_ERR_DTYPE = -3,     /* unknown dtype, or dtype not supported by this entry point */
-  ATTN_ERR_HEADDIM = -4,   /* d is not 32, 64, 96 or 128 */
+  ATTN_ERR_HEADDIM = -4,   /* d is not 32, 64, 96, 128 or 256 (backward: <= 128) */
   ATTN_ERR_ALIGN = -5,     /* a pointer is not 16-byte aligned */
   ATTN_ERR_SCALE = -6,     /* scale is not finite */
   ATTN_ERR_WORKSPACE = -7, /* workspace NULL or smaller than attn_bwd_workspace_bytes() */
@@ -166,7 +166,7 @@ const char* attn_status_str(int status);
 
 /* Library ABI version; bumped when an entry point is added or a signature
  * changes (2: attn_fwd_kv and attn_fwd_kv_workspace_bytes; 3: attn_softmax_rows,
- * and head dimensions 32 and 96). */
+ * and head dimensions 32, 96 and 256). */
 int attn_abi_version(void);
 
 #ifdef __cplusplus

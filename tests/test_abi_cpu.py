@@ -56,7 +56,7 @@ def test_workspace_size():
     assert need <= n <= need + 256
     assert lib.attn_bwd_workspace_bytes(0, 1, 1, 64, 1) == 0
     assert lib.attn_bwd_workspace_bytes(1, 1, 1, 80, 1) == 0
-    assert lib.attn_bwd_workspace_bytes(1, 1, 1, 256, 1) == 0
+    assert lib.attn_bwd_workspace_bytes(1, 1, 1, 256, 1) == 0  # backward d <= 128
     assert lib.attn_bwd_workspace_bytes(1, 1, 1, 64, 0) == 0  # fp32 backward unsupported
 
 
@@ -67,7 +67,7 @@ FAKE = 1 << 20  # a 16-byte aligned non-null address, never dereferenced on erro
 @pytest.mark.parametrize("args,code", [
     (dict(q=0), -1), (dict(lse=0), -1),
     (dict(B=0), -2), (dict(H=-1), -2), (dict(N=0), -2),
-    (dict(d=80), -4), (dict(d=16), -4), (dict(d=256), -4), (dict(d=0), -4),
+    (dict(d=80), -4), (dict(d=16), -4), (dict(d=512), -4), (dict(d=0), -4),
     (dict(dtype=7), -3),
     (dict(q=FAKE + 8), -5), (dict(o=FAKE + 2), -5),
     (dict(scale=float("inf")), -6), (dict(scale=float("nan")), -6),
@@ -83,7 +83,7 @@ def test_fwd_validation(args, code):
 
 
 @pytest.mark.parametrize("args,code", [
-    (dict(dout=0), -1), (dict(dtype=0), -3), (dict(N=0), -2), (dict(d=80), -4),
+    (dict(dout=0), -1), (dict(dtype=0), -3), (dict(N=0), -2), (dict(d=80), -4), (dict(d=256), -4),
     (dict(ws=0), -7), (dict(ws_bytes=16), -7), (dict(dk=FAKE + 4), -5),
     (dict(scale=float("-inf")), -6),
 ])

@@ -4,9 +4,11 @@ same seeded inputs.  Every test here needs an MI355X and the built library.
 Coverage:
 * the five workloads at their real shapes (full oracle where it finishes in
   seconds, sampled query rows at the large shapes; the backward workload on
-  two full heads), and the B4 H16 N4096 causal shape at d = 96 and 32;
+  two full heads), and the B4 H16 N4096 causal shape at d = 96, 32 and 256
+  (forward only at 256);
 * ragged N (tails that span several tiles), N = 1, both masks,
-  d = 32 / 64 / 96 / 128, fp32 and bf16;
+  d = 32 / 64 / 96 / 128 / 256 (forward, fp32 and bf16) and d <= 128
+  (backward);
 * closed forms with exactly representable inputs (Q = 0);
 * the dV / dK sum invariants of the backward at full size;
 * determinism of the forward.
@@ -56,7 +58,7 @@ def test_h8_n1024_workloads(name):
 
 
 @pytest.mark.parametrize("N", [1, 17, 100, 255, 257, 1000])
-@pytest.mark.parametrize("d", [32, 64, 96, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_ragged_forward(N, d, causal, dtype):
@@ -109,6 +111,7 @@ def test_forward_is_deterministic():
     ("b2_h16_n4096_d64_causal_fwdbwd", [(0, 0), (1, 15)]),
     ("b4_h16_n4096_d96_causal", [(0, 0), (3, 15)]),
     ("b4_h16_n4096_d32_causal", [(0, 0), (2, 9)]),
+    ("b4_h16_n4096_d256_causal", [(0, 0), (3, 12)]),
 ])
 def test_full_size_forward_sampled_rows(name, heads):
     w = {**WORKLOADS, **HEADDIM_WORKLOADS}[name]

@@ -3,8 +3,8 @@ range split over workgroups and merged) against the fp64 oracle's
 oracle_attn_fwd_rect on the same seeded inputs.
 
 Coverage: decode (Nq = 1) and chunked prefill shapes, key counts that are not
-tile multiples, Nq = Nk, Nq > 128 (several query tiles), both masks, d = 64
-and 128, automatic and explicit split counts (including more splits than
+tile multiples, Nq = Nk, Nq > 128 (several query tiles), both masks,
+d = 32, 64, 96, 128 and 256, automatic and explicit split counts (including more splits than
 tiles, which the library caps), the decode workload at full size, agreement
 with attn_fwd when Nq = Nk, and bitwise determinism.
 """
@@ -41,7 +41,7 @@ def _check(q, k, v, causal, splits, tag):
 
 
 @pytest.mark.parametrize("Nk", [1, 63, 64, 65, 1000, 4097])
-@pytest.mark.parametrize("d", [32, 64, 96, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_decode_shapes(Nk, d, causal):
     q, k, v = make_kv_inputs(2, 3, 1, Nk, d, seed=100 + Nk + d)
@@ -50,7 +50,7 @@ def test_decode_shapes(Nk, d, causal):
 
 @pytest.mark.parametrize("Nq,Nk", [(7, 100), (64, 64), (128, 1000), (200, 333), (130, 2049),
                                    (300, 300)])
-@pytest.mark.parametrize("d", [32, 64, 96, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_prefill_shapes(Nq, Nk, d, causal):
     q, k, v = make_kv_inputs(1, 2, Nq, Nk, d, seed=200 + Nq + Nk + d)

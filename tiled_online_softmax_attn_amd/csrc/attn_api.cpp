@@ -45,7 +45,8 @@ const char* attn_status_str(int status) {
     case ATTN_ERR_NULL: return "a required pointer is NULL";
     case ATTN_ERR_SHAPE: return "B, H and N must be >= 1 and the sizes must fit 64-bit offsets";
     case ATTN_ERR_DTYPE: return "dtype not supported by this entry point";
-    case ATTN_ERR_HEADDIM: return "head dimension d must be 32, 64, 96 or 128";
+    case ATTN_ERR_HEADDIM:
+      return "head dimension d must be 32, 64, 96, 128 or 256 (backward: at most 128)";
     case ATTN_ERR_ALIGN: return "pointers must be 16-byte aligned";
     case ATTN_ERR_SCALE: return "scale must be finite";
     case ATTN_ERR_WORKSPACE:
@@ -70,7 +71,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
 }
 
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d, int dtype) {
-  if (check_shape(B, H, N, d) != ATTN_OK || dtype != ATTN_DTYPE_BF16) return 0;
+  if (check_shape(B, H, N, d) != ATTN_OK || !attn::bwd_head_dim_supported(d) ||
+      dtype != ATTN_DTYPE_BF16)
+    return 0;
   return attn::bwd_delta_bytes(B, H, N);
 }
 
@@ -81,6 +84,7 @@ static int bwd_common(int phase, const void* q, const void* k, const void* v, co
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL;
   int rc = check_shape(B, H, N, d);
   if (rc != ATTN_OK) return rc;
+  if (!attn::bwd_head_dim_supported(d)) return ATTN_ERR_HEADDIM;
   if (phase < -1 || phase > 2) return ATTN_ERR_SHAPE;
   if (dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
   const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};

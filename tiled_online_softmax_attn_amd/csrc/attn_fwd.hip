@@ -53,7 +53,7 @@ __device__ __forceinline__ void fwd_tile_coords(int bid, int BH, int n_qtiles, b
 // off = 0 under the causal mask and off = N without it (every key visible).
 // A separate unmasked instantiation spilled registers at d = 96 and 128.
 template <int D>
-__global__ void __launch_bounds__(kFwdThreads, 2)
+__global__ void __launch_bounds__(kFwdThreads, D > 128 ? 1 : 2)
 attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      const __bf16* __restrict__ v, __bf16* __restrict__ o,
                      float* __restrict__ lse, int BH, int N, int n_qtiles, int off,
@@ -127,14 +127,30 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   auto qk = [&](f32x16 (&sacc)[2], const ATTN_LDS unsigned char* kbuf) {
     sacc[0] = f32x16{};
     sacc[1] = f32x16{};
+    auto read_k = [&](int s, int kb) {
+      return *reinterpret_cast<const ATTN_LDS bf16x8*>(kbuf + (k_base ^ (32 * s)) + kb * 32 * RB);
+    };
+    if constexpr (D > 128) {
+      // d = 256 runs one wave per SIMD with every register in use: read each
+      // k-step's K fragments one step ahead instead of all at once
+      bf16x8 a[2][2];
+      a[0][0] = read_k(0, 0);
+      a[0][1] = read_k(0, 1);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const int a_off = k_base ^ (32 * s);
+      for (int s = 0; s < KS; ++s) {
+        if (s + 1 < KS) {
+          a[(s + 1) & 1][0] = read_k(s + 1, 0);
+          a[(s + 1) & 1][1] = read_k(s + 1, 1);
+        }
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(kbuf + a_off + kb * 32 * RB);
-        sacc[kb] = mfma_32x32x16(a, qf[s], sacc[kb]);
+        for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma_32x32x16(a[s & 1][kb], qf[s], sacc[kb]);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    } else {
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma_32x32x16(read_k(s, kb), qf[s], sacc[kb]);
     }
   };
 
@@ -372,25 +388,29 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 
 // ---------------------------------------------------------------- fp32 path
 constexpr int kF32Threads = 256;
-constexpr int kF32BQ = 128;  // 2 threads per query
 constexpr int kF32BK = 32;
+// threads per query (each owns d / TPQ dims) and queries per workgroup
+template <int D> constexpr int kF32Tpq = D > 128 ? 4 : 2;
+template <int D> constexpr int kF32BQ = kF32Threads / kF32Tpq<D>;
 
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(kF32Threads)
 attn_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                     const float* __restrict__ v, float* __restrict__ o,
                     float* __restrict__ lse, int BH, int N, int n_qtiles, float scale_log2) {
-  constexpr int DH = D / 2;  // dims owned by each thread of a pair
+  constexpr int TPQ = kF32Tpq<D>;
+  constexpr int BQ = kF32BQ<D>;
+  constexpr int DH = D / TPQ;  // dims owned by each thread of a query
   __shared__ __attribute__((aligned(16))) float ks[kF32BK * D];
   __shared__ __attribute__((aligned(16))) float vs[kF32BK * D];
 
   const int tid = threadIdx.x;
-  const int pair_half = tid & 1;
+  const int pair_half = tid % TPQ;  // this thread's share of the query's dims
   int bh, qt;
   fwd_tile_coords(blockIdx.x, BH, n_qtiles, CAUSAL, bh, qt);
   const int64_t head = (int64_t)bh * N * D;
-  const int qry = qt * kF32BQ + (tid >> 1);
-  const int q_block_last = min(N, (qt + 1) * kF32BQ) - 1;
+  const int qry = qt * BQ + tid / TPQ;
+  const int q_block_last = min(N, (qt + 1) * BQ) - 1;
 
   float qr[DH], oa[DH];
   const float* qrow = q + head + (int64_t)(qry < N ? qry : 0) * D + pair_half * DH;
@@ -427,6 +447,7 @@ attn_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
 #pragma unroll
       for (int c = 0; c < DH; ++c) part = fmaf(qr[c], kr[c], part);
       float dot = part + __shfl_xor(part, 1);
+      if constexpr (TPQ == 4) dot += __shfl_xor(dot, 2);
       const int key = key0 + jj;
       if (key >= N || (CAUSAL && key > qry)) dot = -INFINITY;
       s[jj] = dot;
@@ -474,7 +495,7 @@ hipError_t launch_bf16(const FwdArgs& a) {
 
 template <int D, bool CAUSAL>
 hipError_t launch_f32(const FwdArgs& a) {
-  const int n_qtiles = (a.N + kF32BQ - 1) / kF32BQ;
+  const int n_qtiles = (a.N + kF32BQ<D> - 1) / kF32BQ<D>;
   const int BH = a.B * a.H;
   hipLaunchKernelGGL((attn_fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)(BH * n_qtiles)),
                      dim3(kF32Threads), 0, (hipStream_t)a.stream, (const float*)a.q,
@@ -498,6 +519,7 @@ hipError_t launch_fwd(const FwdArgs& a) {
     case 64: return launch_fwd_d<64>(a);
     case 96: return launch_fwd_d<96>(a);
     case 128: return launch_fwd_d<128>(a);
+    case 256: return launch_fwd_d<256>(a);
     default: return hipErrorInvalidValue;
   }
 }

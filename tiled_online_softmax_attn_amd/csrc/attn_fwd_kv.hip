@@ -37,7 +37,7 @@ constexpr float kKvRescaleSlack = 8.f;  // log2 units: P never exceeds 2^8
 // off = Nk - Nq under the causal mask and off = Nk (every key) without it,
 // so one code path serves both.
 template <int D>
-__global__ void __launch_bounds__(kKvThreads, 2)
+__global__ void __launch_bounds__(kKvThreads, D > 128 ? 1 : 2)
 attn_fwd_kv_partial_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                            const __bf16* __restrict__ v, float* __restrict__ o_part,
                            float* __restrict__ lse_part, int BH, int Nq, int Nk, int off,
@@ -308,6 +308,7 @@ hipError_t launch_fwd_kv(const FwdKvArgs& a) {
     case 64: return launch_kv<64>(a, sp);
     case 96: return launch_kv<96>(a, sp);
     case 128: return launch_kv<128>(a, sp);
+    case 256: return launch_kv<256>(a, sp);
     default: return hipErrorInvalidValue;
   }
 }

@@ -8,9 +8,12 @@
 
 namespace attn {
 
-// Head dimensions every kernel is built for (bf16 and fp32 forward, backward,
-// key/value-cache forward).
-constexpr bool head_dim_supported(int d) { return d == 32 || d == 64 || d == 96 || d == 128; }
+// Head dimensions the forward kernels are built for (bf16 and fp32 forward,
+// key/value-cache forward), and those the backward is built for.
+constexpr bool head_dim_supported(int d) {
+  return d == 32 || d == 64 || d == 96 || d == 128 || d == 256;
+}
+constexpr bool bwd_head_dim_supported(int d) { return head_dim_supported(d) && d <= 128; }
 
 struct FwdArgs {
   const void* q;

@@ -101,11 +101,13 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 //   * ds_read_b128 of one chunk by 8 lanes on 8 consecutive rows, and
 //   * ds_read_b64_tr_b16 by 16 lanes on 4 consecutive rows (first row a
 //     multiple of 4) and 2 adjacent chunks (first chunk even).
-// D = 128 (16 chunks, one row = all 64 banks): 4 (r & 3) + ((r >> 2) & 3).
+// D = 128 (16 chunks, one row = all 64 banks) and D = 256 (32 chunks, two
+// bank rows; the XOR only touches the low 4 bits of the chunk index, which
+// select the bank group): 4 (r & 3) + ((r >> 2) & 3).
 // D = 64 (8 chunks, two rows per 64 banks): bit-reverse of (r >> 1) & 7.
 template <int D>
 __device__ __forceinline__ int tile_swizzle(int r) {
-  if constexpr (D == 128) {
+  if constexpr (D >= 128) {
     return ((r & 3) << 2) | ((r >> 2) & 3);
   } else {
     const int x = (r >> 1) & 7;
@@ -117,14 +119,14 @@ __device__ __forceinline__ int tile_swizzle(int r) {
 // sit in the 64-wide layout and d = 96 rows in the 128-wide one, their upper
 // chunks never written nor read.  The MFMA loops run over d itself (d / 16
 // k-steps, d / 32 output blocks), so the padding costs LDS space only.
-constexpr int tile_width(int d) { return d <= 64 ? 64 : 128; }
+constexpr int tile_width(int d) { return d <= 64 ? 64 : d <= 128 ? 128 : 256; }
 
 // A 64-row tile of a row-major [rows][D] bf16 matrix held in LDS in rows of
 // LD columns without padding between rows, its 16-byte chunks XOR-swizzled by
 // row (tile_swizzle<LD>).  Columns D .. LD - 1 of the layout are unused.
 template <int LD, int D = LD>
 struct SwzTile {
-  static_assert(LD == 64 || LD == 128, "layout widths with a swizzle");
+  static_assert(LD == 64 || LD == 128 || LD == 256, "layout widths with a swizzle");
   static_assert(D % 32 == 0 && D <= LD, "d must be a multiple of 32 within the layout");
   static constexpr int kRows = 64;
   static constexpr int kRowBytes = 2 * LD;
