@@ -7,6 +7,10 @@ preprocess D, dK/dV, dQ) on the causal B=4 H=16 N=4096 d=128 bf16
 workload.  Inputs are generated on the host from a fixed seed, copied to the
 GPU, and resident in HBM before the timed region starts.
 
+With `--workload` naming another attention shape (attn_inputs.WORKLOADS or
+HEADDIM_WORKLOADS, e.g. b4_h16_n4096_d96_causal) a step is the same pass on
+that shape; at d = 256, where no backward is built, the forward alone.
+
 With `--workload` naming a key/value-cache shape (attn_inputs.KV_WORKLOADS,
 e.g. decode_b8_h32_nq1_nk8192_d128) a step is instead one attn_fwd_kv call
 (per-chunk partial kernel + merge kernel) and `value` is the K/V bytes read
