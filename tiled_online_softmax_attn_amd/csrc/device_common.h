@@ -17,10 +17,10 @@
 //   v_permlane32_swap(x, x) returns {x of lanes 0-31 in both halves,
 //     x of lanes 32-63 in both halves}.
 //
-//   global_load_lds_dwordx4 (direct global -> LDS): lane l's 16 bytes land at
-//     LDS address M0 + 16 l, so one wave instruction fills 1 KiB of LDS in
-//     lane order.  The instruction's immediate offset moves the global AND the
-//     LDS address, so it is kept at 0.
+//   buffer_load_dwordx4 ... lds (direct global -> LDS): lane l's 16 bytes
+//     land at LDS address M0 + 16 l, so one wave instruction fills 1 KiB of
+//     LDS in lane order.  The instruction's immediate offset moves the global
+//     AND the LDS address, so it is kept at 0.
 //
 // LDS banks: 64 banks of 4 bytes.  A ds_read_b128 is served 8 lanes at a
 // time and a ds_read_b64_tr_b16 16 lanes at a time; both are conflict-free
@@ -82,13 +82,9 @@ __device__ __forceinline__ float sum_across_halves(float x) {
   return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
-// Asynchronous copy of 16 bytes per lane from global memory to LDS.  `lds`
-// must be the same for every lane of the wave (it is the base of the 1 KiB
-// the wave writes); lane l's bytes land at lds + 16 l.
-__device__ __forceinline__ void lds_dma16(const void* src, ATTN_LDS void* lds) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src, lds, 16, 0,
-                                   0);
-}
+// Word 3 of a raw buffer resource on gfx9-family chips: 32-bit data format
+// (any non-zero format enables untyped loads), everything else default.
+constexpr int kBufferRsrcWord3 = 0x00020000;
 
 // Wait until every outstanding global load of this wave (including LDS DMA)
 // has completed.
@@ -139,8 +135,11 @@ struct SwzTile {
   // using the NW waves of the workgroup.  Lane l of an instruction writes
   // physical chunk l % kChunksPerRow of its row, so it fetches the logical
   // chunk the swizzle maps there; lanes whose logical chunk lies past column
-  // D issue nothing.  Rows at or past `nrows` re-read row nrows - 1 (finite
-  // values that the callers' masks give weight 0).
+  // D issue nothing.  The copies are buffer loads whose resource starts at
+  // row row0 and ends at row nrows (at most 64 rows on), so the per-lane
+  // offsets are the same for every tile and need no address arithmetic in
+  // the loop; rows at or past `nrows` fall outside the resource and read as
+  // zeros (finite values that the callers' masks give weight 0).
   template <int NW>
   static __device__ __forceinline__ void load(const __bf16* src, int row0, int nrows,
                                               ATTN_LDS unsigned char* dst, int wave, int lane) {
@@ -148,14 +147,20 @@ struct SwzTile {
     static_assert(kRows % (kRowsPerDma * NW) == 0, "tile must split over the waves");
     const int r_in = lane / kChunksPerRow;
     const int chunk = lane % kChunksPerRow;
+    const int w = __builtin_amdgcn_readfirstlane(wave);  // LDS destinations in SGPRs
+    // (uniform; readfirstlane keeps the resource in SGPRs where a VALU min
+    // or max would otherwise leave it in VGPRs behind a waterfall loop)
+    const int rows_left = __builtin_amdgcn_readfirstlane(min(max(nrows - row0, 0), kRows));
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(src + (int64_t)row0 * D), (short)0, rows_left * D * 2, kBufferRsrcWord3);
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
-      const int blk = wave * kPerWave + i;
+      const int blk = w * kPerWave + i;
       const int row = blk * kRowsPerDma + r_in;
-      const int g = min(row0 + row, nrows - 1);
       const int logical = chunk ^ tile_swizzle<LD>(row);
       if (kDataChunks == kChunksPerRow || logical < kDataChunks)
-        lds_dma16(src + (int64_t)g * D + logical * 8, dst + blk * 1024);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (ATTN_LDS void*)(dst + blk * 1024), 16,
+                                                  row * (2 * D) + logical * 16, 0, 0, 0);
     }
   }
 
