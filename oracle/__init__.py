@@ -16,8 +16,12 @@ that file's header:
 * ``attn_fwd``      - O = softmax(scale * Q K^T [+ causal mask]) V and the
   per-row logsumexp (CS336 Lecture 5 notes "GPUs, TPUs", sections 8.1, 8.3).
 * ``attn_fwd_rows`` - the same definition for selected query rows only.
+* ``attn_fwd_rect`` - Nq queries at the end of an Nk-key sequence.
 * ``attn_bwd``      - dQ, dK, dV of sum(dO * O) (CS336 L5 notes section 8.4,
   Exercise 9).
+* ``mx_decode``     - values of an MXFP8 tensor (E4M3 codes, one E8M0 scale
+  per 32 elements of a row; CS336 L5 notes section 6.2); attention of MXFP8
+  inputs is ``attn_fwd`` of the decoded values.
 
 Every function is pinned by ``tests/test_oracle_pins.py`` against values the
 pages print, closed forms, brute force in 50-digit decimal arithmetic and
@@ -86,6 +90,8 @@ def _declare(lib):
     lib.oracle_attn_fwd_rect.restype = ctypes.c_int
     lib.oracle_attn_fwd_rect.argtypes = [_DP, _DP, _DP, i64, i64, i64, ctypes.c_int,
                                          ctypes.c_double, _DP, _DP]
+    lib.oracle_mx_decode.restype = ctypes.c_int
+    lib.oracle_mx_decode.argtypes = [ctypes.c_void_p, ctypes.c_void_p, i64, i64, _DP]
     lib.oracle_attn_bwd_head.restype = ctypes.c_int
     lib.oracle_attn_bwd_head.argtypes = [_DP, _DP, _DP, _DP, i64, i64, ctypes.c_int,
                                          ctypes.c_double, _DP, _DP, _DP, _DP, _DP, _DP]
@@ -191,6 +197,27 @@ def attn_fwd_rect(q, k, v, causal: bool, scale: float, lib=None):
                                       int(bool(causal)), float(scale), _ptr(o[g]), _ptr(lse[g]))
         _check(rc, "attn_fwd_rect")
     return o.reshape(lead + (Nq, d)), lse.reshape(lead + (Nq,))
+
+
+def mx_decode(codes, scales, lib=None) -> np.ndarray:
+    """Values of an MXFP8 tensor: ``codes`` uint8 E4M3 of shape [..., d],
+    ``scales`` uint8 E8M0 of shape [..., d / 32] (one per 32 elements of a
+    row).  Returns float64 [..., d].  Accepts numpy arrays or CPU tensors."""
+    lib = lib or load()
+    if hasattr(codes, "detach"):
+        codes = codes.detach().to("cpu").numpy()
+    if hasattr(scales, "detach"):
+        scales = scales.detach().to("cpu").numpy()
+    codes = np.ascontiguousarray(np.asarray(codes).view(np.uint8))
+    scales = np.ascontiguousarray(np.asarray(scales).view(np.uint8))
+    d = codes.shape[-1]
+    if scales.shape != codes.shape[:-1] + (d // 32,):
+        raise ValueError(f"scales shape {scales.shape} does not match codes {codes.shape}")
+    out = np.empty(codes.shape, dtype=np.float64)
+    rows = codes.size // d
+    _check(lib.oracle_mx_decode(codes.ctypes.data, scales.ctypes.data, rows, d, _ptr(out)),
+           "mx_decode")
+    return out
 
 
 def attn_bwd(q, k, v, dout, causal: bool, scale: float, lib=None):

@@ -298,3 +298,37 @@ int oracle_attn_bwd_head(const double* q, const double* k, const double* v,
   free(P); free(dS); free(O); free(L); free(D);
   return 0;
 }
+
+/* ---------------------------------------------------------------- MXFP8
+ * Q and K given in the MXFP8 format the CS336 L5 notes (section 6.2) name:
+ * E4M3 values plus one E8M0 scale for every 32 elements of a row.  The
+ * formats (OCP FP8 and OCP microscaling):
+ *   E4M3: sign bit, 4 exponent bits (bias 7), 3 mantissa bits; exponent
+ *         field 0 holds the subnormals m * 2^-9; S.1111.111 is NaN; there
+ *         are no infinities (largest finite value 448).
+ *   E8M0: an unsigned exponent, value 2^(e - 127); 0xFF is NaN.
+ * The attention of MXFP8 inputs is the attention of their decoded values,
+ * so the oracle only decodes (exactly, in double precision). */
+static double e4m3_value(uint8_t b) {
+  const int sign = b >> 7, e = (b >> 3) & 15, m = b & 7;
+  if (e == 15 && m == 7) return NAN;
+  const double mag = (e == 0) ? ldexp((double)m, -9) : ldexp(8.0 + m, e - 10);
+  return sign ? -mag : mag;
+}
+
+static double e8m0_value(uint8_t e) { return e == 255 ? NAN : ldexp(1.0, (int)e - 127); }
+
+/* rows x d E4M3 codes (row-major) with rows x (d / 32) E8M0 scales: element
+ * (r, c) is e4m3(codes[r][c]) * e8m0(scales[r][c / 32]).  d must be a
+ * multiple of 32. */
+int oracle_mx_decode(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t d,
+                     double* out) {
+  if (!codes || !scales || !out) return -1;
+  if (rows < 0 || d < 32 || d % 32 != 0) return -2;
+  const int64_t nb = d / 32;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < d; ++c)
+      out[r * d + c] = e4m3_value(codes[r * d + c]) * e8m0_value(scales[r * nb + c / 32]);
+  return 0;
+}
+

@@ -26,6 +26,10 @@ What pins what:
   section 4.9 key/value cache): 50-digit brute force with the shifted causal
   mask, Q = 0 closed form, and the blocked merge of per-chunk (O, lse) pairs
   (CS149 L9 notes section 9) that split-key attention relies on.
+* MXFP8 decoding (CS336 L5 notes section 6.2: E4M3 values, one E8M0 scale
+  per 32 elements): every E4M3 code against torch's float8_e4m3fn cast and
+  the format's fixed points (1, 448, 2^-6, 2^-9, NaN); E8M0 against its
+  definition 2^(e-127); the scale of element c is that of block c / 32.
 """
 from __future__ import annotations
 
@@ -402,9 +406,51 @@ def pin_rect_merge(lib):
     _assert_close(o_m, o, 1e-13, 1e-14, "merged O")
 
 
+def pin_mx_e4m3_codes(lib):
+    """Every E4M3 code decodes to torch's float8_e4m3fn value (a separate
+    implementation of the OCP format), and the format's fixed points hold."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8).reshape(8, 32)
+    scales = np.full((8, 1), 127, dtype=np.uint8)  # 2^0
+    got = oracle.mx_decode(codes, scales, lib=lib).reshape(-1)
+    ref = torch.from_numpy(codes.reshape(-1).copy()).view(torch.float8_e4m3fn).double().numpy()
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all(), "NaN codes"
+    assert nan.sum() == 2 and nan[0x7F] and nan[0xFF], "exactly S.1111.111 is NaN"
+    assert np.array_equal(got[~nan], ref[~nan]), "E4M3 values differ from torch's"
+    fixed = {0x00: 0.0, 0x38: 1.0, 0xB8: -1.0, 0x7E: 448.0, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9,
+             0x07: 7 * 2.0 ** -9, 0x40: 2.0, 0x3C: 1.5}
+    for c, val in fixed.items():
+        assert got[c] == val, f"code {c:#04x}: {got[c]} != {val}"
+
+
+def pin_mx_scales(lib):
+    """E8M0 scale e multiplies by 2^(e - 127) (255 is NaN), and element c of a
+    row takes the scale of block c // 32."""
+    d = 128
+    codes = np.full((3, d), 0x38, dtype=np.uint8)  # all 1.0
+    scales = np.array([[127, 128, 126, 200], [0, 254, 127, 127], [255, 127, 1, 129]],
+                      dtype=np.uint8)
+    got = oracle.mx_decode(codes, scales, lib=lib)
+    for r in range(3):
+        for c in range(d):
+            e = int(scales[r, c // 32])
+            want = float("nan") if e == 255 else 2.0 ** (e - 127)
+            if math.isnan(want):
+                assert math.isnan(got[r, c]), f"({r},{c}) should be NaN"
+            else:
+                assert got[r, c] == want, f"({r},{c}): {got[r, c]} != {want}"
+    # a value times its scale (sign and magnitude)
+    codes = np.array([[0xC4] * 32 + [0x11] * 32], dtype=np.uint8)  # -3.0, 2^-9*... codes
+    scales = np.array([[130, 100]], dtype=np.uint8)
+    got = oracle.mx_decode(codes, scales, lib=lib)
+    assert got[0, 0] == -3.0 * 8 and got[0, 40] == (1 + 1 / 8) * 2.0 ** -5 * 2.0 ** -27
+
+
 FORWARD_PINS = [pin_worked_example, pin_blocked_identity, pin_streaming_and_blocked,
                 pin_rows_sum_to_one, pin_constant_v, pin_q_zero, pin_row0_and_single_key,
                 pin_brute_force, pin_large_logits, pin_rows_entry]
 BACKWARD_PINS = [pin_bwd_finite_differences, pin_bwd_D_identity, pin_bwd_invariants]
 RECT_PINS = [pin_rect_brute_force, pin_rect_q_zero, pin_rect_merge]
-ALL_PINS = FORWARD_PINS + BACKWARD_PINS + RECT_PINS
+MX_PINS = [pin_mx_e4m3_codes, pin_mx_scales]
+ALL_PINS = FORWARD_PINS + BACKWARD_PINS + RECT_PINS + MX_PINS

@@ -39,6 +39,11 @@ MUTANTS = {
     "rect_scale_dropped": ("s[j] = dot * scale;", "s[j] = dot;"),
     "rect_lse_log2": ("lse[i] = log(l) + m;", "lse[i] = log2(l) + m;"),
     "rect_pv_key_offset": ("oi[c] += p[j] * vj[c];", "oi[c] += p[j] * vj[c] * (j + 1 < Nk);"),
+    "e4m3_bias": ("ldexp(8.0 + m, e - 10)", "ldexp(8.0 + m, e - 11)"),
+    "e4m3_subnormal_as_normal": ("(e == 0) ? ldexp((double)m, -9) :", ""),
+    "e4m3_no_sign": ("return sign ? -mag : mag;", "return mag;"),
+    "mx_block_of_16": ("scales[r * nb + c / 32]", "scales[r * nb + c / 16 % nb]"),
+    "e8m0_bias": ("ldexp(1.0, (int)e - 127)", "ldexp(1.0, (int)e - 128)"),
 }
 
 
