@@ -201,3 +201,32 @@ def make_softmax_inputs(M: int, N: int, dtype: torch.dtype = torch.bfloat16, see
 
 def softmax_workload_inputs(w: SoftmaxWorkload):
     return make_softmax_inputs(w.M, w.N, w.dtype, w.seed, w.std)
+
+
+def make_mx_inputs(B: int, H: int, N: int, d: int, seed: int = 0, scale_lo: int = 125,
+                   scale_hi: int = 129):
+    """CPU tensors for the MXFP8 forward: q8, k8 uint8 E4M3 codes [B, H, N, d]
+    (float32 N(0, 1) draws cast with torch's float8_e4m3fn conversion), their
+    E8M0 scale codes q_scale, k_scale uint8 [B, H, N, d / 32] drawn uniformly
+    from [scale_lo, scale_hi] (block scales 2^-2 .. 2^2 by default), and v
+    bf16 [B, H, N, d] (N(0, 1)).  Draw order: Q, K, V values, then the Q and
+    K scale codes."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    shape = (B, H, N, d)
+    q = torch.randn(shape, generator=g, dtype=torch.float32)
+    k = torch.randn(shape, generator=g, dtype=torch.float32)
+    v = torch.randn(shape, generator=g, dtype=torch.float32)
+    sshape = (B, H, N, d // 32)
+    qs = torch.randint(scale_lo, scale_hi + 1, sshape, generator=g, dtype=torch.int32)
+    ks = torch.randint(scale_lo, scale_hi + 1, sshape, generator=g, dtype=torch.int32)
+    q8 = q.to(torch.float8_e4m3fn).view(torch.uint8)
+    k8 = k.to(torch.float8_e4m3fn).view(torch.uint8)
+    return q8, qs.to(torch.uint8), k8, ks.to(torch.uint8), v.to(torch.bfloat16)
+
+
+# The headline shape with Q and K in MXFP8 (seed 12).
+MX_WORKLOADS = {
+    "b4_h16_n4096_d128_causal_mxfp8": Workload("b4_h16_n4096_d128_causal_mxfp8", 4, 16, 4096, 128,
+                                               torch.bfloat16, True, 12),
+}

@@ -17,7 +17,8 @@ e.g. decode_b8_h32_nq1_nk8192_d128) a step is instead one attn_fwd_kv call
 per second, the quantity that bounds decode.  With a row-softmax shape
 (attn_inputs.SOFTMAX_WORKLOADS, softmax_m65536_n4096_bf16) a step is one
 attn_softmax_rows call and `value` is the bytes it must move (one read and
-one write of every element) per second.
+one write of every element) per second.  With the MXFP8 shape
+(attn_inputs.MX_WORKLOADS) a step is one attn_fwd_mx call.
 
 Prints ONE JSON line.  `value` is fwd+bwd TFLOP/s by the formula
 4*B*H*N^2*d (halved for causal) for the forward plus 2.5x that for the
@@ -39,6 +40,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 KERNELS = ("fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq")  # one step, in launch order
 COUNTED_KERNELS = KERNELS + ("softmax_rows",)  # kernels the HBM byte counters cover
@@ -361,6 +363,87 @@ def bench_softmax(args, w):
     print(json.dumps(out), flush=True)
 
 
+def bench_mx(args, w):
+    """One step = attn_fwd_mx (Q, K in MXFP8, V bf16) over the whole workload."""
+    import torch
+
+    import tiled_online_softmax_attn_amd as T
+    from attn_inputs import make_mx_inputs
+
+    T.lib()
+    dev = torch.device("cuda:0")
+    eprint(f"[bench] generating inputs for {w.name}")
+    q8, qs, k8, ks, v = make_mx_inputs(w.B, w.H, w.N, w.d, w.seed)
+    q8d, qsd, k8d, ksd, vd = (t.to(dev) for t in (q8, qs, k8, ks, v))
+    o = torch.empty_like(vd)
+    lse = torch.empty((w.B, w.H, w.N), device=dev, dtype=torch.float32)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        T.attn_fwd_mx(q8d, qsd, k8d, ksd, vd, o, lse, w.causal, w.scale, stream)
+
+    eprint(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    eprint(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / args.steps
+    flops = w.fwd_flops()
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / (call_ms * 1e-3) / 1e12
+    # half the FLOPs (S = Q K^T) on the FP8 matrix rate, half (P V) on bf16
+    peak = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
+    roofline = {"kernel": "fwd_mx", "bound": "mfma", "achieved": round(achieved, 1),
+                "peak": round(peak, 1), "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": None, "peak_note": "S on FP8 MFMA (5.0 PFLOP/s), P V on bf16 "
+                                              "(2.5 PFLOP/s), half the FLOPs each",
+                "avg_launch_us": round(call_ms * 1e3, 2)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        lib = oracle.load()
+        import numpy as np
+        heads, t0c = 0, time.perf_counter()
+        for b in range(w.B):
+            for h in range(w.H):
+                qh = oracle.mx_decode(q8[b, h], qs[b, h], lib=lib)
+                kh = oracle.mx_decode(k8[b, h], ks[b, h], lib=lib)
+                oracle.attn_fwd(qh, kh, v[b, h].double().numpy(), w.causal,
+                                float(np.float32(w.scale)), lib=lib)
+                heads += 1
+                if time.perf_counter() - t0c >= args.cpu_baseline_seconds:
+                    break
+            else:
+                continue
+            break
+        el = time.perf_counter() - t0c
+        cpu = {"value": flops / (w.B * w.H) * heads / el / 1e12, "unit": "TFLOP/s",
+               "cores": oracle.num_threads(lib), "kind": "oracle",
+               "sample": f"{heads} of {w.B * w.H} heads of {w.name} (decode + fp64 forward "
+                         f"per head), {el:.1f} s"}
+    out = {
+        "metric": f"fused attention fwd TFLOP/s, Q and K in MXFP8, {w.name}",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8-e4m3 (Q, K; E8M0 block scales) / bf16 (V, P, O)",
+        "data": "synthetic (seeded N(0,1) cast to E4M3, random E8M0 scales 2^-2..2^2; V bf16)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "step": "attn_fwd_mx"},
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -389,8 +472,8 @@ def main():
     import torch
 
     import tiled_online_softmax_attn_amd as T
-    from attn_inputs import (HEADDIM_WORKLOADS, HEADLINE, KV_WORKLOADS, SOFTMAX_WORKLOADS,
-                             WORKLOADS, workload_inputs)
+    from attn_inputs import (HEADDIM_WORKLOADS, HEADLINE, KV_WORKLOADS, MX_WORKLOADS,
+                             SOFTMAX_WORKLOADS, WORKLOADS, workload_inputs)
 
     if not torch.cuda.is_available():
         eprint("bench.py needs a GPU")
@@ -400,6 +483,9 @@ def main():
         return
     if args.workload in SOFTMAX_WORKLOADS:
         bench_softmax(args, SOFTMAX_WORKLOADS[args.workload])
+        return
+    if args.workload in MX_WORKLOADS:
+        bench_mx(args, MX_WORKLOADS[args.workload])
         return
     w = {**WORKLOADS, **HEADDIM_WORKLOADS}[args.workload or HEADLINE]
     # the backward is built for d <= 128; at d = 256 a step is the forward

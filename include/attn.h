@@ -148,6 +148,24 @@ int attn_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse
                 int B, int H, int Nq, int Nk, int d, int causal, float scale, int dtype,
                 int num_splits, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Forward pass with Q and K in MXFP8 (CS336 L5 notes section 6.2: E4M3
+ * values plus one E8M0 scale per 32 elements; here the blocks run along d,
+ * the dimension S = Q K^T contracts) and V in bf16.  Computes exactly what
+ * attn_fwd computes for the decoded Q and K:
+ *   Q[b,h,i,c] = e4m3(q8[b,h,i,c]) * 2^(q_scale[b,h,i,c/32] - 127), K alike.
+ *   q8, k8           : [B][H][N][d] E4M3 codes (OCP FP8: bias 7, no
+ *                      infinities, S.1111.111 = NaN), 16-byte aligned.
+ *   q_scale, k_scale : [B][H][N][d/32] E8M0 scale codes (2^(e-127); 255 =
+ *                      NaN), 4-byte aligned for d = 128, 2-byte for d = 64.
+ *   v                : [B][H][N][d] bf16.  o: bf16 [B][H][N][d].  lse: fp32.
+ *   d                : 64 or 128.
+ * S runs on the gfx950 scaled FP8 matrix instruction; P is rounded to bf16
+ * for P V as in attn_fwd.  Returns the codes of attn_fwd (ATTN_ERR_HEADDIM for
+ * d other than 64 or 128). */
+int attn_fwd_mx(const void* q8, const void* q_scale, const void* k8, const void* k_scale,
+                const void* v, void* o, float* lse, int B, int H, int N, int d, int causal,
+                float scale, void* stream);
+
 /* Row-wise softmax of an M x N row-major matrix x (PDC notes Lecture 5,
  * section 5.20, fused softmax; CS149 L9 notes section 8):
  *   y_ij = e^{x_ij - max_j x_ij} / sum_j e^{x_ij - max_j x_ij}.
@@ -166,7 +184,7 @@ const char* attn_status_str(int status);
 
 /* Library ABI version; bumped when an entry point is added or a signature
  * changes (2: attn_fwd_kv and attn_fwd_kv_workspace_bytes; 3: attn_softmax_rows,
- * and head dimensions 32, 96 and 256). */
+ * and head dimensions 32, 96 and 256; 4: attn_fwd_mx). */
 int attn_abi_version(void);
 
 #ifdef __cplusplus

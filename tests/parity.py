@@ -141,3 +141,16 @@ def oracle_softmax_rows(x: np.ndarray, rows=None) -> np.ndarray:
     rows = range(x.shape[0]) if rows is None else rows
     return np.stack([oracle.softmax_row(np.ascontiguousarray(x[r], dtype=np.float64))[0]
                      for r in rows])
+
+
+def gpu_forward_mx(q8, qs, k8, ks, v, causal, scale):
+    """MXFP8 inputs (CPU tensors); runs attn_fwd_mx into NaN-poisoned outputs;
+    returns CPU (o, lse)."""
+    dev = torch.device("cuda:0")
+    q8d, qsd, k8d, ksd, vd = (t.to(dev) for t in (q8, qs, k8, ks, v))
+    B, H, N, d = q8.shape
+    o = torch.full((B, H, N, d), float("nan"), device=dev, dtype=torch.bfloat16)
+    lse = torch.full((B, H, N), float("nan"), device=dev, dtype=torch.float32)
+    T.attn_fwd_mx(q8d, qsd, k8d, ksd, vd, o, lse, causal, scale)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()

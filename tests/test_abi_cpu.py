@@ -28,7 +28,7 @@ def _lib():
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted(["attn_fwd", "attn_bwd", "attn_bwd_phase",
                                            "attn_bwd_workspace_bytes", "attn_fwd_kv",
-                                           "attn_fwd_kv_workspace_bytes", "attn_softmax_rows",
+                                           "attn_fwd_kv_workspace_bytes", "attn_softmax_rows", "attn_fwd_mx",
                                            "attn_status_str", "attn_abi_version"])
 
 
@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = _lib()
-    assert lib.attn_abi_version() == 3
+    assert lib.attn_abi_version() == 4
     for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, 12345]:
         s = lib.attn_status_str(code)
         assert isinstance(s, bytes) and len(s) > 0
@@ -162,3 +162,19 @@ def test_softmax_rows_validation(args, code):
     a.update(args)
     assert lib.attn_softmax_rows(a["x"] or None, a["y"] or None, a["M"], a["N"], a["dtype"],
                                  None) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(q8=0), -1), (dict(k_scale=0), -1), (dict(N=0), -2), (dict(d=96), -4), (dict(d=256), -4),
+    (dict(q8=FAKE + 8), -5), (dict(q_scale=FAKE + 2), -5), (dict(d=64, k_scale=FAKE + 1), -5),
+    (dict(scale=float("nan")), -6),
+])
+def test_fwd_mx_validation(args, code):
+    lib = _lib()
+    a = dict(q8=FAKE, q_scale=FAKE, k8=FAKE, k_scale=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1,
+             N=16, d=128, causal=1, scale=0.1)
+    a.update(args)
+    rc = lib.attn_fwd_mx(*(a[n] or None for n in ("q8", "q_scale", "k8", "k_scale", "v", "o",
+                                                    "lse")),
+                         a["B"], a["H"], a["N"], a["d"], a["causal"], a["scale"], None)
+    assert rc == code

@@ -1,0 +1,81 @@
+"""GPU parity of attn_fwd_mx (Q and K in MXFP8: E4M3 codes with one E8M0
+scale per 32 elements along d; V bf16) against the fp64 oracle: the oracle
+decodes Q and K exactly (oracle.mx_decode) and runs its attention definition
+on the decoded values.
+
+S is exact up to fp32 summation on the scaled FP8 MFMA, and P and O are
+rounded to bf16 as in attn_fwd, so the bf16 tolerance applies
+(|gpu - oracle| <= 2e-2 + 1e-2 |oracle| on O and lse).
+
+Coverage: d = 64 and 128, both masks, N from 1 to 1000 (tails inside a
+tile and several tiles), block scales 2^-2..2^2, 2^-7..2^7 (large logits)
+and all 2^0, the headline shape at full size on sampled rows, and bitwise
+determinism.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from attn_inputs import MX_WORKLOADS, make_mx_inputs
+from tests.parity import (compare, describe, f32_scale, gpu_forward_mx, log, sample_rows, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tiled_online_softmax_attn_amd as T
+    T.lib()  # raises if libattn.so is missing: no silent fallback
+
+
+def _check_all(N, d, causal, seed, lo=125, hi=129, B=1, H=2):
+    q8, qs, k8, ks, v = make_mx_inputs(B, H, N, d, seed, lo, hi)
+    scale = d ** -0.5
+    log(f"[mx] N={N} d={d} causal={causal} scales [{lo}, {hi}] seed={seed}")
+    o, lse = gpu_forward_mx(q8, qs, k8, ks, v, causal, scale)
+    q = oracle.mx_decode(q8, qs)
+    k = oracle.mx_decode(k8, ks)
+    o_ref, lse_ref = oracle.attn_fwd(q, k, to_np(v), causal, f32_scale(scale))
+    eo = compare(to_np(o), o_ref, torch.bfloat16, f"mx O N={N} d={d}")
+    el = compare(to_np(lse), lse_ref, torch.bfloat16, f"mx lse N={N} d={d}")
+    log(f"    O {describe(eo)} | lse {describe(el)}")
+
+
+@pytest.mark.parametrize("N", [1, 17, 64, 100, 129, 255, 257, 1000])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_shapes(N, d, causal):
+    _check_all(N, d, causal, seed=700 + N + d)
+
+
+@pytest.mark.parametrize("lo,hi", [(120, 134), (127, 127)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_scale_ranges(lo, hi, d):
+    _check_all(300, d, True, seed=800 + lo + d, lo=lo, hi=hi)
+
+
+def test_workload_sampled_rows():
+    w = MX_WORKLOADS["b4_h16_n4096_d128_causal_mxfp8"]
+    log(f"[mx] {w.name}: generating inputs")
+    q8, qs, k8, ks, v = make_mx_inputs(w.B, w.H, w.N, w.d, w.seed)
+    o, lse = gpu_forward_mx(q8, qs, k8, ks, v, w.causal, w.scale)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    for b, h in [(0, 0), (3, 15)]:
+        rows = sample_rows(w.N, 48, seed=b * 100 + h)
+        q = oracle.mx_decode(q8[b, h], qs[b, h])
+        k = oracle.mx_decode(k8[b, h], ks[b, h])
+        o_ref, l_ref = oracle.attn_fwd_rows(q, k, to_np(v[b, h]), w.causal, f32_scale(w.scale), rows)
+        eo = compare(to_np(o[b, h])[rows], o_ref, torch.bfloat16, f"{w.name} O b{b} h{h}")
+        el = compare(to_np(lse[b, h])[rows], l_ref, torch.bfloat16, f"{w.name} lse b{b} h{h}")
+        log(f"    b{b} h{h} O {describe(eo)} | lse {describe(el)}")
+
+
+def test_deterministic():
+    q8, qs, k8, ks, v = make_mx_inputs(2, 4, 1000, 128, seed=9)
+    o1, l1 = gpu_forward_mx(q8, qs, k8, ks, v, True, 128 ** -0.5)
+    o2, l2 = gpu_forward_mx(q8, qs, k8, ks, v, True, 128 ** -0.5)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)

@@ -28,8 +28,8 @@ STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR
           -4: "ATTN_ERR_HEADDIM", -5: "ATTN_ERR_ALIGN", -6: "ATTN_ERR_SCALE",
           -7: "ATTN_ERR_WORKSPACE", -8: "ATTN_ERR_HIP"}
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_phase", "attn_bwd_workspace_bytes",
-           "attn_fwd_kv", "attn_fwd_kv_workspace_bytes", "attn_softmax_rows", "attn_status_str",
-           "attn_abi_version")
+           "attn_fwd_kv", "attn_fwd_kv_workspace_bytes", "attn_softmax_rows", "attn_fwd_mx",
+           "attn_status_str", "attn_abi_version")
 
 
 class AttnLibraryMissing(RuntimeError):
@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
                                   ctypes.c_size_t, vp]
         L.attn_fwd_kv_workspace_bytes.restype = ctypes.c_size_t
         L.attn_fwd_kv_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+        L.attn_fwd_mx.restype = i
+        L.attn_fwd_mx.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
         L.attn_softmax_rows.restype = i
         L.attn_softmax_rows.argtypes = [vp, vp, ctypes.c_longlong, i, i, vp]
         L.attn_status_str.restype = ctypes.c_char_p
@@ -182,6 +184,20 @@ def attn_fwd_kv(q, k, v, o, lse, causal: bool, scale: float, num_splits: int, wo
                            _ptr(workspace), ws_bytes, _stream_handle(stream))
     if rc != 0:
         raise AttnError(rc, "attn_fwd_kv")
+
+
+def attn_fwd_mx(q8, q_scale, k8, k_scale, v, o, lse, causal: bool, scale: float,
+                stream=None) -> None:
+    """Enqueue the forward with Q and K in MXFP8: q8, k8 E4M3 codes [B, H, N,
+    d] (uint8 or float8_e4m3fn tensors), q_scale, k_scale E8M0 codes
+    [B, H, N, d / 32] (uint8), v and o bf16 [B, H, N, d], lse fp32 [B, H, N]."""
+    _check_contig(q8, q_scale, k8, k_scale, v, o, lse)
+    B, H, N, d = _shape(q8)
+    rc = lib().attn_fwd_mx(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(v), _ptr(o),
+                           _ptr(lse), B, H, N, d, int(bool(causal)), float(scale),
+                           _stream_handle(stream))
+    if rc != 0:
+        raise AttnError(rc, "attn_fwd_mx")
 
 
 def attn_softmax_rows(x, y, stream=None) -> None:

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_fwd_kv.hip", "attn_bwd.hip", "softmax_rows.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_fwd_kv.hip", "attn_bwd.hip", "softmax_rows.hip", "attn_fwd_mx.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -156,6 +156,24 @@ int attn_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse
   attn::FwdKvArgs a{q, k, v, o, lse, B, H, Nq, Nk, d, causal != 0, scale, num_splits,
                     workspace, stream};
   return attn::launch_fwd_kv(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_fwd_mx(const void* q8, const void* q_scale, const void* k8, const void* k_scale,
+                const void* v, void* o, float* lse, int B, int H, int N, int d, int causal,
+                float scale, void* stream) {
+  if (!q8 || !q_scale || !k8 || !k_scale || !v || !o || !lse) return ATTN_ERR_NULL;
+  int rc = check_shape(B, H, N, d);
+  if (rc != ATTN_OK) return rc;
+  if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return ATTN_ERR_ALIGN;
+  // scale rows are d / 32 bytes, read as one 16- or 32-bit word
+  const uintptr_t salign = d == 128 ? 3u : 1u;
+  if ((reinterpret_cast<uintptr_t>(q_scale) & salign) || (reinterpret_cast<uintptr_t>(k_scale) & salign))
+    return ATTN_ERR_ALIGN;
+  if (!isfinite(scale)) return ATTN_ERR_SCALE;
+  attn::FwdMxArgs a{q8, q_scale, k8, k_scale, v, o, lse, B, H, N, d, causal != 0, scale, stream};
+  return attn::launch_fwd_mx(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 int attn_softmax_rows(const void* x, void* y, long long M, int N, int dtype, void* stream) {

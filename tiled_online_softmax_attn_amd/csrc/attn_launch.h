@@ -72,6 +72,23 @@ struct KvSplit {
 };
 KvSplit kv_split_plan(int B, int H, int Nq, int Nk, int d, int num_splits);
 
+// Forward with Q and K in MXFP8 (E4M3 codes, one E8M0 scale per 32 elements
+// along d) and V in bf16 (attn_fwd_mx).
+struct FwdMxArgs {
+  const void* q8;       // [B][H][N][d] E4M3
+  const void* q_scale;  // [B][H][N][d / 32] E8M0
+  const void* k8;
+  const void* k_scale;
+  const void* v;        // [B][H][N][d] bf16
+  void* o;              // [B][H][N][d] bf16
+  float* lse;           // [B][H][N]
+  int B, H, N, d;
+  int causal;
+  float scale;
+  void* stream;
+};
+hipError_t launch_fwd_mx(const FwdMxArgs& a);
+
 // Row-wise softmax of an M x N row-major matrix (attn_softmax_rows).
 struct SoftmaxArgs {
   const void* x;
