@@ -56,6 +56,18 @@ __device__ __forceinline__ i32x8 concat8(i32x4 lo, i32x4 hi) {
   return r;
 }
 
+// s_waitcnt with vmcnt = VM (at most VM of this wave's memory reads still in
+// flight) and lgkmcnt = 0, then s_barrier; the asm statements keep the
+// compiler from moving memory accesses across it.
+template <int VM>
+__device__ __forceinline__ void wait_copies_barrier() {
+  static_assert(VM >= 0 && VM < 63, "vmcnt field");
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | ((VM >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
 // Scales of a row's D / 32 blocks as one 32-bit word (byte b = block b).
 template <int D>
 __device__ __forceinline__ int load_scales(const unsigned char* row) {
@@ -82,18 +94,24 @@ attn_fwd_mx_kernel(const unsigned char* __restrict__ q8, const unsigned char* __
   constexpr int KS = D / 64;  // k-steps of the scaled S^T MFMA
   constexpr int DB = D / 32;  // 32-wide d blocks of O^T
   constexpr int NB = D / 32;  // MX blocks per row
+  // rings of three buffers (tile t in buffer t mod 3): copies run two
+  // iterations ahead of their use (K 8 KB and V 16 KB per buffer at d = 128,
+  // 72 KB per workgroup, two workgroups per CU)
   __shared__ __attribute__((aligned(1024))) unsigned char lds_k0[KTile::kBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char lds_k1[KTile::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_k2[KTile::kBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char lds_v0[VTile::kBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char lds_v1[VTile::kBytes];
-  auto k_lds = [&](auto par_tag) {
-    return (ATTN_LDS unsigned char*)(decltype(par_tag)::value ? lds_k1 : lds_k0);
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_v2[VTile::kBytes];
+  auto k_lds = [&](auto tag) {
+    constexpr int b = decltype(tag)::value % 3;
+    return (ATTN_LDS unsigned char*)(b == 0 ? lds_k0 : b == 1 ? lds_k1 : lds_k2);
   };
-  auto v_lds = [&](auto par_tag) {
-    return (ATTN_LDS unsigned char*)(decltype(par_tag)::value ? lds_v1 : lds_v0);
+  auto v_lds = [&](auto tag) {
+    constexpr int b = decltype(tag)::value % 3;
+    return (ATTN_LDS unsigned char*)(b == 0 ? lds_v0 : b == 1 ? lds_v1 : lds_v2);
   };
-  using Par0 = std::integral_constant<int, 0>;
-  using Par1 = std::integral_constant<int, 1>;
+
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -139,12 +157,14 @@ attn_fwd_mx_kernel(const unsigned char* __restrict__ q8, const unsigned char* __
     VTile::template load<kMxThreads / 64>(vh, j * kMxBK, N, dst, wave, lane);
   };
   // scale words of the lane's two keys of tile j (rows past the end re-read
-  // the last row; the mask gives those keys weight 0)
+  // the last row; the mask gives those keys weight 0), as loaded: the shift
+  // by 8 half happens where they are used, so that nothing waits for the
+  // load before then
   auto load_ksc = [&](int j, int (&dst)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int key = min(j * kMxBK + kb * 32 + l32, N - 1);
-      dst[kb] = load_scales<D>(ksh + (int64_t)key * NB) >> (8 * half);
+      dst[kb] = load_scales<D>(ksh + (int64_t)key * NB);
     }
   };
   const int k_base = KTile::row_read_base(l32, half);
@@ -156,7 +176,7 @@ attn_fwd_mx_kernel(const unsigned char* __restrict__ q8, const unsigned char* __
   for (int b = 0; b < DB; ++b) oacc[b] = f32x16{};
   float m_ref = -INFINITY;  // reference maximum (log2 units), moved lazily
   float l_run = 0.f;        // this lane's share of the running sum
-  int ksc[2][2];            // K scale words of the tiles of parity 0 / 1, [key half]
+  int ksc[3][2];            // K scale words of tile t in ksc[t mod 3], [key half]
 
   // S^T of one tile (K buffer kbuf, scale words ks_) into sacc; `between(i)`
   // runs after the i-th of the 2 KS MFMAs
@@ -169,8 +189,9 @@ attn_fwd_mx_kernel(const unsigned char* __restrict__ q8, const unsigned char* __
   };
   auto qk_mfma = [&](f32x16 (&sacc)[2], const i32x8& a, int i, const int (&ks_)[2]) {
     const int s = i >> 1, kb = i & 1;
-    if (s == 0) sacc[kb] = mfma_mx<0>(a, qf[0], sacc[kb], ks_[kb], qsc);
-    else sacc[kb] = mfma_mx<2>(a, qf[KS - 1], sacc[kb], ks_[kb], qsc);
+    const int ksw = ks_[kb] >> (8 * half);
+    if (s == 0) sacc[kb] = mfma_mx<0>(a, qf[0], sacc[kb], ksw, qsc);
+    else sacc[kb] = mfma_mx<2>(a, qf[KS - 1], sacc[kb], ksw, qsc);
   };
   auto qk = [&](f32x16 (&sacc)[2], const ATTN_LDS unsigned char* kbuf, const int (&ks_)[2]) {
     sacc[0] = f32x16{};
@@ -179,8 +200,9 @@ attn_fwd_mx_kernel(const unsigned char* __restrict__ q8, const unsigned char* __
     for (int i = 0; i < 2 * KS; ++i) qk_mfma(sacc, read_k(kbuf, i >> 1, i & 1), i, ks_);
   };
 
-  // Tile j.  On entry `sc` holds S^T of tile j; with NEXT the step forms S^T
-  // of tile j+1 into `sn` (K buffer and scale words of parity 1 - par) while
+  // Tile j (tag T = j mod 3).  On entry `sc` holds S^T of tile j; with NEXT
+  // the step forms S^T of tile j+1 into `sn` (K buffer and scale words
+  // T + 1) while
   // the VALU exponentiates tile j, then adds V_j^T P_j^T.  Issue order, eight
   // slots: slot t issues S^T MFMA t (t < 2 KS), the exponentials of 4 scores
   // and, from slot 2 on, two of the 4 DB PV MFMAs whose 16 keys are already
@@ -190,7 +212,7 @@ attn_fwd_mx_kernel(const unsigned char* __restrict__ q8, const unsigned char* __
                   auto next_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
     constexpr bool NEXT = decltype(next_tag)::value;
-    constexpr int P = decltype(par_tag)::value;
+    constexpr int T = decltype(par_tag)::value;
     const int key0 = j * kMxBK;
     if constexpr (MASK) {
 #pragma unroll
@@ -248,8 +270,8 @@ attn_fwd_mx_kernel(const unsigned char* __restrict__ q8, const unsigned char* __
     constexpr int kPvPerSlot = US / 8;  // 2 at d = 128, 1 at d = 64
     constexpr int kPvInLoop = kPvPerSlot * (kSlots - 2);
     if constexpr (NEXT) {
-      using Other = std::integral_constant<int, 1 - P>;
-      const ATTN_LDS unsigned char* kbuf = k_lds(Other{});
+      using Next = std::integral_constant<int, (T + 1) % 3>;
+      const ATTN_LDS unsigned char* kbuf = k_lds(Next{});
       sn[0] = f32x16{};
       sn[1] = f32x16{};
       i32x8 ka[2];
@@ -262,7 +284,7 @@ attn_fwd_mx_kernel(const unsigned char* __restrict__ q8, const unsigned char* __
 #pragma unroll
           for (int w = 0; w < kPvPerSlot; ++w) va[(t + 1) & 1][w] = read_v(kPvPerSlot * (t - 1) + w);
         }
-        if (t < 2 * KS) qk_mfma(sn, ka[t & 1], t, ksc[1 - P]);
+        if (t < 2 * KS) qk_mfma(sn, ka[t & 1], t, ksc[(T + 1) % 3]);
         exp_part(t);
         if (t >= 2) {
 #pragma unroll
@@ -296,54 +318,67 @@ attn_fwd_mx_kernel(const unsigned char* __restrict__ q8, const unsigned char* __
 
   // last tile this wave computes: later tiles lie wholly past all its queries
   const int last_tile = (int)min((int64_t)n_tiles - 1, ((int64_t)q_wave0 + 31 + off) / kMxBK);
-  // Iteration j reads K tile j+1 (buffer 1 - P) and V tile j (buffer P); the
-  // copies of K tile j+2 (into buffer P, whose tile j was last read in
-  // iteration j-1) and V tile j+1 (into buffer 1 - P) are in flight.
-  auto iteration = [&](const int j, auto par_tag, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-    constexpr int P = decltype(par_tag)::value;
-    using Other = std::integral_constant<int, 1 - P>;
-    if (j + 2 < n_tiles) {
-      load_k(j + 2, k_lds(par_tag));
-      load_ksc(j + 2, ksc[P]);
-    }
-    if (j + 1 < n_tiles) load_v(j + 1, v_lds(Other{}));
+  // Iteration j (tag T = j mod 3) reads K tile j+1 and V tile j; it copies
+  // K tile j+3 (into the buffer of K tile j, last read in iteration j-1), V
+  // tile j+2 (into the buffer of V tile j-1) and the scale words of K tile
+  // j+3, always the same number of copies (past the end they read zeros, or
+  // the last key's scales), so that the wait at its end can leave exactly
+  // this iteration's copies in flight.
+  constexpr int kCopiesK = KTile::kRows / KTile::kRowsPerDma / (kMxThreads / 64);
+  constexpr int kCopiesV = VTile::kRows / VTile::kRowsPerDma / (kMxThreads / 64);
+  constexpr int kInFlight = kCopiesK + kCopiesV + 2;
+  auto iteration = [&](const int j, auto T_tag, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    constexpr int T = decltype(T_tag)::value;
+    load_k(j + 3, k_lds(std::integral_constant<int, T>{}));
+    load_v(j + 2, v_lds(std::integral_constant<int, T + 2>{}));
+    load_ksc(j + 3, ksc[T]);
     if (j <= last_tile) {
       const int key0 = j * kMxBK;
       const bool need_mask =
           (key0 + kMxBK > N) || ((int64_t)key0 + kMxBK - 1 > (int64_t)q_wave0 + off);
       const bool next = j < last_tile;
       if (need_mask) {
-        if (next) step(j, par_tag, sc, sn, std::true_type{}, std::true_type{});
-        else step(j, par_tag, sc, sn, std::true_type{}, std::false_type{});
+        if (next) step(j, T_tag, sc, sn, std::true_type{}, std::true_type{});
+        else step(j, T_tag, sc, sn, std::true_type{}, std::false_type{});
       } else {
-        if (next) step(j, par_tag, sc, sn, std::false_type{}, std::true_type{});
-        else step(j, par_tag, sc, sn, std::false_type{}, std::false_type{});
+        if (next) step(j, T_tag, sc, sn, std::false_type{}, std::true_type{});
+        else step(j, T_tag, sc, sn, std::false_type{}, std::false_type{});
       }
     }
-    wait_vmem();
-    __syncthreads();
+    wait_copies_barrier<kInFlight>();
   };
 
-  // prologue: K tiles 0 and 1, V tile 0 and the scale words of K tiles 0
-  // and 1 loaded; S^T of tile 0
-  load_k(0, k_lds(Par0{}));
-  load_v(0, v_lds(Par0{}));
+  // prologue: K tiles 0..2, V tiles 0..1 and the scale words of K tiles 0..2
+  // issued; K tiles 0, 1, V tile 0 and their scales landed; S^T of tile 0
+  load_k(0, k_lds(std::integral_constant<int, 0>{}));
   load_ksc(0, ksc[0]);
-  if (n_tiles > 1) {
-    load_k(1, k_lds(Par1{}));
-    load_ksc(1, ksc[1]);
-  } else {
-    ksc[1][0] = ksc[1][1] = 0;
+  load_k(1, k_lds(std::integral_constant<int, 1>{}));
+  load_ksc(1, ksc[1]);
+  load_v(0, v_lds(std::integral_constant<int, 0>{}));
+  load_k(2, k_lds(std::integral_constant<int, 2>{}));
+  load_v(1, v_lds(std::integral_constant<int, 1>{}));
+  load_ksc(2, ksc[2]);
+  wait_copies_barrier<kCopiesK + kCopiesV + 2>();
+  f32x16 s_cur[2], s_nxt[2];
+  qk(s_cur, k_lds(std::integral_constant<int, 0>{}), ksc[0]);
+  wait_copies_barrier<kCopiesK + kCopiesV + 2>();  // K buffer 0 is refilled in iteration 0
+  auto advance = [&]() {  // S^T of the next tile becomes the current one
+    s_cur[0] = s_nxt[0];
+    s_cur[1] = s_nxt[1];
+  };
+  for (int j = 0; j < n_tiles; j += 3) {
+    iteration(j, std::integral_constant<int, 0>{}, s_cur, s_nxt);
+    advance();
+    if (j + 1 < n_tiles) {
+      iteration(j + 1, std::integral_constant<int, 1>{}, s_cur, s_nxt);
+      advance();
+    }
+    if (j + 2 < n_tiles) {
+      iteration(j + 2, std::integral_constant<int, 2>{}, s_cur, s_nxt);
+      advance();
+    }
   }
   wait_vmem();
-  __syncthreads();
-  f32x16 s_even[2], s_odd[2];
-  qk(s_even, k_lds(Par0{}), ksc[0]);
-  __syncthreads();  // K buffer 0 is refilled in iteration 0
-  for (int j = 0; j < n_tiles; j += 2) {
-    iteration(j, Par0{}, s_even, s_odd);
-    if (j + 1 < n_tiles) iteration(j + 1, Par1{}, s_odd, s_even);
-  }
 
   // ---- epilogue: O = O / l, lse = ln2 * (m + log2 l)
   const float l_tot = sum_across_halves(l_run);
