@@ -9,7 +9,8 @@ GPU, and resident in HBM before the timed region starts.
 
 With `--workload` naming another attention shape (attn_inputs.WORKLOADS or
 HEADDIM_WORKLOADS, e.g. b4_h16_n4096_d96_causal) a step is the same pass on
-that shape; at d = 256, where no backward is built, the forward alone.
+that shape; at d = 256 and in fp32, where no backward is built, the forward
+alone.
 
 With `--workload` naming a key/value-cache shape (attn_inputs.KV_WORKLOADS,
 e.g. decode_b8_h32_nq1_nk8192_d128) a step is instead one attn_fwd_kv call
@@ -277,6 +278,19 @@ def bench_kv(args, w):
     print(json.dumps(out), flush=True)
 
 
+def cpu_baseline_all(budget_s: float) -> int:
+    """The oracle on a bounded sample (whole heads, about budget_s seconds) of
+    each attention workload: forward, plus the backward where the workload
+    has one; one JSON line each."""
+    from attn_inputs import WORKLOADS, workload_inputs
+    for w in WORKLOADS.values():
+        eprint(f"[cpu_baseline] {w.name}")
+        q, k, v, do = workload_inputs(w, with_dout=True)
+        res = cpu_baseline(w, q, k, v, do, budget_s, backward=w.backward)
+        print(json.dumps({"workload": w.name, **res}), flush=True)
+    return 0
+
+
 def copy_reference(copy_mib: float) -> None:
     """One plain device copy of copy_mib MiB (x * 1), the known-size kernel
     that calibrates the HBM byte counters."""
@@ -452,6 +466,9 @@ def main():
     ap.add_argument("--workload", default=None, help="workload name (default: the headline)")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-baseline-all", action="store_true",
+                    help="time the oracle on a bounded sample of every attention workload "
+                         "(host only, no GPU) and print one JSON line per workload")
     ap.add_argument("--copy-mib", type=float, default=0.0,
                     help="run one plain device copy of this many MiB before timing "
                          "(reference kernel for the HBM byte counters)")
@@ -463,6 +480,9 @@ def main():
     if args.pmc_summary:
         from attn_inputs import HEADLINE
         sys.exit(pmc_summary(args.pmc_summary, args.copy_mib, args.workload or HEADLINE))
+
+    if args.cpu_baseline_all:
+        sys.exit(cpu_baseline_all(args.cpu_baseline_seconds))
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         eprint("bench.py: this build runs on exactly one GPU; multi-GPU runs are not "
@@ -488,8 +508,9 @@ def main():
         bench_mx(args, MX_WORKLOADS[args.workload])
         return
     w = {**WORKLOADS, **HEADDIM_WORKLOADS}[args.workload or HEADLINE]
-    # the backward is built for d <= 128; at d = 256 a step is the forward
-    backward = w.d <= 128
+    # the backward is built for bf16 with d <= 128; otherwise a step is the
+    # forward alone
+    backward = w.d <= 128 and w.dtype == torch.bfloat16
     run_kernels = KERNELS if backward else KERNELS[:1]
     T.lib()
     dev = torch.device("cuda:0")
@@ -536,9 +557,12 @@ def main():
     wall = time.perf_counter() - t0
 
     per_kernel_ms = {kn: 0.0 for kn in run_kernels}
+    samples = {kn: [] for kn in run_kernels}
     for e in evs:
         for i, kn in enumerate(run_kernels):
-            per_kernel_ms[kn] += e[i].elapsed_time(e[i + 1])
+            t = e[i].elapsed_time(e[i + 1])
+            per_kernel_ms[kn] += t
+            samples[kn].append(t)
     event_total_ms = evs[0][0].elapsed_time(evs[-1][-1])
     ms_per_step = wall * 1e3 / args.steps
     flops_step = w.fwd_flops() + (w.bwd_flops() if backward else 0.0)
@@ -552,7 +576,9 @@ def main():
             achieved, peak, u = amount / (avg_ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
         else:
             achieved, peak, u = amount / (avg_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
-        kernels[kn] = {"avg_ms": round(avg_ms, 5), "bound": bound, "achieved": round(achieved, 2),
+        srt = sorted(samples[kn])
+        kernels[kn] = {"avg_ms": round(avg_ms, 5), "median_ms": round(srt[len(srt) // 2], 5),
+                       "min_ms": round(srt[0], 5), "bound": bound, "achieved": round(achieved, 2),
                        "peak": peak, "unit": u, "frac": round(achieved / peak, 4),
                        "traffic": measured_traffic(kn, w.name)}
     dominant = max(run_kernels, key=lambda kn: per_kernel_ms[kn])
