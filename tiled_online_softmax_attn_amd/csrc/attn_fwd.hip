@@ -253,39 +253,55 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       // k-step 2 + u / 2 >= 2 kt + 2.  The last four PV steps follow the
       // loop.  MFMA and VALU work are thus spread evenly over the step.
       static_assert(KS == 8 && US == 16, "schedule written for d = 128");
+      // While in this loop the wave takes issue priority over the other wave
+      // of its SIMD (which may be issuing copies or a row maximum), so that
+      // the matrix unit stays fed.
+      __builtin_amdgcn_s_setprio(1);
       constexpr int kPvStart = 2;
       constexpr int kPvInLoop = 2 * (KS - kPvStart);
       const ATTN_LDS unsigned char* kbuf = k_lds(Other{});
       sn[0] = f32x16{};
       sn[1] = f32x16{};
-      bf16x8 a[2][2], va[2][2];
+      // K and V fragments are read two k-steps ahead of their MFMAs
+      constexpr int PD = 2;
+      bf16x8 a[PD + 1][2], va[PD + 1][2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        a[0][kb] = *reinterpret_cast<const ATTN_LDS bf16x8*>(kbuf + k_base + kb * 32 * RB);
+      for (int s0 = 0; s0 < PD; ++s0)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          a[s0][kb] = *reinterpret_cast<const ATTN_LDS bf16x8*>(kbuf + (k_base ^ (32 * s0)) + kb * 32 * RB);
+#pragma unroll
+      for (int s0 = 0; s0 < PD; ++s0)
+        if (s0 >= kPvStart) {
+          const int u0 = 2 * (s0 - kPvStart);
+          va[s0 % (PD + 1)][0] = read_v(u0);
+          va[s0 % (PD + 1)][1] = read_v(u0 + 1);
+        }
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        if (s + 1 < KS) {
+        if (s + PD < KS) {
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
-            a[(s + 1) & 1][kb] = *reinterpret_cast<const ATTN_LDS bf16x8*>(
-                kbuf + (k_base ^ (32 * (s + 1))) + kb * 32 * RB);
+            a[(s + PD) % (PD + 1)][kb] = *reinterpret_cast<const ATTN_LDS bf16x8*>(
+                kbuf + (k_base ^ (32 * (s + PD))) + kb * 32 * RB);
         }
-        // V fragments of the PV steps of k-step s + 1
-        if (s + 1 >= kPvStart && s + 1 < KS) {
-          const int u0 = 2 * (s + 1 - kPvStart);
-          va[(s + 1) & 1][0] = read_v(u0);
-          va[(s + 1) & 1][1] = read_v(u0 + 1);
+        // V fragments of the PV steps of k-step s + PD
+        if (s + PD >= kPvStart && s + PD < KS) {
+          const int u0 = 2 * (s + PD - kPvStart);
+          va[(s + PD) % (PD + 1)][0] = read_v(u0);
+          va[(s + PD) % (PD + 1)][1] = read_v(u0 + 1);
         }
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) sn[kb] = mfma_32x32x16(a[s & 1][kb], qf[s], sn[kb]);
+        for (int kb = 0; kb < 2; ++kb) sn[kb] = mfma_32x32x16(a[s % (PD + 1)][kb], qf[s], sn[kb]);
         exp_part(s);
         if (s >= kPvStart) {
           const int u0 = 2 * (s - kPvStart);
-          pv(u0, va[s & 1][0]);
-          pv(u0 + 1, va[s & 1][1]);
+          pv(u0, va[s % (PD + 1)][0]);
+          pv(u0 + 1, va[s % (PD + 1)][1]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_s_setprio(0);
       l_run += psum;
       bf16x8 vt[2];
       vt[0] = read_v(kPvInLoop);
