@@ -383,7 +383,7 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   static_assert(kDqBK == Tile::kRows, "key tile is one SwzTile");
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr bool kPipelineHalves = (D <= 64);
+  constexpr bool kPipelineHalves = (D <= 64) || CAUSAL;
   constexpr int RB = Tile::kRowBytes;
   // K and V tiles of 64 keys (SwzTile layout), two buffers each; K is read
   // both by rows (S^T) and transposed (dQ^T).  One LDS object per buffer, so
@@ -465,10 +465,10 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       const bool need_mask = (key0 + kDqBK > N) || (CAUSAL && key0 + kDqBK - 1 > q_wave0);
 
       if constexpr (kPipelineHalves) {
-        // The tile's 64 keys are two 32-key halves kb = 0, 1.  At d = 64 they
-        // are software-pipelined like the dK/dV kernel's query blocks (at
-        // d = 128 the pipelined order needs more registers than two waves per
-        // SIMD allow, and the plain order measured as fast):
+        // The tile's 64 keys are two 32-key halves kb = 0, 1, software-
+        // pipelined like the dK/dV kernel's query blocks (at d = 96 and 128
+        // without the causal mask this order spills registers at two waves
+        // per SIMD, so those take the plain order below):
         //   A  S^T, dP^T of half 0                       (MFMA)
         //   B  S^T, dP^T of half 1 |  P^T, dS^T of half 0 (VALU)
         //   C  dQ^T of half 0      |  P^T, dS^T of half 1
