@@ -175,7 +175,7 @@ int attn_fwd_mx(const void* q8, const void* q_scale, const void* k8, const void*
  *            least one finite entry.
  * Each row is read from HBM once and written once (twice read for rows of
  * more than 16384 elements).  Returns ATTN_OK, ATTN_ERR_NULL, ATTN_ERR_SHAPE
- * (M or N < 1, or M above 2^40), ATTN_ERR_DTYPE, ATTN_ERR_ALIGN
+ * (M or N < 1, M above 2^40 or M * N above 2^48), ATTN_ERR_DTYPE, ATTN_ERR_ALIGN
  * (x or y not 16-byte aligned) or ATTN_ERR_HIP. */
 int attn_softmax_rows(const void* x, void* y, long long M, int N, int dtype, void* stream);
 

@@ -154,6 +154,7 @@ def test_kv_validation(args, code):
 
 @pytest.mark.parametrize("args,code", [
     (dict(x=0), -1), (dict(y=0), -1), (dict(M=0), -2), (dict(N=0), -2), (dict(M=(1 << 40) + 1), -2),
+    (dict(M=1 << 30, N=1 << 20), -2),
     (dict(dtype=2), -3), (dict(x=FAKE + 4), -5), (dict(y=FAKE + 2), -5),
 ])
 def test_softmax_rows_validation(args, code):

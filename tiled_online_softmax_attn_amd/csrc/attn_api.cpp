@@ -179,7 +179,8 @@ int attn_fwd_mx(const void* q8, const void* q_scale, const void* k8, const void*
 int attn_softmax_rows(const void* x, void* y, long long M, int N, int dtype, void* stream) {
   if (!x || !y) return ATTN_ERR_NULL;
   if (M < 1 || N < 1) return ATTN_ERR_SHAPE;
-  if (M > (1LL << 40)) return ATTN_ERR_SHAPE;  // M * N elements must stay addressable
+  // M * N elements (at most 2^48) must stay addressable with 64-bit offsets
+  if (M > (1LL << 40) || M * (long long)N > (1LL << 48)) return ATTN_ERR_SHAPE;
   if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
   if (!aligned16(x) || !aligned16(y)) return ATTN_ERR_ALIGN;
   attn::SoftmaxArgs a{x, y, (int64_t)M, N, dtype == ATTN_DTYPE_BF16, stream};
