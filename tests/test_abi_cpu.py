@@ -179,3 +179,16 @@ def test_fwd_mx_validation(args, code):
                                                     "lse")),
                          a["B"], a["H"], a["N"], a["d"], a["causal"], a["scale"], None)
     assert rc == code
+
+
+def test_binding_refuses_host_tensors():
+    """The binding passes raw pointers, so host tensors are refused before any
+    library call (they would be dereferenced as device addresses)."""
+    import torch
+    import tiled_online_softmax_attn_amd as T
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 1, 8)
+    with pytest.raises(ValueError):
+        T.attn_fwd(q, q.clone(), q.clone(), torch.empty_like(q), lse, True, 0.125)
+    with pytest.raises(ValueError):
+        T.attn_softmax_rows(q, torch.empty_like(q))

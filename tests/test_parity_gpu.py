@@ -154,3 +154,27 @@ def test_fwdbwd_workload_backward(name, heads):
         for name, got in (("dq", dq), ("dk", dk), ("dv", dv)):
             e = compare(to_np(got[b, h]), ref[name], w.dtype, f"{w.name} {name} b{b} h{h}")
             log(f"    {name} b{b} h{h} {describe(e)}")
+
+
+def test_binding_refuses_mismatched_tensors():
+    """Every tensor must match the shape and dtype implied by Q and sit on Q's
+    GPU; the binding raises before a kernel could read or write past one."""
+    import tiled_online_softmax_attn_amd as T
+    dev = torch.device("cuda:0")
+    q = torch.zeros(1, 2, 100, 64, dtype=torch.bfloat16, device=dev)
+    lse = torch.zeros(1, 2, 100, device=dev)
+    short = torch.zeros(1, 2, 99, 64, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ValueError):
+        T.attn_fwd(q, short, q, torch.empty_like(q), lse, True, 0.125)
+    with pytest.raises(ValueError):
+        T.attn_fwd(q, q, q, torch.empty_like(q), lse.double(), True, 0.125)
+    with pytest.raises(ValueError):
+        T.attn_fwd(q, q, q.float(), torch.empty_like(q), lse, True, 0.125)
+    with pytest.raises(ValueError):
+        T.attn_fwd(q, q, q, torch.empty_like(q), lse.cpu(), True, 0.125)
+    ws = torch.empty(T.attn_bwd_workspace_bytes(1, 2, 100, 64), dtype=torch.uint8, device=dev)
+    g = [torch.empty_like(q) for _ in range(3)]
+    with pytest.raises(ValueError):
+        T.attn_bwd(q, q, q, q, q, lse, g[0], short, g[2], ws, True, 0.125)
+    with pytest.raises(ValueError):
+        T.attn_fwd_kv(q, short, q, torch.empty_like(q), lse, False, 0.125, 0, None)

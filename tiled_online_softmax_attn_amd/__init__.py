@@ -119,11 +119,38 @@ def _check_contig(*ts):
             raise ValueError("tensors must be contiguous [B, H, N, d] (lse [B, H, N])")
 
 
+def _check(where: str, t, shape, dtypes, device) -> None:
+    """The kernels see raw pointers and the sizes taken from the first
+    tensor, so every other tensor must have exactly the expected shape and
+    dtype and live on the same GPU; anything else is refused here rather than
+    read or written out of bounds."""
+    if t is None:
+        return  # the library reports ATTN_ERR_NULL
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{where}: expected a torch.Tensor")
+    if t.device.type != "cuda" or t.device != device:
+        raise ValueError(f"{where}: tensor on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{where}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{where}: dtype {t.dtype}, expected one of {dtypes}")
+
+
+def _check_workspace(where: str, ws, device) -> None:
+    if ws is None:
+        return
+    if not isinstance(ws, torch.Tensor) or ws.device != device or not ws.is_contiguous():
+        raise ValueError(f"{where}: workspace must be a contiguous tensor on {device}")
+
+
 def attn_fwd(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
     """Enqueue the forward: o = softmax(scale q k^T [+ causal]) v, lse = row
     logsumexp.  All tensors preallocated by the caller."""
     _check_contig(q, k, v, o, lse)
     B, H, N, d = _shape(q)
+    for name, t in (("k", k), ("v", v), ("o", o)):
+        _check(f"attn_fwd {name}", t, q.shape, (q.dtype,), q.device)
+    _check("attn_fwd lse", lse, (B, H, N), (torch.float32,), q.device)
     rc = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
                         int(bool(causal)), float(scale), _dtype_code(q), _stream_handle(stream))
     if rc != 0:
@@ -136,12 +163,22 @@ def attn_bwd_workspace_bytes(B: int, H: int, N: int, d: int,
     return int(lib().attn_bwd_workspace_bytes(B, H, N, d, code))
 
 
+def _check_bwd(where, q, k, v, o, dout, lse, dq, dk, dv, workspace) -> None:
+    B, H, N, _ = _shape(q)
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk),
+                    ("dv", dv)):
+        _check(f"{where} {name}", t, q.shape, (q.dtype,), q.device)
+    _check(f"{where} lse", lse, (B, H, N), (torch.float32,), q.device)
+    _check_workspace(where, workspace, q.device)
+
+
 def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool, scale: float,
              stream=None) -> None:
     """Enqueue the backward: dq, dk, dv of sum(dout * o).  ``workspace`` is a
     device tensor of at least attn_bwd_workspace_bytes() bytes."""
     _check_contig(q, k, v, o, dout, lse, dq, dk, dv)
     B, H, N, d = _shape(q)
+    _check_bwd("attn_bwd", q, k, v, o, dout, lse, dq, dk, dv, workspace)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                         _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, B, H, N, d,
@@ -152,9 +189,11 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool, scale: 
 
 def attn_bwd_phase(phase: int, q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool,
                    scale: float, stream=None) -> None:
-    """Enqueue one phase of attn_bwd (0 preprocess, 1 main, 2 dQ convert)."""
+    """Enqueue one phase of attn_bwd (0: D = rowsum(dO * O) into the
+    workspace; 1: dK and dV; 2: dQ)."""
     _check_contig(q, k, v, o, dout, lse, dq, dk, dv)
     B, H, N, d = _shape(q)
+    _check_bwd(f"attn_bwd_phase({phase})", q, k, v, o, dout, lse, dq, dk, dv, workspace)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = lib().attn_bwd_phase(int(phase), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
                               _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes,
@@ -177,7 +216,14 @@ def attn_fwd_kv(q, k, v, o, lse, causal: bool, scale: float, num_splits: int, wo
     (0 = chosen by the library) whose partial results are merged."""
     _check_contig(q, k, v, o, lse)
     B, H, Nq, d = _shape(q)
+    if not isinstance(k, torch.Tensor) or k.dim() != 4:
+        raise ValueError("attn_fwd_kv: k must be a [B, H, Nk, d] tensor")
     Nk = int(k.shape[2])
+    _check("attn_fwd_kv k", k, (B, H, Nk, d), (q.dtype,), q.device)
+    _check("attn_fwd_kv v", v, (B, H, Nk, d), (q.dtype,), q.device)
+    _check("attn_fwd_kv o", o, q.shape, (q.dtype,), q.device)
+    _check("attn_fwd_kv lse", lse, (B, H, Nq), (torch.float32,), q.device)
+    _check_workspace("attn_fwd_kv", workspace, q.device)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = lib().attn_fwd_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
                            int(bool(causal)), float(scale), _dtype_code(q), int(num_splits),
@@ -193,6 +239,15 @@ def attn_fwd_mx(q8, q_scale, k8, k_scale, v, o, lse, causal: bool, scale: float,
     [B, H, N, d / 32] (uint8), v and o bf16 [B, H, N, d], lse fp32 [B, H, N]."""
     _check_contig(q8, q_scale, k8, k_scale, v, o, lse)
     B, H, N, d = _shape(q8)
+    codes = (torch.uint8, torch.float8_e4m3fn)
+    dev = q8.device
+    _check("attn_fwd_mx q8", q8, (B, H, N, d), codes, dev)
+    _check("attn_fwd_mx k8", k8, (B, H, N, d), codes, dev)
+    _check("attn_fwd_mx q_scale", q_scale, (B, H, N, d // 32), (torch.uint8,), dev)
+    _check("attn_fwd_mx k_scale", k_scale, (B, H, N, d // 32), (torch.uint8,), dev)
+    _check("attn_fwd_mx v", v, (B, H, N, d), (torch.bfloat16,), dev)
+    _check("attn_fwd_mx o", o, (B, H, N, d), (torch.bfloat16,), dev)
+    _check("attn_fwd_mx lse", lse, (B, H, N), (torch.float32,), dev)
     rc = lib().attn_fwd_mx(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(v), _ptr(o),
                            _ptr(lse), B, H, N, d, int(bool(causal)), float(scale),
                            _stream_handle(stream))
@@ -206,6 +261,9 @@ def attn_softmax_rows(x, y, stream=None) -> None:
     _check_contig(x, y)
     if x.shape != y.shape or x.dtype != y.dtype:
         raise ValueError("x and y must have the same shape and dtype")
+    _check("attn_softmax_rows y", y, x.shape, (x.dtype,), x.device)
+    if x.device.type != "cuda":
+        raise ValueError(f"attn_softmax_rows: tensor on {x.device}, expected a GPU tensor")
     N = int(x.shape[-1]) if x.dim() > 0 else 1
     M = x.numel() // max(N, 1)
     rc = lib().attn_softmax_rows(_ptr(x), _ptr(y), M, N, _dtype_code(x), _stream_handle(stream))
