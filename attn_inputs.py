@@ -61,8 +61,12 @@ WORKLOADS = {
 HEADLINE = "b4_h16_n4096_d128_causal"
 
 # The headline shape at the other head dimensions the kernels take (forward
-# and backward; d = 256 forward only); the pages fix no workload for them.
+# and backward; d = 256 forward only), and at a length that is a multiple of
+# neither tile (4001 = 31 * 128 + 33 queries, 62 * 64 + 33 keys: tail tiles
+# on both loops); the pages fix no workload for them.
 HEADDIM_WORKLOADS = {
+    "b4_h16_n4001_d128_causal": Workload("b4_h16_n4001_d128_causal", 4, 16, 4001, 128,
+                                         torch.bfloat16, True, 13, backward=True),
     "b4_h16_n4096_d256_causal": Workload("b4_h16_n4096_d256_causal", 4, 16, 4096, 256,
                                          torch.bfloat16, True, 11),
     "b4_h16_n4096_d96_causal": Workload("b4_h16_n4096_d96_causal", 4, 16, 4096, 96,

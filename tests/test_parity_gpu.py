@@ -3,9 +3,10 @@ same seeded inputs.  Every test here needs an MI355X and the built library.
 
 Coverage:
 * the five workloads at their real shapes (full oracle where it finishes in
-  seconds, sampled query rows at the large shapes; the backward workload on
-  two full heads), and the B4 H16 N4096 causal shape at d = 96, 32 and 256
-  (forward only at 256);
+  seconds, sampled query rows at the large shapes; the backward on whole heads
+  of the backward workload and of the headline shape), the B4 H16 N4096 causal
+  shape at d = 96, 32 and 256 (forward only at 256), and B4 H16 N4001 d128
+  causal (tail tiles on both loops, forward and backward);
 * ragged N (tails that span several tiles), N = 1, both masks,
   d = 32 / 64 / 96 / 128 / 256 (forward, fp32 and bf16) and d <= 128
   (backward);
@@ -112,6 +113,7 @@ def test_forward_is_deterministic():
     ("b4_h16_n4096_d96_causal", [(0, 0), (3, 15)]),
     ("b4_h16_n4096_d32_causal", [(0, 0), (2, 9)]),
     ("b4_h16_n4096_d256_causal", [(0, 0), (3, 12)]),
+    ("b4_h16_n4001_d128_causal", [(0, 0), (3, 15)]),
 ])
 def test_full_size_forward_sampled_rows(name, heads):
     w = {**WORKLOADS, **HEADDIM_WORKLOADS}[name]
@@ -129,13 +131,15 @@ def test_full_size_forward_sampled_rows(name, heads):
 
 @pytest.mark.parametrize("name,heads", [
     ("b2_h16_n4096_d64_causal_fwdbwd", [(0, 0), (1, 11)]),
+    ("b4_h16_n4096_d128_causal", [(3, 14)]),
+    ("b4_h16_n4001_d128_causal", [(1, 6)]),
     ("b4_h16_n4096_d96_causal", [(2, 5)]),
     ("b4_h16_n4096_d32_causal", [(1, 3)]),
 ])
 def test_fwdbwd_workload_backward(name, heads):
     w = {**WORKLOADS, **HEADDIM_WORKLOADS}[name]
     log(f"[bwd] {w.name}: generating inputs")
-    q, k, v, do = workload_inputs(w)
+    q, k, v, do = workload_inputs(w, with_dout=True)
     o, lse = gpu_forward(q, k, v, w.causal, w.scale)
     dq, dk, dv = gpu_backward(q, k, v, o, lse, do, w.causal, w.scale)
     for t in (dq, dk, dv):
