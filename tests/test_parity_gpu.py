@@ -12,7 +12,8 @@ Coverage:
   (backward);
 * closed forms with exactly representable inputs (Q = 0);
 * the dV / dK sum invariants of the backward at full size;
-* determinism of the forward.
+* determinism of the forward;
+* a long sequence (N = 65573, both masks) on sampled rows.
 """
 import numpy as np
 import pytest
@@ -182,3 +183,21 @@ def test_binding_refuses_mismatched_tensors():
         T.attn_bwd(q, q, q, q, q, lse, g[0], short, g[2], ws, True, 0.125)
     with pytest.raises(ValueError):
         T.attn_fwd_kv(q, short, q, torch.empty_like(q), lse, False, 0.125, 0, None)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_long_sequence_forward_sampled_rows(causal):
+    """N = 65573 (ragged, 513 query tiles per head): row, tile and workgroup
+    indices far beyond the workload sizes; sampled rows against the oracle."""
+    N, d = 65573, 128
+    q, k, v = make_inputs(1, 2, N, d, torch.bfloat16, seed=21)
+    scale = d ** -0.5
+    log(f"[fwd] long sequence N={N} d={d} causal={causal}")
+    o, lse = gpu_forward(q, k, v, causal, scale)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    for h in (0, 1):
+        rows = sample_rows(N, 48, seed=31 + h)
+        o_ref, l_ref = oracle_rows_fwd(q, k, v, causal, scale, 0, h, rows)
+        eo = compare(to_np(o[0, h])[rows], o_ref, torch.bfloat16, f"N={N} O h{h}")
+        el = compare(to_np(lse[0, h])[rows], l_ref, torch.bfloat16, f"N={N} lse h{h}")
+        log(f"    h{h} O {describe(eo)} | lse {describe(el)}")

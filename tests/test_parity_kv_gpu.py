@@ -6,7 +6,7 @@ Coverage: decode (Nq = 1) and chunked prefill shapes, key counts that are not
 tile multiples, Nq = Nk, Nq > 128 (several query tiles), both masks,
 d = 32, 64, 96, 128 and 256, automatic and explicit split counts (including more splits than
 tiles, which the library caps), the decode workload at full size, agreement
-with attn_fwd when Nq = Nk, and bitwise determinism.
+with attn_fwd when Nq = Nk, a 131077-key cache, and bitwise determinism.
 """
 import numpy as np
 import pytest
@@ -105,3 +105,10 @@ def test_deterministic():
     o1, l1 = gpu_forward_kv(q, k, v, True, 128 ** -0.5, 0)
     o2, l2 = gpu_forward_kv(q, k, v, True, 128 ** -0.5, 0)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_long_cache(causal):
+    """One query against a 131077-key cache (2049 key tiles, many splits)."""
+    q, k, v = make_kv_inputs(1, 2, 1, 131077, 128, seed=41)
+    _check(q, k, v, causal, 0, "decode Nk=131077 d=128")
