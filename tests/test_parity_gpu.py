@@ -13,7 +13,8 @@ Coverage:
 * closed forms with exactly representable inputs (Q = 0);
 * the dV / dK sum invariants of the backward at full size;
 * determinism of the forward;
-* a long sequence (N = 65573, both masks) on sampled rows.
+* a long sequence (N = 65573, both masks) on sampled rows;
+* many heads (B = 6, H = 37) of a short sequence, forward and backward.
 """
 import numpy as np
 import pytest
@@ -80,6 +81,21 @@ def test_ragged_backward(N, d, causal):
     ref = oracle.attn_bwd(to_np(q), to_np(k), to_np(v), to_np(do), causal, f32_scale(scale))
     for name, got in (("dq", dq), ("dk", dk), ("dv", dv)):
         e = compare(to_np(got), ref[name], torch.bfloat16, f"ragged bwd {name}")
+        log(f"    {name} {describe(e)}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_many_heads(d, causal):
+    """222 heads (B*H not a multiple of the 8 XCDs the grid is dealt over) of
+    33 queries: the workgroup -> (head, tile) mapping on a wide, shallow grid."""
+    q, k, v, do = make_inputs(6, 37, 33, d, torch.bfloat16, seed=300 + d, with_dout=True)
+    scale = d ** -0.5
+    o, lse = _fwd_full_check(q, k, v, causal, scale, torch.bfloat16, f"many heads d={d}")
+    dq, dk, dv = gpu_backward(q, k, v, o, lse, do, causal, scale)
+    ref = oracle.attn_bwd(to_np(q), to_np(k), to_np(v), to_np(do), causal, f32_scale(scale))
+    for name, got in (("dq", dq), ("dk", dk), ("dv", dv)):
+        e = compare(to_np(got), ref[name], torch.bfloat16, f"many heads bwd {name}")
         log(f"    {name} {describe(e)}")
 
 
