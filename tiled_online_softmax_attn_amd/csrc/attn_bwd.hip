@@ -75,8 +75,10 @@ bwd_preprocess_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ d
 constexpr int kKvBK = 128;  // keys per workgroup (32 per wave)
 constexpr int kKvBQ = 64;   // queries per inner step (one SwzTile)
 
+// d <= 64 fits two waves per SIMD (256 registers each, a shorter operand
+// ring below); d = 96 and 128 need one wave's whole register file.
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(kBwdThreads, 1)
+__global__ void __launch_bounds__(kBwdThreads, D <= 64 ? 2 : 1)
 bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 const __bf16* __restrict__ v, const __bf16* __restrict__ dout,
                 const float* __restrict__ lse, const float* __restrict__ delta,
@@ -284,10 +286,11 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       // The tile is one sequence of steps g: KS row steps of block 0 (A), KS
       // of block 1 (B), 2*DB transposed steps of block 0 (C) and of block 1
       // (D).  Both kinds read two bf16x8 fragments, so one ring of registers
-      // holds the fragments of the next kPrefetch steps.
+      // holds the fragments of the next kPrefetch steps (two at d <= 64, where
+      // the second wave of the SIMD also hides LDS latency).
       constexpr int US = 2 * DB;
       constexpr int NSTEPS = 2 * KS + 2 * US;
-      constexpr int kPrefetch = 3;
+      constexpr int kPrefetch = D <= 64 ? 2 : 3;
       auto read_step = [&](int g) {
         if (g < KS) { const RowFrag f = read_row(0, g); return TrFrag{f.q, f.d}; }
         if (g < 2 * KS) { const RowFrag f = read_row(1, g - KS); return TrFrag{f.q, f.d}; }
