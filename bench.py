@@ -282,8 +282,8 @@ def cpu_baseline_all(budget_s: float) -> int:
     """The oracle on a bounded sample (whole heads, about budget_s seconds) of
     each attention workload: forward, plus the backward where the workload
     has one; one JSON line each."""
-    from attn_inputs import WORKLOADS, workload_inputs
-    for w in WORKLOADS.values():
+    from attn_inputs import HEADDIM_WORKLOADS, WORKLOADS, workload_inputs
+    for w in [*WORKLOADS.values(), *HEADDIM_WORKLOADS.values()]:
         eprint(f"[cpu_baseline] {w.name}")
         q, k, v, do = workload_inputs(w, with_dout=True)
         res = cpu_baseline(w, q, k, v, do, budget_s, backward=w.backward)
