@@ -50,6 +50,7 @@ KERNEL_SOURCES = {"fwd": "attn_fwd.hip", "bwd_preprocess": "attn_bwd.hip",
                   "bwd_dkdv": "attn_bwd.hip", "bwd_dq": "attn_bwd.hip",
                   "softmax_rows": "softmax_rows.hip"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+PROBE_LIB = os.path.join(ROOT, "tiled_online_softmax_attn_amd", "libattn_probe.so")
 
 
 def eprint(*a):
@@ -97,6 +98,88 @@ def algorithmic(w, kernel: str):
     return BHN * w.d * 2 * 2 + BHN * 4, "byte", "hbm"
 
 
+def measure_peaks(full: bool = False) -> dict:
+    """Measured ceilings (libattn_probe.so, include/attn_probe.h): the dense
+    bf16 MFMA rate with nothing else in the loop and with one or two groups
+    of the softmax's per-score VALU work (FMA, exponential, add) per MFMA,
+    the shader clock under that load, the v_exp_f32 rate, and a plain HBM
+    copy.  Each probe is timed with HIP events on the stream it runs on;
+    the best of `reps` launches is kept (the ceiling, not the average)."""
+    import ctypes
+
+    import torch
+    if not os.path.exists(PROBE_LIB):
+        raise RuntimeError(f"{PROBE_LIB} is not built")
+    L = ctypes.CDLL(PROBE_LIB)
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    L.attn_probe_mfma.argtypes = [vp, vp, i, i, i, vp]
+    L.attn_probe_exp.argtypes = [vp, vp, i, i, vp]
+    L.attn_probe_copy.argtypes = [vp, vp, ctypes.c_longlong, vp]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    blocks = 1024  # 4 workgroups of 4 waves per CU: 4 waves per SIMD
+    out = torch.empty(blocks * 256, device=dev)
+    clk = torch.zeros(blocks * 2, device=dev, dtype=torch.int64)
+    reps = 7 if full else 3
+
+    def timed(launch):
+        best = None
+        for _ in range(reps + 1):  # the first launch warms up
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            rc = launch()
+            e1.record(stream)
+            if rc != 0:
+                raise RuntimeError(f"probe launch failed: {rc}")
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None or ms < best else best
+        return best
+
+    def clock_ghz():
+        c = clk.view(blocks, 2).double().cpu()
+        ok = c[:, 1] > 0
+        ghz = (c[ok, 0] / (c[ok, 1] / 1e8) / 1e9).sort().values
+        return round(float(ghz[len(ghz) // 2]), 3)
+
+    res = {"probe_blocks": blocks}
+    iters = 20000 if full else 6000
+    for groups in (0, 1, 2):
+        ms = timed(lambda: L.attn_probe_mfma(out.data_ptr(), clk.data_ptr(), blocks, iters, groups, sh))
+        flops = blocks * 4 * iters * 4 * 32768.0
+        key = "mfma_bf16" if groups == 0 else f"mfma_bf16_softmax{groups}"
+        res[f"{key}_tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
+        res[f"{key}_clock_ghz"] = clock_ghz()
+    eiters = 8000 if full else 3000
+    ms = timed(lambda: L.attn_probe_exp(out.data_ptr(), clk.data_ptr(), blocks, eiters, sh))
+    exps = blocks * 256 * eiters * 8.0
+    ghz = clock_ghz()
+    res["exp_per_s"] = float(f"{exps / (ms * 1e-3):.4g}")
+    res["exp_clock_ghz"] = ghz
+    # wave64 v_exp_f32 instructions per SIMD per cycle -> cycles per instruction
+    res["exp_cycles_per_wave_instr"] = round(ghz * 1e9 / (exps / (ms * 1e-3) / 64 / 1024), 2)
+    nbytes = (1 << 30) if full else (512 << 20)
+    src = torch.ones(nbytes // 4, device=dev)
+    dst = torch.empty_like(src)
+    ms = timed(lambda: L.attn_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, sh))
+    res["hbm_copy_gbs"] = round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
+    res["hbm_copy_bytes"] = 2 * nbytes
+    del src, dst
+    return res
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, q, k, v, do, budget_s: float, backward: bool = True):
     import numpy as np
 
@@ -121,10 +204,44 @@ def cpu_baseline(w, q, k, v, do, budget_s: float, backward: bool = True):
         break
     el = time.perf_counter() - t0
     return {"value": per_head * heads / el / 1e12, "unit": "TFLOP/s",
-            "cores": oracle.num_threads(lib), "kind": "oracle",
+            "cores": oracle.num_threads(lib), "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{heads} of {w.B * w.H} heads of {w.name} (fp64 forward"
                       f"{' + backward' if backward else ''} per head, S and P materialised), "
                       f"{el:.1f} s"}
+
+
+def cpu_baseline_single_thread(budget_s: float) -> dict:
+    """The oracle's forward on one host thread, for the two small workloads
+    (fp32 B1 H1 N256 d64 and bf16 B1 H8 N1024 d64), whole heads for at most
+    budget_s seconds each: GFLOP/s by the same formula as the GPU."""
+    import numpy as np
+
+    import oracle
+    from attn_inputs import WORKLOADS, workload_inputs
+    lib = oracle.load()
+    prev = oracle.num_threads(lib)
+    oracle.set_num_threads(1, lib=lib)
+    out = {}
+    try:
+        for name in ("single_head_f32", "h8_n1024_d64"):
+            w = WORKLOADS[name]
+            q, k, v = workload_inputs(w, with_dout=False)
+            scale = float(np.float32(w.scale))
+            f64 = lambda t: t.to("cpu").double().numpy()
+            heads, t0 = 0, time.perf_counter()
+            for h in range(w.B * w.H):
+                b, hh = divmod(h, w.H)
+                oracle.attn_fwd(f64(q[b, hh]), f64(k[b, hh]), f64(v[b, hh]), w.causal, scale,
+                                lib=lib)
+                heads += 1
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+            el = time.perf_counter() - t0
+            out[name] = {"gflops": round(w.fwd_flops() / (w.B * w.H) * heads / el / 1e9, 3),
+                         "heads": heads, "seconds": round(el, 3)}
+    finally:
+        oracle.set_num_threads(prev, lib=lib)
+    return out
 
 
 def kernel_key(name: str):
@@ -472,6 +589,11 @@ def main():
     ap.add_argument("--copy-mib", type=float, default=0.0,
                     help="run one plain device copy of this many MiB before timing "
                          "(reference kernel for the HBM byte counters)")
+    ap.add_argument("--peak", action="store_true",
+                    help="measure the chip's ceilings (MFMA rate alone and with the softmax's "
+                         "VALU work, shader clock, v_exp_f32 rate, HBM copy) and print them")
+    ap.add_argument("--no-peak", action="store_true",
+                    help="leave the measured ceilings out of the report line")
     ap.add_argument("--pmc-summary", nargs="+", default=None, metavar="DIR",
                     help="summarise rocprofv3 FETCH_SIZE/WRITE_SIZE passes into "
                          "profiles/traffic.json and exit (needs --copy-mib of the profiled run)")
@@ -498,6 +620,12 @@ def main():
     if not torch.cuda.is_available():
         eprint("bench.py needs a GPU")
         sys.exit(1)
+    if args.peak:
+        eprint("[bench] measuring the chip's ceilings")
+        print(json.dumps({"peak_measured": measure_peaks(full=True),
+                          "peak_nominal": {"mfma_bf16_tflops": PEAK_BF16_TFLOPS,
+                                           "hbm_gbs": PEAK_HBM_GBS}}), flush=True)
+        return
     if args.workload in KV_WORKLOADS:
         bench_kv(args, KV_WORKLOADS[args.workload])
         return
@@ -581,16 +709,35 @@ def main():
                        "min_ms": round(srt[0], 5), "bound": bound, "achieved": round(achieved, 2),
                        "peak": peak, "unit": u, "frac": round(achieved / peak, 4),
                        "traffic": measured_traffic(kn, w.name)}
+        if kn == "bwd_dq":
+            # of dQ's three block products only dQ = dS K is the method's
+            # work (S and dP are recomputed): its rate counted that way
+            algo = w.fwd_flops() / 2 / (avg_ms * 1e-3) / 1e12
+            kernels[kn]["achieved_algorithmic"] = round(algo, 2)
+            kernels[kn]["frac_algorithmic"] = round(algo / PEAK_BF16_TFLOPS, 4)
     dominant = max(run_kernels, key=lambda kn: per_kernel_ms[kn])
     dk_ = kernels[dominant]
     roofline = {"kernel": dominant, "bound": dk_["bound"], "achieved": dk_["achieved"],
                 "peak": dk_["peak"], "unit": dk_["unit"], "frac": dk_["frac"],
                 "traffic": dk_["traffic"]}
 
+    peaks = None
+    if not args.no_peak:
+        eprint("[bench] measuring the chip's ceilings (after the timed region)")
+        peaks = measure_peaks(full=False)
+        if roofline["unit"] == "TFLOP/s":
+            roofline["peak_measured"] = peaks["mfma_bf16_tflops"]
+            roofline["frac_of_measured"] = round(roofline["achieved"] / peaks["mfma_bf16_tflops"], 4)
+        else:
+            roofline["peak_measured"] = peaks["hbm_copy_gbs"]
+            roofline["frac_of_measured"] = round(roofline["achieved"] / peaks["hbm_copy_gbs"], 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         eprint("[bench] timing the oracle on the host")
         cpu = cpu_baseline(w, q, k, v, do, args.cpu_baseline_seconds, backward)
+        if w.name == HEADLINE:
+            cpu["single_thread_small_workloads"] = cpu_baseline_single_thread(3.0)
 
     fwd_ms = kernels["fwd"]["avg_ms"]
     bwd_ms = sum(kernels[kn]["avg_ms"] for kn in run_kernels[1:])
@@ -619,6 +766,7 @@ def main():
         "event_ms_per_step": round(event_total_ms / args.steps, 4),
         "roofline": roofline,
         "kernels": kernels,
+        "peak_measured": peaks,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

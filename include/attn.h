@@ -22,7 +22,11 @@
  *   float32 [B][H][N].  Element type is given by `dtype`; lse is always fp32.
  * - Q, K and V all have the same N (self-attention).  `causal` != 0 hides key
  *   j from query i when j > i (the diagonal is visible).  `scale` multiplies
- *   Q K^T before the softmax; pass 1/sqrt(d) for the usual scaling.
+ *   Q K^T before the softmax.  The pages scale by 1/sqrt(d) (CS336 L5 notes
+ *   sections 8.1 and 8.3; PDC notes Lecture 4, section 4.8), a positive
+ *   number, and the kernels are built for a positive scale: it must be finite
+ *   and > 0, otherwise ATTN_ERR_SCALE (0, -0.0 and negative values included).
+ *   Results are finite as long as scale * |q_i . k_j| fits fp32.
  * - N may be any value >= 1 (no tile multiple is required); d must be 32, 64,
  *   96, 128 or 256 (the backward: 32, 64, 96 or 128).  bf16 is supported by
  *   every entry point; fp32 by the forward only.
@@ -33,7 +37,8 @@
  *   kernel surface at that synchronisation, not in the return code.
  * - Arguments are validated on the host before anything is enqueued; on a
  *   non-zero return nothing was written.  Outputs must not alias inputs.
- * - All pointers must be 16-byte aligned (the kernels use 128-bit accesses).
+ * - Tensor pointers must be 16-byte aligned (the kernels use 128-bit
+ *   accesses); lse, read and written one float at a time, 4-byte aligned.
  * - Calls are thread-safe: the library keeps no per-call global state.
  */
 #ifndef ATTN_H_
@@ -58,8 +63,8 @@ typedef enum {
   ATTN_ERR_SHAPE = -2,     /* B, H or N < 1, or sizes overflow 64-bit offsets */
   ATTN_ERR_DTYPE = -3,     /* unknown dtype, or dtype not supported by this entry point */
   ATTN_ERR_HEADDIM = -4,   /* d is not 32, 64, 96, 128 or 256 (backward: <= 128) */
-  ATTN_ERR_ALIGN = -5,     /* a pointer is not 16-byte aligned */
-  ATTN_ERR_SCALE = -6,     /* scale is not finite */
+  ATTN_ERR_ALIGN = -5,     /* a pointer is not 16-byte aligned (lse: 4-byte) */
+  ATTN_ERR_SCALE = -6,     /* scale is not finite, or not > 0 */
   ATTN_ERR_WORKSPACE = -7, /* workspace NULL or smaller than attn_bwd_workspace_bytes() */
   ATTN_ERR_HIP = -8        /* the HIP runtime refused a launch */
 } attn_status_t;

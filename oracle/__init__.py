@@ -79,6 +79,8 @@ def _declare(lib):
     i64 = ctypes.c_int64
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
+    lib.oracle_set_num_threads.restype = None
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
     lib.oracle_softmax_row.restype = ctypes.c_int
     lib.oracle_softmax_row.argtypes = [_DP, i64, _DP, _DP, _DP]
     lib.oracle_attn_fwd_head.restype = ctypes.c_int
@@ -119,6 +121,11 @@ def _check(rc: int, what: str):
 
 def num_threads(lib=None) -> int:
     return int((lib or load()).oracle_num_threads())
+
+
+def set_num_threads(n: int, lib=None) -> None:
+    """Threads of later calls (for timing); results do not depend on it."""
+    (lib or load()).oracle_set_num_threads(int(n))
 
 
 def softmax_row(x, lib=None):

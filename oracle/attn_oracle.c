@@ -53,6 +53,15 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Thread count of later calls (timing on one thread); no effect on results. */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* Safe softmax of one row (CS149 L9 notes section 8; PDC notes 4.13.2):
  * m = max x, f = exp(x - m), l = sum f, p = f / l.  Entries equal to -inf
  * (masked) get p = 0.  At least one entry must be finite. */

@@ -35,8 +35,9 @@ def to_np(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu").to(torch.float64).numpy()
 
 
-def compare(gpu, ref, dtype: torch.dtype, what: str) -> dict:
-    """Assert the stated tolerance; return the error summary."""
+def compare(gpu, ref, dtype: torch.dtype, what: str, extra=None) -> dict:
+    """Assert the stated tolerance (plus an elementwise rounding bound
+    ``extra`` where one is derived for the case); return the error summary."""
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert gpu.shape == ref.shape, f"{what}: shape {gpu.shape} vs {ref.shape}"
@@ -48,10 +49,43 @@ def compare(gpu, ref, dtype: torch.dtype, what: str) -> dict:
         assert max_abs <= F32_ATOL, f"{what}: max abs err {max_abs:.3e} > {F32_ATOL}"
     else:
         bound = BF16_ATOL + BF16_RTOL * np.abs(ref)
+        if extra is not None:
+            bound = bound + np.asarray(extra, dtype=np.float64)
         bad = err > bound
         assert not bad.any(), (f"{what}: {int(bad.sum())} of {err.size} elements outside "
                                f"2e-2 + 1e-2|ref| (max abs {max_abs:.3e})")
     return {"max_abs": max_abs, "max_rel": max_rel}
+
+
+BF16_U = 2.0 ** -8  # unit roundoff of bf16 (8 significant bits, round to nearest)
+
+
+def bwd_rounding_bound(q, k, v, dout, causal, scale) -> dict:
+    """Elementwise bound on what the bf16 rounding points of the backward add
+    to dQ, dK and dV, from the oracle's fp64 P (one head, [N, d] inputs).
+
+    The kernels round four quantities to bf16 (u = 2^-8 relative each): O
+    in the forward, which also carries the rounding of P before P V, so
+    D_i = sum_k dO_ik O_ik is off by at most
+        dD_i = 2u sum_k |dO_ik| (P |V|)_ik;
+    dS = P (dP - D) before dQ and dK; and P before dV.  With everything else
+    in fp32,
+        |ddQ| <= scale (dD (P |K|) + u |dS| |K|)
+        |ddK| <= scale (P^T (dD |Q|) + u |dS|^T |Q|)
+        |ddV| <= u P^T |dO|.
+    At scale 1/sqrt(d) this stays inside the stated 2e-2 + 1e-2 |ref|; it
+    grows with the scale (scale 1.0 makes the logits sqrt(d) times larger)."""
+    Q, K, V, dO = (np.asarray(to_np(t) if hasattr(t, "detach") else t, dtype=np.float64)
+                   for t in (q, k, v, dout))
+    sc = f32_scale(scale)
+    _, _, P = oracle.attn_fwd(Q, K, V, causal, sc, return_p=True)
+    O = P @ V
+    dS = P * (dO @ V.T - (dO * O).sum(1)[:, None])
+    u = BF16_U
+    dD = 2 * u * (np.abs(dO) * (P @ np.abs(V))).sum(1)
+    return {"dq": sc * (dD[:, None] * (P @ np.abs(K)) + u * np.abs(dS) @ np.abs(K)),
+            "dk": sc * (P.T @ (dD[:, None] * np.abs(Q)) + u * np.abs(dS).T @ np.abs(Q)),
+            "dv": u * P.T @ np.abs(dO)}
 
 
 def gpu_forward(q, k, v, causal, scale):
@@ -103,7 +137,7 @@ def describe(err: dict) -> str:
     return f"max_abs={err['max_abs']:.3e} max_rel={err['max_rel']:.3e}"
 
 
-__all__ = ["compare", "gpu_forward", "gpu_backward", "sample_rows", "oracle_full_fwd",
+__all__ = ["compare", "bwd_rounding_bound", "gpu_forward", "gpu_backward", "sample_rows", "oracle_full_fwd",
            "oracle_rows_fwd", "to_np", "f32_scale", "log", "describe", "math"]
 
 

@@ -10,11 +10,37 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
 
 
-def declared_functions():
-    text = open(HEADER).read()
+PROBE_HEADER = os.path.join(ROOT, "include", "attn_probe.h")
+PROBE_LIB = os.path.join(ROOT, "tiled_online_softmax_attn_amd", "libattn_probe.so")
+
+
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\**\s+\**(attn_[a-z_0-9]+)\s*\(",
                                  text, flags=re.M)))
+
+
+def test_every_header_is_covered():
+    """include/ holds the two C ABIs checked below and nothing else."""
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == ["attn.h", "attn_probe.h"]
+
+
+def test_probe_library_exports_every_declared_symbol():
+    names = declared_functions(PROBE_HEADER)
+    assert names == ["attn_probe_copy", "attn_probe_exp", "attn_probe_mfma"]
+    if not os.path.exists(PROBE_LIB):
+        pytest.skip("libattn_probe.so not built (run __graft_entry__.build())")
+    lib = ctypes.CDLL(PROBE_LIB)
+    for name in names:
+        assert hasattr(lib, name), f"libattn_probe.so does not export {name}"
+    # argument checks return before any launch
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    lib.attn_probe_mfma.argtypes = [vp, vp, i, i, i, vp]
+    lib.attn_probe_copy.argtypes = [vp, vp, ctypes.c_longlong, vp]
+    assert lib.attn_probe_mfma(None, None, 1, 1, 0, None) != 0
+    assert lib.attn_probe_mfma(FAKE, FAKE, 1, 1, 3, None) != 0
+    assert lib.attn_probe_copy(FAKE, FAKE, 24, None) != 0
 
 
 def _lib():
@@ -69,8 +95,14 @@ FAKE = 1 << 20  # a 16-byte aligned non-null address, never dereferenced on erro
     (dict(B=0), -2), (dict(H=-1), -2), (dict(N=0), -2),
     (dict(d=80), -4), (dict(d=16), -4), (dict(d=512), -4), (dict(d=0), -4),
     (dict(dtype=7), -3),
-    (dict(q=FAKE + 8), -5), (dict(o=FAKE + 2), -5),
+    (dict(q=FAKE + 8), -5), (dict(o=FAKE + 2), -5), (dict(lse=FAKE + 2), -5),
     (dict(scale=float("inf")), -6), (dict(scale=float("nan")), -6),
+    # the scale must be > 0: zero, negative zero and negative scales are refused
+    (dict(scale=0.0), -6), (dict(scale=-0.0), -6), (dict(scale=-0.125), -6),
+    (dict(scale=-1e-30), -6),
+    # lse needs 4-byte alignment only: this call passes the alignment check and
+    # stops at the (later) scale check, so nothing is launched
+    (dict(lse=FAKE + 4, scale=0.0), -6),
 ])
 def test_fwd_validation(args, code):
     lib = _lib()
@@ -85,7 +117,9 @@ def test_fwd_validation(args, code):
 @pytest.mark.parametrize("args,code", [
     (dict(dout=0), -1), (dict(dtype=0), -3), (dict(N=0), -2), (dict(d=80), -4), (dict(d=256), -4),
     (dict(ws=0), -7), (dict(ws_bytes=16), -7), (dict(dk=FAKE + 4), -5),
-    (dict(scale=float("-inf")), -6),
+    (dict(lse=FAKE + 2), -5),
+    (dict(scale=float("-inf")), -6), (dict(scale=0.0), -6), (dict(scale=-0.0), -6),
+    (dict(scale=-0.5), -6), (dict(lse=FAKE + 4, scale=-0.0), -6),
 ])
 def test_bwd_validation(args, code):
     lib = _lib()
@@ -138,7 +172,9 @@ def test_kv_workspace_size():
     (dict(B=0), -2), (dict(Nq=0), -2), (dict(Nk=0), -2), (dict(splits=-1), -2),
     (dict(Nq=20, Nk=10, causal=1), -2),
     (dict(d=48), -4), (dict(dtype=0), -3), (dict(dtype=5), -3),
-    (dict(k=FAKE + 4), -5), (dict(scale=float("nan")), -6),
+    (dict(k=FAKE + 4), -5), (dict(lse=FAKE + 1), -5), (dict(scale=float("nan")), -6),
+    (dict(scale=0.0), -6), (dict(scale=-0.0), -6), (dict(scale=-2.0), -6),
+    (dict(lse=FAKE + 4, scale=0.0), -6),
     (dict(ws=0), -7), (dict(ws_bytes=8), -7), (dict(ws=FAKE + 8), -5),
 ])
 def test_kv_validation(args, code):
@@ -155,6 +191,9 @@ def test_kv_validation(args, code):
 @pytest.mark.parametrize("args,code", [
     (dict(x=0), -1), (dict(y=0), -1), (dict(M=0), -2), (dict(N=0), -2), (dict(M=(1 << 40) + 1), -2),
     (dict(M=1 << 30, N=1 << 20), -2),
+    # M * N = 2^63 overflows a 64-bit product: refused, not wrapped negative
+    (dict(M=1 << 40, N=1 << 23), -2), (dict(M=1 << 40, N=(1 << 31) - 1), -2),
+    (dict(M=(1 << 40) - 1, N=1 << 24), -2),
     (dict(dtype=2), -3), (dict(x=FAKE + 4), -5), (dict(y=FAKE + 2), -5),
 ])
 def test_softmax_rows_validation(args, code):
@@ -168,7 +207,9 @@ def test_softmax_rows_validation(args, code):
 @pytest.mark.parametrize("args,code", [
     (dict(q8=0), -1), (dict(k_scale=0), -1), (dict(N=0), -2), (dict(d=96), -4), (dict(d=256), -4),
     (dict(q8=FAKE + 8), -5), (dict(q_scale=FAKE + 2), -5), (dict(d=64, k_scale=FAKE + 1), -5),
-    (dict(scale=float("nan")), -6),
+    (dict(lse=FAKE + 2), -5),
+    (dict(scale=float("nan")), -6), (dict(scale=0.0), -6), (dict(scale=-0.0), -6),
+    (dict(scale=-0.1), -6), (dict(lse=FAKE + 4, scale=0.0), -6),
 ])
 def test_fwd_mx_validation(args, code):
     lib = _lib()

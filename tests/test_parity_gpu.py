@@ -12,7 +12,9 @@ Coverage:
   (backward);
 * closed forms with exactly representable inputs (Q = 0);
 * the dV / dK sum invariants of the backward at full size;
-* determinism of the forward;
+* scales other than 1/sqrt(d) (1.0 and 0.02) on causal and unmasked ragged
+  shapes, forward (bf16 and fp32) and backward;
+* determinism of the forward and of the backward; lse at a 4-byte offset;
 * a long sequence (N = 65573, both masks) on sampled rows;
 * many heads (B = 6, H = 37) of a short sequence, forward and backward.
 """
@@ -22,7 +24,8 @@ import torch
 
 import oracle
 from attn_inputs import HEADDIM_WORKLOADS, WORKLOADS, make_inputs, workload_inputs
-from tests.parity import (compare, describe, f32_scale, gpu_backward, gpu_forward, log,
+from tests.parity import (bwd_rounding_bound, compare, describe, f32_scale, gpu_backward,
+                          gpu_forward, log,
                           oracle_full_fwd, oracle_rows_fwd, sample_rows, to_np)
 
 pytestmark = pytest.mark.gpu
@@ -114,12 +117,101 @@ def test_q_zero_closed_form():
             compare(to_np(lse)[0, 0], want_l, dtype, "Q=0 lse")
 
 
+# ------------------------------------------------------------ scales other than 1/sqrt(d)
+# The contract is any finite scale > 0.  A larger scale makes the rows peaky
+# (scale 1.0 at d = 128: logits of standard deviation ~11, so the lazy
+# reference maximum moves within a tile), a small one flat (0.02: nearly
+# uniform rows).  Causal ragged shapes put masked keys in the first tile
+# and a tail in the last one.
+@pytest.mark.parametrize("scale", [1.0, 0.02])
+@pytest.mark.parametrize("N,d", [(100, 32), (257, 64), (255, 96), (1000, 128), (300, 256)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_forward_other_scales_bf16(scale, N, d, causal):
+    q, k, v = make_inputs(1, 2, N, d, torch.bfloat16, seed=400 + N + d)
+    _fwd_full_check(q, k, v, causal, scale, torch.bfloat16, f"scale={scale} N={N} d={d}")
+
+
+# fp32: the 1e-5 bound on O and lse is kept; at scale 1.0 the logits and lse
+# grow with sqrt(d) and so does their fp32 rounding, so the larger head
+# dimensions are taken at the small scale only.
+@pytest.mark.parametrize("scale,N,d", [(1.0, 100, 32), (1.0, 257, 64), (0.02, 255, 96),
+                                       (0.02, 1000, 128), (0.02, 300, 256)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_forward_other_scales_f32(scale, N, d, causal):
+    q, k, v = make_inputs(1, 2, N, d, torch.float32, seed=450 + N + d)
+    _fwd_full_check(q, k, v, causal, scale, torch.float32, f"f32 scale={scale} N={N} d={d}")
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.02])
+@pytest.mark.parametrize("N,d", [(100, 32), (257, 64), (255, 96), (300, 128)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_other_scales(scale, N, d, causal):
+    q, k, v, do = make_inputs(1, 2, N, d, torch.bfloat16, seed=500 + N + d, with_dout=True)
+    log(f"[bwd] scale={scale} N={N} d={d} causal={causal}")
+    o, lse = gpu_forward(q, k, v, causal, scale)
+    dq, dk, dv = gpu_backward(q, k, v, o, lse, do, causal, scale)
+    ref = oracle.attn_bwd(to_np(q), to_np(k), to_np(v), to_np(do), causal, f32_scale(scale))
+    # beyond 1/sqrt(d) the bf16 rounding of O, P and dS is amplified by the
+    # scale: the stated tolerance plus the bound those rounding points give
+    for h in range(q.shape[1]):
+        bnd = bwd_rounding_bound(q[0, h], k[0, h], v[0, h], do[0, h], causal, scale)
+        for name, got in (("dq", dq), ("dk", dk), ("dv", dv)):
+            e = compare(to_np(got[0, h]), ref[name][0, h], torch.bfloat16,
+                        f"scale={scale} bwd {name} h{h}", extra=bnd[name])
+            log(f"    {name} h{h} {describe(e)} (max bound {bnd[name].max():.3e})")
+
+
 def test_forward_is_deterministic():
     q, k, v = make_inputs(1, 4, 777, 128, torch.bfloat16, seed=9)
     o1, l1 = gpu_forward(q, k, v, True, 128 ** -0.5)
     o2, l2 = gpu_forward(q, k, v, True, 128 ** -0.5)
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_is_deterministic(d):
+    """attn_bwd writes every gradient element exactly once (no atomics), so
+    two calls on the same inputs and workspace agree bit for bit; d = 64 and
+    128 take the two register layouts of the dK/dV kernel."""
+    import tiled_online_softmax_attn_amd as T
+    dev = torch.device("cuda:0")
+    q, k, v, do = (t.to(dev) for t in make_inputs(2, 3, 777, d, torch.bfloat16, seed=11 + d,
+                                                   with_dout=True))
+    scale = d ** -0.5
+    o, lse = T.flash_attention_forward(q, k, v, True, scale)
+    ws = torch.empty(T.attn_bwd_workspace_bytes(2, 3, 777, d), device=dev, dtype=torch.uint8)
+    outs = []
+    for _ in range(2):
+        g = [torch.full_like(q, float("nan")) for _ in range(3)]
+        T.attn_bwd(q, k, v, o, do, lse, g[0], g[1], g[2], ws, True, scale)
+        torch.cuda.synchronize()
+        outs.append(g)
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_lse_at_4_byte_offset():
+    """lse is accessed one float at a time, so a view that starts 4 bytes
+    into a buffer is accepted and gives the same results as an aligned one."""
+    import tiled_online_softmax_attn_amd as T
+    dev = torch.device("cuda:0")
+    B, H, N, d = 1, 2, 300, 64
+    q, k, v, do = (t.to(dev) for t in make_inputs(B, H, N, d, torch.bfloat16, seed=77,
+                                                   with_dout=True))
+    o_a, lse_a = T.flash_attention_forward(q, k, v, True, 0.125)
+    buf = torch.full((B * H * N + 1,), float("nan"), device=dev)
+    lse_b = buf[1:].view(B, H, N)
+    assert lse_b.data_ptr() % 16 == 4
+    o_b = torch.empty_like(q)
+    T.attn_fwd(q, k, v, o_b, lse_b, True, 0.125)
+    torch.cuda.synchronize()
+    assert torch.equal(lse_a, lse_b) and torch.equal(o_a.view(torch.int16), o_b.view(torch.int16))
+    g_a = T.flash_attention_backward(q, k, v, o_a, lse_a, do, True, 0.125)
+    g_b = T.flash_attention_backward(q, k, v, o_b, lse_b, do, True, 0.125)
+    torch.cuda.synchronize()
+    for a, b in zip(g_a, g_b):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
 # ------------------------------------------------------------ full-size workloads

@@ -4,7 +4,7 @@ oracle_attn_fwd_rect on the same seeded inputs.
 
 Coverage: decode (Nq = 1) and chunked prefill shapes, key counts that are not
 tile multiples, Nq = Nk, Nq > 128 (several query tiles), both masks,
-d = 32, 64, 96, 128 and 256, automatic and explicit split counts (including more splits than
+d = 32, 64, 96, 128 and 256, scales 1.0 and 0.02 besides 1/sqrt(d), automatic and explicit split counts (including more splits than
 tiles, which the library caps), the decode workload at full size, agreement
 with attn_fwd when Nq = Nk, a 131077-key cache, and bitwise determinism.
 """
@@ -27,9 +27,9 @@ def _gpu():
     T.lib()  # raises if libattn.so is missing: no silent fallback
 
 
-def _check(q, k, v, causal, splits, tag):
+def _check(q, k, v, causal, splits, tag, scale=None):
     d = q.shape[-1]
-    scale = d ** -0.5
+    scale = d ** -0.5 if scale is None else scale
     log(f"[kv] {tag} q={tuple(q.shape)} k={tuple(k.shape)} causal={causal} splits={splits}")
     o, lse = gpu_forward_kv(q, k, v, causal, scale, splits)
     o_ref, lse_ref = oracle.attn_fwd_rect(q.double().numpy(), k.double().numpy(),
@@ -55,6 +55,17 @@ def test_decode_shapes(Nk, d, causal):
 def test_prefill_shapes(Nq, Nk, d, causal):
     q, k, v = make_kv_inputs(1, 2, Nq, Nk, d, seed=200 + Nq + Nk + d)
     _check(q, k, v, causal, 0, f"prefill Nq={Nq} Nk={Nk} d={d}")
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.02])
+@pytest.mark.parametrize("Nq,Nk,d", [(1, 1000, 128), (7, 100, 64), (200, 333, 96),
+                                     (130, 2049, 128), (1, 4097, 256), (100, 300, 32)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_other_scales(scale, Nq, Nk, d, causal):
+    """Scales other than 1/sqrt(d): peaky (1.0) and nearly flat (0.02) rows,
+    with the shifted causal mask and ragged key counts."""
+    q, k, v = make_kv_inputs(1, 2, Nq, Nk, d, seed=250 + Nq + Nk + d)
+    _check(q, k, v, causal, 0, f"scale={scale} Nq={Nq} Nk={Nk} d={d}", scale=scale)
 
 
 @pytest.mark.parametrize("splits", [1, 2, 3, 7, 1000])

@@ -9,7 +9,7 @@ rounded to bf16 as in attn_fwd, so the bf16 tolerance applies
 
 Coverage: d = 64 and 128, both masks, N from 1 to 1000 (tails inside a
 tile and several tiles), block scales 2^-2..2^2, 2^-7..2^7 (large logits)
-and all 2^0, the headline shape at full size on sampled rows, and bitwise
+and all 2^0, softmax scales 1.0 and 0.02 besides 1/sqrt(d), the headline shape at full size on sampled rows, and bitwise
 determinism.
 """
 import numpy as np
@@ -31,9 +31,9 @@ def _gpu():
     T.lib()  # raises if libattn.so is missing: no silent fallback
 
 
-def _check_all(N, d, causal, seed, lo=125, hi=129, B=1, H=2):
+def _check_all(N, d, causal, seed, lo=125, hi=129, B=1, H=2, scale=None):
     q8, qs, k8, ks, v = make_mx_inputs(B, H, N, d, seed, lo, hi)
-    scale = d ** -0.5
+    scale = d ** -0.5 if scale is None else scale
     log(f"[mx] N={N} d={d} causal={causal} scales [{lo}, {hi}] seed={seed}")
     o, lse = gpu_forward_mx(q8, qs, k8, ks, v, causal, scale)
     q = oracle.mx_decode(q8, qs)
@@ -55,6 +55,14 @@ def test_shapes(N, d, causal):
 @pytest.mark.parametrize("d", [64, 128])
 def test_scale_ranges(lo, hi, d):
     _check_all(300, d, True, seed=800 + lo + d, lo=lo, hi=hi)
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.02])
+@pytest.mark.parametrize("N,d", [(257, 64), (1000, 128), (100, 128)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_other_scales(scale, N, d, causal):
+    """Softmax scales other than 1/sqrt(d) (peaky and nearly flat rows)."""
+    _check_all(N, d, causal, seed=850 + N + d, scale=scale)
 
 
 def test_workload_sampled_rows():

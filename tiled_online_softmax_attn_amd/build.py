@@ -17,6 +17,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
 SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_fwd_kv.hip", "attn_bwd.hip", "softmax_rows.hip", "attn_fwd_mx.hip"]
+# the measured-ceiling probes (include/attn_probe.h), a library of their own
+PROBE_LIB = os.path.join(PKG, "libattn_probe.so")
+PROBE_SOURCES = ["roofline_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -40,21 +43,28 @@ def _compile(src: str, obj_dir: str, extra: list[str]) -> str:
     return obj
 
 
+def _link(objs: list[str], out: str) -> None:
+    tmp = out + ".tmp"
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, out)
+
+
 def build(verbose: bool = False, extra: list[str] | None = None) -> str:
-    """Compile every source and link libattn.so in the package directory."""
+    """Compile every source and link libattn.so (and libattn_probe.so) in the
+    package directory."""
     extra = list(extra or [])
     if verbose:
         extra += ["-Rpass-analysis=kernel-resource-usage"]
     obj_dir = os.path.join(PKG, "_build")
     os.makedirs(obj_dir, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, obj_dir, extra), SOURCES))
-    tmp = LIB + ".tmp"
-    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp],
-                       capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, obj_dir, extra), srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     return LIB
 
 

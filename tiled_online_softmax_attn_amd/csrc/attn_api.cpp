@@ -12,6 +12,14 @@ namespace {
 constexpr int kAbiVersion = 4;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+// lse is read and written one float at a time
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// The pages scale Q K^T by 1/sqrt(d) before the softmax, a positive number;
+// the kernels rely on scale > 0 (the row maximum is taken on the unscaled
+// scores, and masked scores are -inf before the scaling).  Zero, -0.0,
+// negative and non-finite scales are refused.
+bool scale_ok(float scale) { return isfinite(scale) && scale > 0.f; }
 
 // Shape checks shared by every entry point.  Element counts must fit in
 // int64 offsets and the workgroup count in a 32-bit grid.
@@ -47,8 +55,8 @@ const char* attn_status_str(int status) {
     case ATTN_ERR_DTYPE: return "dtype not supported by this entry point";
     case ATTN_ERR_HEADDIM:
       return "head dimension d must be 32, 64, 96, 128 or 256 (backward: at most 128)";
-    case ATTN_ERR_ALIGN: return "pointers must be 16-byte aligned";
-    case ATTN_ERR_SCALE: return "scale must be finite";
+    case ATTN_ERR_ALIGN: return "pointers must be 16-byte aligned (lse: 4-byte)";
+    case ATTN_ERR_SCALE: return "scale must be finite and > 0";
     case ATTN_ERR_WORKSPACE:
       return "workspace is NULL or smaller than the matching *_workspace_bytes()";
     case ATTN_ERR_HIP: return "the HIP runtime refused the kernel launch";
@@ -62,9 +70,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   int rc = check_shape(B, H, N, d);
   if (rc != ATTN_OK) return rc;
   if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F32) return ATTN_ERR_DTYPE;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse))
     return ATTN_ERR_ALIGN;
-  if (!isfinite(scale)) return ATTN_ERR_SCALE;
+  if (!scale_ok(scale)) return ATTN_ERR_SCALE;
   attn::FwdArgs a{q, k, v, o, lse, B, H, N, d, causal != 0, scale, dtype == ATTN_DTYPE_BF16,
                   stream};
   return attn::launch_fwd(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
@@ -87,10 +95,11 @@ static int bwd_common(int phase, const void* q, const void* k, const void* v, co
   if (!attn::bwd_head_dim_supported(d)) return ATTN_ERR_HEADDIM;
   if (phase < -1 || phase > 2) return ATTN_ERR_SHAPE;
   if (dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
-  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
+  const void* ptrs[] = {q, k, v, o, dout, dq, dk, dv};
   for (const void* p : ptrs)
     if (!aligned16(p)) return ATTN_ERR_ALIGN;
-  if (!isfinite(scale)) return ATTN_ERR_SCALE;
+  if (!aligned4(lse)) return ATTN_ERR_ALIGN;
+  if (!scale_ok(scale)) return ATTN_ERR_SCALE;
   const size_t need = attn_bwd_workspace_bytes(B, H, N, d, dtype);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
@@ -146,10 +155,11 @@ int attn_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse
   int rc = check_kv_shape(B, H, Nq, Nk, d, causal, num_splits);
   if (rc != ATTN_OK) return rc;
   if (dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
-  const void* ptrs[] = {q, k, v, o, lse};
+  const void* ptrs[] = {q, k, v, o};
   for (const void* p : ptrs)
     if (!aligned16(p)) return ATTN_ERR_ALIGN;
-  if (!isfinite(scale)) return ATTN_ERR_SCALE;
+  if (!aligned4(lse)) return ATTN_ERR_ALIGN;
+  if (!scale_ok(scale)) return ATTN_ERR_SCALE;
   const size_t need = attn_fwd_kv_workspace_bytes(B, H, Nq, Nk, d, num_splits, dtype);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
@@ -165,13 +175,13 @@ int attn_fwd_mx(const void* q8, const void* q_scale, const void* k8, const void*
   int rc = check_shape(B, H, N, d);
   if (rc != ATTN_OK) return rc;
   if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
-  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v) || !aligned16(o) || !aligned4(lse))
     return ATTN_ERR_ALIGN;
   // scale rows are d / 32 bytes, read as one 16- or 32-bit word
   const uintptr_t salign = d == 128 ? 3u : 1u;
   if ((reinterpret_cast<uintptr_t>(q_scale) & salign) || (reinterpret_cast<uintptr_t>(k_scale) & salign))
     return ATTN_ERR_ALIGN;
-  if (!isfinite(scale)) return ATTN_ERR_SCALE;
+  if (!scale_ok(scale)) return ATTN_ERR_SCALE;
   attn::FwdMxArgs a{q8, q_scale, k8, k_scale, v, o, lse, B, H, N, d, causal != 0, scale, stream};
   return attn::launch_fwd_mx(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
@@ -179,8 +189,9 @@ int attn_fwd_mx(const void* q8, const void* q_scale, const void* k8, const void*
 int attn_softmax_rows(const void* x, void* y, long long M, int N, int dtype, void* stream) {
   if (!x || !y) return ATTN_ERR_NULL;
   if (M < 1 || N < 1) return ATTN_ERR_SHAPE;
-  // M * N elements (at most 2^48) must stay addressable with 64-bit offsets
-  if (M > (1LL << 40) || M * (long long)N > (1LL << 48)) return ATTN_ERR_SHAPE;
+  // M * N elements (at most 2^48) must stay addressable with 64-bit offsets;
+  // checked by division, since the product itself may overflow
+  if (M > (1LL << 40) || (long long)N > (1LL << 48) / M) return ATTN_ERR_SHAPE;
   if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
   if (!aligned16(x) || !aligned16(y)) return ATTN_ERR_ALIGN;
   attn::SoftmaxArgs a{x, y, (int64_t)M, N, dtype == ATTN_DTYPE_BF16, stream};
