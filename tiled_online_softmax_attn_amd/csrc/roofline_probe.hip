@@ -103,20 +103,20 @@ __global__ void __launch_bounds__(256) exp_probe_kernel(float* __restrict__ out,
   out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
-// dst = src, 16 bytes per lane per access, grid-stride with four accesses in
-// flight per lane, nontemporal hints (the data is touched once).
+// dst = src, 16 bytes per lane per access: a workgroup copies 16 KiB, its
+// four 4 KiB slices read one after another by its 256 lanes (all four loads
+// in flight before the stores), with nontemporal hints (the data is touched
+// once).  One workgroup per 16 KiB, no grid-stride loop.
 __global__ void __launch_bounds__(256) copy_probe_kernel(const f32x4* __restrict__ src,
                                                          f32x4* __restrict__ dst, int64_t n16) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    f32x4 v[4];
+  const int64_t base = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+  f32x4 v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+  for (int u = 0; u < 4; ++u)
+    if (base + u * 256 < n16) v[u] = __builtin_nontemporal_load(src + base + u * 256);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) __builtin_nontemporal_store(v[u], dst + i + u * stride);
-  }
-  for (; i < n16; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+  for (int u = 0; u < 4; ++u)
+    if (base + u * 256 < n16) __builtin_nontemporal_store(v[u], dst + base + u * 256);
 }
 
 }  // namespace
@@ -147,8 +147,9 @@ int attn_probe_copy(const void* src, void* dst, long long bytes, void* stream) {
   if (!src || !dst || bytes < 16 || (bytes & 15) || ((uintptr_t)src & 15) || ((uintptr_t)dst & 15))
     return (int)hipErrorInvalidValue;
   const int64_t n16 = bytes / 16;
-  const int64_t want = (n16 + 255) / 256;
-  const unsigned blocks = (unsigned)(want < 8192 ? want : 8192);
+  const int64_t blocks64 = (n16 + 1023) / 1024;
+  if (blocks64 > 0x7fffffff) return (int)hipErrorInvalidValue;
+  const unsigned blocks = (unsigned)blocks64;
   hipLaunchKernelGGL(copy_probe_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
                      (const f32x4*)src, (f32x4*)dst, n16);
   return (int)hipGetLastError();
