@@ -66,7 +66,8 @@ typedef enum {
   ATTN_ERR_ALIGN = -5,     /* a pointer is not 16-byte aligned (lse: 4-byte) */
   ATTN_ERR_SCALE = -6,     /* scale is not finite, or not > 0 */
   ATTN_ERR_WORKSPACE = -7, /* workspace NULL or smaller than attn_bwd_workspace_bytes() */
-  ATTN_ERR_HIP = -8        /* the HIP runtime refused a launch */
+  ATTN_ERR_HIP = -8,       /* the HIP runtime refused a launch */
+  ATTN_ERR_SCRATCH = -9    /* attn_bwd_noalloc: B*H*N above its static scratch */
 } attn_status_t;
 
 /* Forward pass (CS336 L5 notes section 8.3).
@@ -104,6 +105,23 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
              const void* dout, const float* lse, void* dq, void* dk, void* dv,
              void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
              int causal, float scale, int dtype, void* stream);
+
+/* attn_bwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels and results, bit for bit, with the D vector kept in a static
+ * device array of the library (16 MiB on each GPU it runs on, held until the
+ * process ends) instead of a caller workspace.  It calls no hipMalloc or
+ * hipFree; the array's device address is looked up (hipGetSymbolAddress) on
+ * the first call made with a device current.  Arguments and errors are
+ * those of attn_bwd without the workspace, plus ATTN_ERR_SCRATCH when
+ * B * H * N exceeds 4,194,304 query rows.  Every call on one GPU shares that
+ * GPU's array: calls that overlap in time on one GPU (two streams, two host
+ * threads) race and give undefined results; calls in sequence on one
+ * stream do not.  Call it with the device that holds the tensors current. */
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                     int B, int H, int N, int d, int causal, float scale, int dtype,
+                     void* stream);
 
 /* One phase of attn_bwd, for callers that schedule or time the phases
  * separately.  attn_bwd(...) is exactly phases 0, 1, 2 in this order on one
@@ -189,7 +207,7 @@ const char* attn_status_str(int status);
 
 /* Library ABI version; bumped when an entry point is added or a signature
  * changes (2: attn_fwd_kv and attn_fwd_kv_workspace_bytes; 3: attn_softmax_rows,
- * and head dimensions 32, 96 and 256; 4: attn_fwd_mx). */
+ * and head dimensions 32, 96 and 256; 4: attn_fwd_mx; 5: attn_bwd_noalloc). */
 int attn_abi_version(void);
 
 #ifdef __cplusplus

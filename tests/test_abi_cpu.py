@@ -52,7 +52,8 @@ def _lib():
 
 
 def test_header_declares_expected_entry_points():
-    assert declared_functions() == sorted(["attn_fwd", "attn_bwd", "attn_bwd_phase",
+    assert declared_functions() == sorted(["attn_fwd", "attn_bwd", "attn_bwd_noalloc",
+                                           "attn_bwd_phase",
                                            "attn_bwd_workspace_bytes", "attn_fwd_kv",
                                            "attn_fwd_kv_workspace_bytes", "attn_softmax_rows", "attn_fwd_mx",
                                            "attn_status_str", "attn_abi_version"])
@@ -68,8 +69,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = _lib()
-    assert lib.attn_abi_version() == 4
-    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, 12345]:
+    assert lib.attn_abi_version() == 5
+    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, 12345]:
         s = lib.attn_status_str(code)
         assert isinstance(s, bytes) and len(s) > 0
 
@@ -130,6 +131,26 @@ def test_bwd_validation(args, code):
                                                "dv", "ws")),
                       a["ws_bytes"], a["B"], a["H"], a["N"], a["d"], a["causal"], a["scale"],
                       a["dtype"], None)
+    assert rc == code
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(dout=0), -1), (dict(lse=0), -1), (dict(dtype=0), -3), (dict(N=0), -2),
+    (dict(d=80), -4), (dict(d=256), -4), (dict(dk=FAKE + 4), -5), (dict(lse=FAKE + 2), -5),
+    (dict(scale=0.0), -6), (dict(scale=float("nan")), -6),
+    # above the 16 MiB static scratch (4194304 query rows), refused before any
+    # device call
+    (dict(B=1, H=5, N=838861), -9), (dict(B=64, H=64, N=1025), -9),
+])
+def test_bwd_noalloc_validation(args, code):
+    lib = _lib()
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, dout=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+             B=1, H=1, N=16, d=64, causal=1, scale=0.125, dtype=1)
+    a.update(args)
+    rc = lib.attn_bwd_noalloc(*(a[n] or None for n in ("q", "k", "v", "o", "dout", "lse", "dq",
+                                                       "dk", "dv")),
+                              a["B"], a["H"], a["N"], a["d"], a["causal"], a["scale"], a["dtype"],
+                              None)
     assert rc == code
 
 

@@ -26,8 +26,8 @@ ATTN_DTYPE_F32 = 0
 ATTN_DTYPE_BF16 = 1
 STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_DTYPE",
           -4: "ATTN_ERR_HEADDIM", -5: "ATTN_ERR_ALIGN", -6: "ATTN_ERR_SCALE",
-          -7: "ATTN_ERR_WORKSPACE", -8: "ATTN_ERR_HIP"}
-EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_phase", "attn_bwd_workspace_bytes",
+          -7: "ATTN_ERR_WORKSPACE", -8: "ATTN_ERR_HIP", -9: "ATTN_ERR_SCRATCH"}
+EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_noalloc", "attn_bwd_phase", "attn_bwd_workspace_bytes",
            "attn_fwd_kv", "attn_fwd_kv_workspace_bytes", "attn_softmax_rows", "attn_fwd_mx",
            "attn_status_str", "attn_abi_version")
 
@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd.restype = i
         L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                i, i, i, i, i, f, i, vp]
+        L.attn_bwd_noalloc.restype = i
+        L.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
         L.attn_bwd_phase.restype = i
         L.attn_bwd_phase.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                      i, i, i, i, i, f, i, vp]
@@ -185,6 +187,21 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool, scale: 
                         int(bool(causal)), float(scale), _dtype_code(q), _stream_handle(stream))
     if rc != 0:
         raise AttnError(rc, "attn_bwd")
+
+
+def attn_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, causal: bool, scale: float,
+                     stream=None) -> None:
+    """Enqueue the backward with no workspace: the library's static device
+    scratch holds D (B*H*N at most 4194304 rows).  Results equal attn_bwd's
+    bit for bit; calls that overlap in time on one GPU race."""
+    _check_contig(q, k, v, o, dout, lse, dq, dk, dv)
+    B, H, N, d = _shape(q)
+    _check_bwd("attn_bwd_noalloc", q, k, v, o, dout, lse, dq, dk, dv, None)
+    rc = lib().attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, int(bool(causal)),
+                                float(scale), _dtype_code(q), _stream_handle(stream))
+    if rc != 0:
+        raise AttnError(rc, "attn_bwd_noalloc")
 
 
 def attn_bwd_phase(phase: int, q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool,

@@ -5,11 +5,40 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "attn_launch.h"
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
+
+// Device scratch of attn_bwd_noalloc: the D vector (one fp32 per query row)
+// that attn_bwd keeps in the caller's workspace.  16 MiB per GPU, so
+// B * H * N <= 4,194,304 rows.  In host code `scratch` names a host-side
+// stand-in, never the device address: that comes from hipGetSymbolAddress,
+// once per device, and is what every kernel argument uses.
+constexpr size_t kNoallocScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};  // device address of `scratch`, per device
+
+// Device address of `scratch` on the current device, looked up on the first
+// call made with that device current and kept for the life of the process.
+int noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ATTN_ERR_HIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return ATTN_OK;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 // lse is read and written one float at a time
@@ -60,6 +89,8 @@ const char* attn_status_str(int status) {
     case ATTN_ERR_WORKSPACE:
       return "workspace is NULL or smaller than the matching *_workspace_bytes()";
     case ATTN_ERR_HIP: return "the HIP runtime refused the kernel launch";
+    case ATTN_ERR_SCRATCH:
+      return "B*H*N exceeds the static scratch of attn_bwd_noalloc (4194304 query rows)";
     default: return "unknown attn status";
   }
 }
@@ -85,10 +116,10 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N, int d, int dtype) {
   return attn::bwd_delta_bytes(B, H, N);
 }
 
-static int bwd_common(int phase, const void* q, const void* k, const void* v, const void* o,
-                      const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                      void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
-                      int causal, float scale, int dtype, void* stream) {
+// Every check of the backward except the workspace.
+static int bwd_check(int phase, const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, const void* dq, const void* dk,
+                     const void* dv, int B, int H, int N, int d, float scale, int dtype) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL;
   int rc = check_shape(B, H, N, d);
   if (rc != ATTN_OK) return rc;
@@ -100,6 +131,15 @@ static int bwd_common(int phase, const void* q, const void* k, const void* v, co
     if (!aligned16(p)) return ATTN_ERR_ALIGN;
   if (!aligned4(lse)) return ATTN_ERR_ALIGN;
   if (!scale_ok(scale)) return ATTN_ERR_SCALE;
+  return ATTN_OK;
+}
+
+static int bwd_common(int phase, const void* q, const void* k, const void* v, const void* o,
+                      const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                      void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                      int causal, float scale, int dtype, void* stream) {
+  int rc = bwd_check(phase, q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, dtype);
+  if (rc != ATTN_OK) return rc;
   const size_t need = attn_bwd_workspace_bytes(B, H, N, d, dtype);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
@@ -115,6 +155,23 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int dtype, void* stream) {
   return bwd_common(-1, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N,
                     d, causal, scale, dtype, stream);
+}
+
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                     int H, int N, int d, int causal, float scale, int dtype, void* stream) {
+  int rc = bwd_check(-1, q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, dtype);
+  if (rc != ATTN_OK) return rc;
+  if ((size_t)B * (size_t)H * (size_t)N * sizeof(float) > kNoallocScratchBytes)
+    return ATTN_ERR_SCRATCH;
+  void* ws = nullptr;
+  rc = noalloc_scratch(&ws);
+  if (rc != ATTN_OK) return rc;
+  // the same three kernels as attn_bwd; phase 0 writes every D entry that
+  // phases 1 and 2 read, so nothing in the scratch needs clearing
+  attn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, (float*)ws, B, H, N, d, causal != 0,
+                  scale, stream};
+  return attn::launch_bwd(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 int attn_bwd_phase(int phase, const void* q, const void* k, const void* v, const void* o,
