@@ -19,6 +19,8 @@ that file's header:
 * ``attn_fwd_rect`` - Nq queries at the end of an Nk-key sequence.
 * ``attn_bwd``      - dQ, dK, dV of sum(dO * O) (CS336 L5 notes section 8.4,
   Exercise 9).
+* ``attn_bwd_rect`` - the same gradient for Nq queries at the end of an
+  Nk-key sequence (the backward of ``attn_fwd_rect``).
 * ``mx_decode``     - values of an MXFP8 tensor (E4M3 codes, one E8M0 scale
   per 32 elements of a row; CS336 L5 notes section 6.2); attention of MXFP8
   inputs is ``attn_fwd`` of the decoded values.
@@ -96,6 +98,9 @@ def _declare(lib):
     lib.oracle_mx_decode.argtypes = [ctypes.c_void_p, ctypes.c_void_p, i64, i64, _DP]
     lib.oracle_attn_bwd_head.restype = ctypes.c_int
     lib.oracle_attn_bwd_head.argtypes = [_DP, _DP, _DP, _DP, i64, i64, ctypes.c_int,
+                                         ctypes.c_double, _DP, _DP, _DP, _DP, _DP, _DP]
+    lib.oracle_attn_bwd_rect.restype = ctypes.c_int
+    lib.oracle_attn_bwd_rect.argtypes = [_DP, _DP, _DP, _DP, i64, i64, i64, ctypes.c_int,
                                          ctypes.c_double, _DP, _DP, _DP, _DP, _DP, _DP]
     return lib
 
@@ -249,3 +254,31 @@ def attn_bwd(q, k, v, dout, causal: bool, scale: float, lib=None):
     res["lse"] = lse.reshape(lead + (N,))
     res["D"] = D.reshape(lead + (N,))
     return res
+
+
+def attn_bwd_rect(q, k, v, dout, causal: bool, scale: float, lib=None):
+    """dq [..., Nq, d], dk, dv [..., Nk, d] of sum(dout * O) for Nq queries
+    (the last Nq positions) against Nk keys, plus the oracle's own (o, lse,
+    D).  Returns a dict of float64 arrays."""
+    lib = lib or load()
+    qh, lead = _heads(q)
+    kh, _ = _heads(k)
+    vh, _ = _heads(v)
+    doh, _ = _heads(dout)
+    G, Nq, d = qh.shape
+    Nk = kh.shape[1]
+    dq = np.empty_like(qh)
+    o = np.empty_like(qh)
+    dk = np.empty_like(kh)
+    dv = np.empty_like(kh)
+    lse = np.empty((G, Nq), dtype=np.float64)
+    D = np.empty((G, Nq), dtype=np.float64)
+    for g in range(G):
+        rc = lib.oracle_attn_bwd_rect(
+            _ptr(qh[g]), _ptr(kh[g]), _ptr(vh[g]), _ptr(doh[g]), Nq, Nk, d,
+            int(bool(causal)), float(scale), _ptr(dq[g]), _ptr(dk[g]), _ptr(dv[g]),
+            _ptr(o[g]), _ptr(lse[g]), _ptr(D[g]))
+        _check(rc, "attn_bwd_rect")
+    return {"dq": dq.reshape(lead + (Nq, d)), "dk": dk.reshape(lead + (Nk, d)),
+            "dv": dv.reshape(lead + (Nk, d)), "o": o.reshape(lead + (Nq, d)),
+            "lse": lse.reshape(lead + (Nq,)), "D": D.reshape(lead + (Nq,))}

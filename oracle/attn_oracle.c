@@ -308,6 +308,93 @@ int oracle_attn_bwd_head(const double* q, const double* k, const double* v,
   return 0;
 }
 
+/* Backward of oracle_attn_fwd_rect: the exact gradient of sum(dO * O) for
+ * Nq queries at the end of an Nk-key sequence (chunked prefill), in the terms
+ * of CS336 L5 notes section 8.4 with the shifted causal mask of the forward
+ * (query i sees keys 0 .. i + Nk - Nq).  q, dout: [Nq][d]; k, v: [Nk][d];
+ * dq: [Nq][d]; dk, dv: [Nk][d].  o_out [Nq][d], lse_out [Nq] and D_out [Nq],
+ * when not NULL, receive the oracle's own O, lse and D.  Written out
+ * directly: P [Nq][Nk] row by row (scores, mask, safe softmax), then D,
+ * dPr = dO V^T, dSr = P * (dPr - D), dQ, dK, dV. */
+int oracle_attn_bwd_rect(const double* q, const double* k, const double* v,
+                         const double* dout, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                         double scale, double* dq, double* dk, double* dv, double* o_out,
+                         double* lse_out, double* D_out) {
+  if (!q || !k || !v || !dout || !dq || !dk || !dv) return -1;
+  if (Nq < 1 || Nk < 1 || d < 1 || (causal && Nk < Nq)) return -2;
+  const int64_t shift = Nk - Nq;
+  const size_t nqk = (size_t)Nq * (size_t)Nk;
+  double* Pr = (double*)malloc(sizeof(double) * nqk);
+  double* dSr = (double*)malloc(sizeof(double) * nqk);
+  double* Or = (double*)malloc(sizeof(double) * (size_t)Nq * (size_t)d);
+  double* Lr = (double*)malloc(sizeof(double) * (size_t)Nq);
+  double* Dr = (double*)malloc(sizeof(double) * (size_t)Nq);
+  double* srow = (double*)malloc(sizeof(double) * (size_t)Nk);
+  if (!Pr || !dSr || !Or || !Lr || !Dr || !srow) {
+    free(Pr); free(dSr); free(Or); free(Lr); free(Dr); free(srow);
+    return -3;
+  }
+  /* P = softmax(scale q k^T + mask) row by row, O = P V, lse = m + ln l */
+  for (int64_t r = 0; r < Nq; ++r) {
+    for (int64_t t = 0; t < Nk; ++t) {
+      if (causal && t > r + shift) {
+        srow[t] = -INFINITY;
+        continue;
+      }
+      double qk = 0.0;
+      for (int64_t c = 0; c < d; ++c) qk += q[r * d + c] * k[t * d + c];
+      srow[t] = scale * qk;
+    }
+    double mr, lr;
+    oracle_softmax_row(srow, Nk, Pr + r * Nk, &mr, &lr);
+    Lr[r] = mr + log(lr);
+    for (int64_t c = 0; c < d; ++c) {
+      double acc = 0.0;
+      for (int64_t t = 0; t < Nk; ++t) acc += Pr[r * Nk + t] * v[t * d + c];
+      Or[r * d + c] = acc;
+    }
+    double dd = 0.0;
+    for (int64_t c = 0; c < d; ++c) dd += dout[r * d + c] * Or[r * d + c];
+    Dr[r] = dd;
+  }
+  /* dSr = P * (dO V^T - D) */
+#pragma omp parallel for schedule(dynamic, 8)
+  for (int64_t r = 0; r < Nq; ++r) {
+    for (int64_t t = 0; t < Nk; ++t) {
+      double dpr = 0.0;
+      for (int64_t c = 0; c < d; ++c) dpr += dout[r * d + c] * v[t * d + c];
+      dSr[r * Nk + t] = Pr[r * Nk + t] * (dpr - Dr[r]);
+    }
+  }
+  /* dQ = scale * dSr K */
+#pragma omp parallel for schedule(dynamic, 8)
+  for (int64_t r = 0; r < Nq; ++r) {
+    for (int64_t c = 0; c < d; ++c) {
+      double acc = 0.0;
+      for (int64_t t = 0; t < Nk; ++t) acc += dSr[r * Nk + t] * k[t * d + c];
+      dq[r * d + c] = scale * acc;
+    }
+  }
+  /* dK = scale * dSr^T Q and dV = P^T dO, one key row t at a time */
+#pragma omp parallel for schedule(dynamic, 8)
+  for (int64_t t = 0; t < Nk; ++t) {
+    for (int64_t c = 0; c < d; ++c) {
+      double ak = 0.0, av = 0.0;
+      for (int64_t r = 0; r < Nq; ++r) {
+        ak += dSr[r * Nk + t] * q[r * d + c];
+        av += Pr[r * Nk + t] * dout[r * d + c];
+      }
+      dk[t * d + c] = scale * ak;
+      dv[t * d + c] = av;
+    }
+  }
+  if (o_out) memcpy(o_out, Or, sizeof(double) * (size_t)Nq * (size_t)d);
+  if (lse_out) memcpy(lse_out, Lr, sizeof(double) * (size_t)Nq);
+  if (D_out) memcpy(D_out, Dr, sizeof(double) * (size_t)Nq);
+  free(Pr); free(dSr); free(Or); free(Lr); free(Dr); free(srow);
+  return 0;
+}
+
 /* ---------------------------------------------------------------- MXFP8
  * Q and K given in the MXFP8 format the CS336 L5 notes (section 6.2) name:
  * E4M3 values plus one E8M0 scale for every 32 elements of a row.  The

@@ -25,7 +25,9 @@ What pins what:
 * Nq queries against Nk keys (the last Nq positions, PDC notes Lecture 4
   section 4.9 key/value cache): 50-digit brute force with the shifted causal
   mask, Q = 0 closed form, and the blocked merge of per-chunk (O, lse) pairs
-  (CS149 L9 notes section 9) that split-key attention relies on.
+  (CS149 L9 notes section 9) that split-key attention relies on; its backward
+  by finite differences of that brute force, the dV / dK sums, the D identity,
+  and Nq = Nk against the square backward.
 * MXFP8 decoding (CS336 L5 notes section 6.2: E4M3 values, one E8M0 scale
   per 32 elements): every E4M3 code against torch's float8_e4m3fn cast and
   the format's fixed points (1, 448, 2^-6, 2^-9, NaN); E8M0 against its
@@ -406,6 +408,65 @@ def pin_rect_merge(lib):
     _assert_close(o_m, o, 1e-13, 1e-14, "merged O")
 
 
+def pin_rect_bwd_finite_differences(lib):
+    """Gradient of L = sum(dO * O) for Nq queries at the end of Nk keys, by
+    central differences of the 50-digit shifted-mask forward (independent of
+    the oracle's forward and backward)."""
+    rng = _rng(34)
+    h = Decimal("1e-15")
+    for Nq, Nk, d, causal in [(2, 5, 3, True), (3, 4, 2, False), (1, 4, 3, True), (3, 3, 2, True)]:
+        q, do = rng.normal(size=(2, Nq, d))
+        k, v = rng.normal(size=(2, Nk, d))
+        scale = 1 / math.sqrt(d)
+        g = oracle.attn_bwd_rect(q, k, v, do, causal, scale, lib=lib)
+        base = {"q": _to_dec(q), "k": _to_dec(k), "v": _to_dec(v)}
+        dod = _to_dec(do)
+
+        def loss(t):
+            O, _ = dec_forward_rect(t["q"], t["k"], t["v"], causal, scale)
+            return sum((O[i][c] * dod[i][c] for i in range(Nq) for c in range(d)), Decimal(0))
+
+        for name, rows in (("q", Nq), ("k", Nk), ("v", Nk)):
+            fd = np.zeros((rows, d))
+            for i in range(rows):
+                for c in range(d):
+                    t = {n: [row[:] for row in a] for n, a in base.items()}
+                    t[name][i][c] = base[name][i][c] + h
+                    lp = loss(t)
+                    t[name][i][c] = base[name][i][c] - h
+                    lm = loss(t)
+                    fd[i, c] = float((lp - lm) / (2 * h))
+            _assert_close(g["d" + name], fd, 1e-10, 1e-12, f"rect finite differences d{name}")
+
+
+def pin_rect_bwd_invariants(lib):
+    """For Nq queries against Nk keys: sum_j dV_j = sum_i dO_i (rows of P sum
+    to 1), sum_j dK_j = 0 (each row of dS sums to 0), the D identity of CS336
+    L5 notes Exercise 9, and O, lse equal to the rectangular forward's."""
+    rng = _rng(35)
+    for Nq, Nk, causal in [(13, 40, True), (40, 13, False), (29, 29, True)]:
+        q, do = rng.normal(size=(2, Nq, 6))
+        k, v = rng.normal(size=(2, Nk, 6))
+        g = oracle.attn_bwd_rect(q, k, v, do, causal, 0.45, lib=lib)
+        _assert_close(g["dv"].sum(0), do.sum(0), 1e-12, 1e-12, "rect sum dV")
+        _assert_close(g["dk"].sum(0), np.zeros(6), 0, 1e-12 * np.abs(g["dk"]).sum(), "rect sum dK")
+        o, lse = oracle.attn_fwd_rect(q, k, v, causal, 0.45, lib=lib)
+        _assert_close(g["o"], o, 1e-13, 1e-14, "rect bwd O")
+        _assert_close(g["lse"], lse, 1e-14, 1e-14, "rect bwd lse")
+        _assert_close(g["D"], (do * o).sum(-1), 1e-12, 1e-12, "rect D definition")
+
+
+def pin_rect_bwd_square(lib):
+    """Nq = Nk is the square backward, pinned on its own above."""
+    rng = _rng(36)
+    for causal in (False, True):
+        q, k, v, do = rng.normal(size=(4, 21, 5))
+        a = oracle.attn_bwd(q, k, v, do, causal, 0.5, lib=lib)
+        b = oracle.attn_bwd_rect(q, k, v, do, causal, 0.5, lib=lib)
+        for n in ("dq", "dk", "dv"):
+            _assert_close(b[n], a[n], 1e-13, 1e-13, f"rect square {n}")
+
+
 def pin_mx_e4m3_codes(lib):
     """Every E4M3 code decodes to torch's float8_e4m3fn value (a separate
     implementation of the OCP format), and the format's fixed points hold."""
@@ -451,6 +512,7 @@ FORWARD_PINS = [pin_worked_example, pin_blocked_identity, pin_streaming_and_bloc
                 pin_rows_sum_to_one, pin_constant_v, pin_q_zero, pin_row0_and_single_key,
                 pin_brute_force, pin_large_logits, pin_rows_entry]
 BACKWARD_PINS = [pin_bwd_finite_differences, pin_bwd_D_identity, pin_bwd_invariants]
-RECT_PINS = [pin_rect_brute_force, pin_rect_q_zero, pin_rect_merge]
+RECT_PINS = [pin_rect_brute_force, pin_rect_q_zero, pin_rect_merge,
+             pin_rect_bwd_finite_differences, pin_rect_bwd_invariants, pin_rect_bwd_square]
 MX_PINS = [pin_mx_e4m3_codes, pin_mx_scales]
 ALL_PINS = FORWARD_PINS + BACKWARD_PINS + RECT_PINS + MX_PINS

@@ -39,6 +39,14 @@ MUTANTS = {
     "rect_scale_dropped": ("s[j] = dot * scale;", "s[j] = dot;"),
     "rect_lse_log2": ("lse[i] = log(l) + m;", "lse[i] = log2(l) + m;"),
     "rect_pv_key_offset": ("oi[c] += p[j] * vj[c];", "oi[c] += p[j] * vj[c] * (j + 1 < Nk);"),
+    "rect_bwd_mask_unshifted": ("if (causal && t > r + shift) {", "if (causal && t > r) {"),
+    "rect_bwd_ds_sign": ("dSr[r * Nk + t] = Pr[r * Nk + t] * (dpr - Dr[r]);",
+                         "dSr[r * Nk + t] = Pr[r * Nk + t] * (dpr + Dr[r]);"),
+    "rect_bwd_dk_uses_P": ("ak += dSr[r * Nk + t] * q[r * d + c];", "ak += Pr[r * Nk + t] * q[r * d + c];"),
+    "rect_bwd_dv_uses_V": ("av += Pr[r * Nk + t] * dout[r * d + c];", "av += Pr[r * Nk + t] * v[t * d + c];"),
+    "rect_bwd_dq_no_scale": ("dq[r * d + c] = scale * acc;", "dq[r * d + c] = acc;"),
+    "rect_bwd_D_uses_Q": ("dd += dout[r * d + c] * Or[r * d + c];", "dd += dout[r * d + c] * q[r * d + c];"),
+    "rect_bwd_dk_wrong_key": ("ak += dSr[r * Nk + t] * q[r * d + c];", "ak += dSr[r * Nk + (Nk - 1 - t)] * q[r * d + c];"),
     "e4m3_bias": ("ldexp(8.0 + m, e - 10)", "ldexp(8.0 + m, e - 11)"),
     "e4m3_subnormal_as_normal": ("(e == 0) ? ldexp((double)m, -9) :", ""),
     "e4m3_no_sign": ("return sign ? -mag : mag;", "return mag;"),
