@@ -114,6 +114,7 @@ class KvWorkload:
     dtype: torch.dtype
     causal: bool
     seed: int
+    backward: bool = False  # a step is attn_fwd_kv + attn_bwd_kv (dO drawn after V)
 
     @property
     def scale(self) -> float:
@@ -141,24 +142,31 @@ KV_WORKLOADS = {
                                                 128, torch.bfloat16, True, 6),
     "prefill_b2_h16_nq512_nk4096_d128": KvWorkload("prefill_b2_h16_nq512_nk4096_d128", 2, 16, 512,
                                                    4096, 128, torch.bfloat16, True, 7),
+    # the same chunk as a training step: forward and backward
+    "prefill_b2_h16_nq512_nk4096_d128_fwdbwd": KvWorkload(
+        "prefill_b2_h16_nq512_nk4096_d128_fwdbwd", 2, 16, 512, 4096, 128, torch.bfloat16, True, 7,
+        backward=True),
 }
 
 
 def make_kv_inputs(B: int, H: int, Nq: int, Nk: int, d: int, dtype: torch.dtype = torch.bfloat16,
-                   seed: int = 0):
-    """CPU tensors q [B, H, Nq, d] and k, v [B, H, Nk, d]: a seeded CPU
-    generator draws Q, K, V in that order as float32 N(0, 1), then rounds to
-    ``dtype``."""
+                   seed: int = 0, with_dout: bool = False):
+    """CPU tensors q [B, H, Nq, d] and k, v [B, H, Nk, d] (and dO [B, H, Nq,
+    d] with ``with_dout``): a seeded CPU generator draws Q, K, V (then dO) in
+    that order as float32 N(0, 1), then rounds to ``dtype``."""
     g = torch.Generator(device="cpu")
     g.manual_seed(int(seed))
     q = torch.randn((B, H, Nq, d), generator=g, dtype=torch.float32)
     k = torch.randn((B, H, Nk, d), generator=g, dtype=torch.float32)
     v = torch.randn((B, H, Nk, d), generator=g, dtype=torch.float32)
-    return q.to(dtype), k.to(dtype), v.to(dtype)
+    out = [q.to(dtype), k.to(dtype), v.to(dtype)]
+    if with_dout:
+        out.append(torch.randn((B, H, Nq, d), generator=g, dtype=torch.float32).to(dtype))
+    return tuple(out)
 
 
 def kv_workload_inputs(w: KvWorkload):
-    return make_kv_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, w.seed)
+    return make_kv_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, w.seed, w.backward)
 
 
 @dataclass(frozen=True)

@@ -334,6 +334,77 @@ def cpu_baseline_kv(w, q, k, v, budget_s: float):
                       f"{el:.1f} s"}
 
 
+def bench_kv_fwdbwd(args, w):
+    """One step = attn_fwd_kv + attn_bwd_kv (the training step of a chunked
+    prefill: Nq queries at the end of an Nk-token sequence); TFLOP/s by the
+    formula: 4 d times the visible (query, key) pairs for the forward, 2.5
+    times that for the backward."""
+    import torch
+
+    import tiled_online_softmax_attn_amd as T
+    from attn_inputs import kv_workload_inputs
+
+    T.lib()
+    dev = torch.device("cuda:0")
+    eprint(f"[bench] generating inputs for {w.name}")
+    q, k, v, do = kv_workload_inputs(w)
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.Nq), device=dev, dtype=torch.float32)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    ws_f = torch.empty(T.attn_fwd_kv_workspace_bytes(w.B, w.H, w.Nq, w.Nk, w.d, 0, w.dtype),
+                       device=dev, dtype=torch.uint8)
+    ws_b = torch.empty(T.attn_bwd_kv_workspace_bytes(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype),
+                       device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        T.attn_fwd_kv(qd, kd, vd, o, lse, w.causal, w.scale, 0, ws_f, stream)
+        if ev:
+            ev[1].record(stream)
+        T.attn_bwd_kv(qd, kd, vd, o, dod, lse, dq, dk, dv, ws_b, w.causal, w.scale, stream)
+        if ev:
+            ev[2].record(stream)
+
+    eprint(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    eprint(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    f_fwd = w.flops()
+    f_bwd = 2.5 * f_fwd
+    value = (f_fwd + f_bwd) * args.steps / wall / 1e12
+    bwd_rate = f_bwd / (bwd_ms * 1e-3) / 1e12
+    fwd_rate = f_fwd / (fwd_ms * 1e-3) / 1e12
+    dom = "bwd_kv" if bwd_ms >= fwd_ms else "fwd_kv"
+    ach = bwd_rate if dom == "bwd_kv" else fwd_rate
+    roofline = {"kernel": dom + " (one call)", "bound": "mfma", "achieved": round(ach, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": None}
+    out = {
+        "metric": f"chunked-prefill training step TFLOP/s (attn_fwd_kv + attn_bwd_kv), {w.name}",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q, K, V, dO)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                   "causal": w.causal, "step": "attn_fwd_kv + attn_bwd_kv"},
+        "fwd_ms": round(fwd_ms, 5), "bwd_ms": round(bwd_ms, 5), "fwd_tflops": round(fwd_rate, 2),
+        "bwd_tflops": round(bwd_rate, 2), "roofline": roofline, "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def bench_kv(args, w):
     """One step = attn_fwd_kv over the whole cache workload."""
     import torch
@@ -627,7 +698,8 @@ def main():
                                            "hbm_gbs": PEAK_HBM_GBS}}), flush=True)
         return
     if args.workload in KV_WORKLOADS:
-        bench_kv(args, KV_WORKLOADS[args.workload])
+        wk = KV_WORKLOADS[args.workload]
+        (bench_kv_fwdbwd if wk.backward else bench_kv)(args, wk)
         return
     if args.workload in SOFTMAX_WORKLOADS:
         bench_softmax(args, SOFTMAX_WORKLOADS[args.workload])

@@ -171,6 +171,31 @@ int attn_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse
                 int B, int H, int Nq, int Nk, int d, int causal, float scale, int dtype,
                 int num_splits, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace attn_bwd_kv needs: the D vector (B*H*Nq fp32),
+ * rounded up to a multiple of 256.  Returns 0 for invalid sizes, d above
+ * 128 or an unsupported dtype. */
+size_t attn_bwd_kv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype);
+
+/* Backward of attn_fwd_kv (CS336 L5 notes section 8.4 with the mask of a
+ * key/value cache, PDC notes Lecture 4, section 4.9): Nq queries at the last
+ * Nq positions of an Nk-token sequence, the training step of chunked
+ * prefill.  Returns the gradients of sum(dout * O), recomputing attention
+ * from the saved lse as attn_bwd does.
+ *   q, o, dout, dq : [B][H][Nq][d] bf16 (dq written).
+ *   k, v, dk, dv   : [B][H][Nk][d] bf16 (dk, dv written).
+ *   lse            : [B][H][Nq] float32, the forward's (attn_fwd_kv writes it).
+ *   causal         : != 0 hides key j from query i when j > i + Nk - Nq, and
+ *                    then requires Nk >= Nq; 0 lets every query see every key.
+ *   workspace      : at least attn_bwd_kv_workspace_bytes() bytes, caller-
+ *                    owned, contents on entry ignored.
+ * Nq = Nk is attn_bwd, bit for bit (the same kernels).  d <= 128, bf16.
+ * Every output element is written once (no atomics).  Errors: those of
+ * attn_fwd_kv and attn_bwd.  Calls that share a workspace must not overlap. */
+int attn_bwd_kv(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                size_t workspace_bytes, int B, int H, int Nq, int Nk, int d, int causal,
+                float scale, int dtype, void* stream);
+
 /* Forward pass with Q and K in MXFP8 (CS336 L5 notes section 6.2: E4M3
  * values plus one E8M0 scale per 32 elements; here the blocks run along d,
  * the dimension S = Q K^T contracts) and V in bf16.  Computes exactly what
@@ -207,7 +232,8 @@ const char* attn_status_str(int status);
 
 /* Library ABI version; bumped when an entry point is added or a signature
  * changes (2: attn_fwd_kv and attn_fwd_kv_workspace_bytes; 3: attn_softmax_rows,
- * and head dimensions 32, 96 and 256; 4: attn_fwd_mx; 5: attn_bwd_noalloc). */
+ * and head dimensions 32, 96 and 256; 4: attn_fwd_mx; 5: attn_bwd_noalloc; 6: attn_bwd_kv and
+ * attn_bwd_kv_workspace_bytes). */
 int attn_abi_version(void);
 
 #ifdef __cplusplus

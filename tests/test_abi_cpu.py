@@ -55,7 +55,8 @@ def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted(["attn_fwd", "attn_bwd", "attn_bwd_noalloc",
                                            "attn_bwd_phase",
                                            "attn_bwd_workspace_bytes", "attn_fwd_kv",
-                                           "attn_fwd_kv_workspace_bytes", "attn_softmax_rows", "attn_fwd_mx",
+                                           "attn_fwd_kv_workspace_bytes", "attn_bwd_kv",
+                                           "attn_bwd_kv_workspace_bytes", "attn_softmax_rows", "attn_fwd_mx",
                                            "attn_status_str", "attn_abi_version"])
 
 
@@ -69,7 +70,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = _lib()
-    assert lib.attn_abi_version() == 5
+    assert lib.attn_abi_version() == 6
     for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, 12345]:
         s = lib.attn_status_str(code)
         assert isinstance(s, bytes) and len(s) > 0
@@ -206,6 +207,36 @@ def test_kv_validation(args, code):
     rc = lib.attn_fwd_kv(a["q"] or None, a["k"], a["v"], a["o"], a["lse"] or None, a["B"],
                          a["H"], a["Nq"], a["Nk"], a["d"], a["causal"], a["scale"], a["dtype"],
                          a["splits"], a["ws"] or None, a["ws_bytes"], None)
+    assert rc == code
+
+
+def test_bwd_kv_workspace_size():
+    lib = _lib()
+    assert lib.attn_bwd_kv_workspace_bytes(2, 16, 512, 4096, 128, 1) == 2 * 16 * 512 * 4
+    assert lib.attn_bwd_kv_workspace_bytes(1, 3, 7, 100, 64, 1) == 256  # 84 bytes, rounded
+    assert lib.attn_bwd_kv_workspace_bytes(1, 1, 7, 100, 256, 1) == 0  # backward d <= 128
+    assert lib.attn_bwd_kv_workspace_bytes(1, 1, 7, 100, 64, 0) == 0  # bf16 only
+    assert lib.attn_bwd_kv_workspace_bytes(1, 1, 0, 100, 64, 1) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(q=0), -1), (dict(dv=0), -1), (dict(B=0), -2), (dict(Nq=0), -2), (dict(Nk=0), -2),
+    (dict(Nq=20, Nk=10, causal=1), -2), (dict(d=48), -4), (dict(d=256), -4),
+    (dict(dtype=0), -3), (dict(dk=FAKE + 4), -5), (dict(lse=FAKE + 2), -5),
+    (dict(scale=0.0), -6), (dict(scale=-1.0), -6), (dict(scale=float("inf")), -6),
+    (dict(lse=FAKE + 4, scale=0.0), -6),
+    (dict(ws=0), -7), (dict(ws_bytes=8), -7), (dict(ws=FAKE + 8), -5),
+])
+def test_bwd_kv_validation(args, code):
+    lib = _lib()
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, dout=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+             ws=FAKE, ws_bytes=1 << 30, B=1, H=1, Nq=4, Nk=100, d=64, causal=1, scale=0.125,
+             dtype=1)
+    a.update(args)
+    rc = lib.attn_bwd_kv(*(a[n] or None for n in ("q", "k", "v", "o", "dout", "lse", "dq", "dk",
+                                                  "dv", "ws")),
+                         a["ws_bytes"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["causal"],
+                         a["scale"], a["dtype"], None)
     assert rc == code
 
 

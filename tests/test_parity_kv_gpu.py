@@ -7,6 +7,10 @@ tile multiples, Nq = Nk, Nq > 128 (several query tiles), both masks,
 d = 32, 64, 96, 128 and 256, scales 1.0 and 0.02 besides 1/sqrt(d), automatic and explicit split counts (including more splits than
 tiles, which the library caps), the decode workload at full size, agreement
 with attn_fwd when Nq = Nk, a 131077-key cache, and bitwise determinism.
+
+attn_bwd_kv (the backward of attn_fwd_kv) against oracle_attn_bwd_rect: the
+same (Nq, Nk) shapes and more, d = 32 ... 128, both masks, Nq > Nk without
+the mask, Nq = Nk bit for bit against attn_bwd, and the prefill workload.
 """
 import numpy as np
 import pytest
@@ -14,7 +18,8 @@ import torch
 
 import oracle
 from attn_inputs import KV_WORKLOADS, kv_workload_inputs, make_kv_inputs
-from tests.parity import compare, describe, f32_scale, gpu_forward, gpu_forward_kv, log, to_np
+from tests.parity import (compare, describe, f32_scale, gpu_backward, gpu_forward, gpu_forward_kv,
+                          log, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -123,3 +128,99 @@ def test_decode_long_cache(causal):
     """One query against a 131077-key cache (2049 key tiles, many splits)."""
     q, k, v = make_kv_inputs(1, 2, 1, 131077, 128, seed=41)
     _check(q, k, v, causal, 0, "decode Nk=131077 d=128")
+
+
+# ------------------------------------------------------------ attn_bwd_kv
+def gpu_backward_kv(q, k, v, o, lse, dout, causal, scale):
+    """CPU tensors in; attn_bwd_kv on the GPU into NaN-poisoned outputs with a
+    poisoned workspace; returns CPU dq, dk, dv."""
+    import tiled_online_softmax_attn_amd as T
+    dev = torch.device("cuda:0")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    qd, kd, vd, od, dod, ld = (t.to(dev) for t in (q, k, v, o, dout, lse))
+    ws = torch.full((T.attn_bwd_kv_workspace_bytes(B, H, Nq, Nk, d),), 0xFF, device=dev,
+                    dtype=torch.uint8)
+    dq = torch.full_like(qd, float("nan"))
+    dk = torch.full_like(kd, float("nan"))
+    dv = torch.full_like(vd, float("nan"))
+    T.attn_bwd_kv(qd, kd, vd, od, dod, ld, dq, dk, dv, ws, causal, scale)
+    torch.cuda.synchronize()
+    return dq.cpu(), dk.cpu(), dv.cpu()
+
+
+def _dout(B, H, Nq, d, seed):
+    g = torch.Generator("cpu")
+    g.manual_seed(int(seed))
+    return torch.randn(B, H, Nq, d, generator=g).to(torch.bfloat16)
+
+
+def _check_bwd(q, k, v, causal, tag, seed):
+    d = q.shape[-1]
+    scale = d ** -0.5
+    do = _dout(*q.shape, seed)
+    log(f"[bwd_kv] {tag} q={tuple(q.shape)} k={tuple(k.shape)} causal={causal}")
+    o, lse = gpu_forward_kv(q, k, v, causal, scale, 0)
+    dq, dk, dv = gpu_backward_kv(q, k, v, o, lse, do, causal, scale)
+    ref = oracle.attn_bwd_rect(to_np(q), to_np(k), to_np(v), to_np(do), causal, f32_scale(scale))
+    for name, got in (("dq", dq), ("dk", dk), ("dv", dv)):
+        e = compare(to_np(got), ref[name], torch.bfloat16, f"{tag} {name}")
+        log(f"    {name} {describe(e)}")
+
+
+@pytest.mark.parametrize("Nq,Nk", [(7, 100), (64, 64), (128, 1000), (200, 333), (130, 2049),
+                                   (1, 65), (33, 4097), (300, 300)])
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_shapes(Nq, Nk, d, causal):
+    """Backward of Nq queries at the end of Nk keys against the oracle's
+    rectangular gradient: query tiles that straddle the shifted diagonal,
+    ragged tails on both sides, a single query."""
+    q, k, v = make_kv_inputs(1, 2, Nq, Nk, d, seed=600 + Nq + Nk + d)
+    _check_bwd(q, k, v, causal, f"Nq={Nq} Nk={Nk} d={d}", seed=610 + Nq + d)
+
+
+@pytest.mark.parametrize("Nq,Nk", [(300, 100), (129, 64)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_more_queries_than_keys(Nq, Nk, d):
+    """Without the mask Nq may exceed Nk."""
+    q, k, v = make_kv_inputs(1, 2, Nq, Nk, d, seed=650 + Nq + d)
+    _check_bwd(q, k, v, False, f"Nq={Nq} > Nk={Nk} d={d}", seed=660 + Nq + d)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_square_equals_attn_bwd(causal, d):
+    """Nq = Nk runs the kernels of attn_bwd with the same offsets: bit for
+    bit the same gradients."""
+    q, k, v = make_kv_inputs(2, 3, 517, 517, d, seed=670 + d)
+    do = _dout(2, 3, 517, d, 671 + d)
+    scale = d ** -0.5
+    o, lse = gpu_forward(q, k, v, causal, scale)
+    a = gpu_backward(q, k, v, o, lse, do, causal, scale)
+    b = gpu_backward_kv(q, k, v, o, lse, do, causal, scale)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+def test_backward_prefill_workload():
+    """The prefill workload (B2 H16 Nq512 Nk4096 d128 causal): the sum
+    invariants on every head, the oracle on two whole heads."""
+    w = KV_WORKLOADS["prefill_b2_h16_nq512_nk4096_d128"]
+    q, k, v = kv_workload_inputs(w)
+    do = _dout(w.B, w.H, w.Nq, w.d, 690)
+    log(f"[bwd_kv] {w.name}")
+    o, lse = gpu_forward_kv(q, k, v, w.causal, w.scale, 0)
+    dq, dk, dv = gpu_backward_kv(q, k, v, o, lse, do, w.causal, w.scale)
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
+    sdv, sdo = dv.double().sum(2), do.double().sum(2)
+    assert torch.allclose(sdv, sdo, atol=2e-2 * w.Nk ** 0.5, rtol=1e-2)
+    sdk = dk.double().sum(2)
+    assert (sdk.abs() <= 2e-2 * w.Nk ** 0.5 + 1e-2 * dk.double().abs().sum(2)).all()
+    for b, h in [(0, 0), (1, 13)]:
+        ref = oracle.attn_bwd_rect(to_np(q[b, h]), to_np(k[b, h]), to_np(v[b, h]), to_np(do[b, h]),
+                                   w.causal, f32_scale(w.scale))
+        for name, got in (("dq", dq), ("dk", dk), ("dv", dv)):
+            e = compare(to_np(got[b, h]), ref[name], torch.bfloat16, f"{w.name} {name} b{b} h{h}")
+            log(f"    {name} b{b} h{h} {describe(e)}")

@@ -28,7 +28,8 @@ STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR
           -4: "ATTN_ERR_HEADDIM", -5: "ATTN_ERR_ALIGN", -6: "ATTN_ERR_SCALE",
           -7: "ATTN_ERR_WORKSPACE", -8: "ATTN_ERR_HIP", -9: "ATTN_ERR_SCRATCH"}
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_noalloc", "attn_bwd_phase", "attn_bwd_workspace_bytes",
-           "attn_fwd_kv", "attn_fwd_kv_workspace_bytes", "attn_softmax_rows", "attn_fwd_mx",
+           "attn_fwd_kv", "attn_fwd_kv_workspace_bytes", "attn_bwd_kv", "attn_bwd_kv_workspace_bytes",
+           "attn_softmax_rows", "attn_fwd_mx",
            "attn_status_str", "attn_abi_version")
 
 
@@ -71,6 +72,11 @@ def lib() -> ctypes.CDLL:
                                   ctypes.c_size_t, vp]
         L.attn_fwd_kv_workspace_bytes.restype = ctypes.c_size_t
         L.attn_fwd_kv_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+        L.attn_bwd_kv.restype = i
+        L.attn_bwd_kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                  i, i, i, i, i, i, f, i, vp]
+        L.attn_bwd_kv_workspace_bytes.restype = ctypes.c_size_t
+        L.attn_bwd_kv_workspace_bytes.argtypes = [i, i, i, i, i, i]
         L.attn_fwd_mx.restype = i
         L.attn_fwd_mx.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
         L.attn_softmax_rows.restype = i
@@ -249,6 +255,35 @@ def attn_fwd_kv(q, k, v, o, lse, causal: bool, scale: float, num_splits: int, wo
         raise AttnError(rc, "attn_fwd_kv")
 
 
+def attn_bwd_kv_workspace_bytes(B: int, H: int, Nq: int, Nk: int, d: int,
+                                dtype: torch.dtype = torch.bfloat16) -> int:
+    code = ATTN_DTYPE_BF16 if dtype == torch.bfloat16 else ATTN_DTYPE_F32
+    return int(lib().attn_bwd_kv_workspace_bytes(B, H, Nq, Nk, d, code))
+
+
+def attn_bwd_kv(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool, scale: float,
+                stream=None) -> None:
+    """Enqueue the backward of attn_fwd_kv: q, o, dout, dq [B, H, Nq, d]; k, v,
+    dk, dv [B, H, Nk, d]; lse [B, H, Nq]; the queries are the last Nq
+    positions.  ``workspace``: at least attn_bwd_kv_workspace_bytes() bytes."""
+    _check_contig(q, k, v, o, dout, lse, dq, dk, dv)
+    B, H, Nq, d = _shape(q)
+    if not isinstance(k, torch.Tensor) or k.dim() != 4:
+        raise ValueError("attn_bwd_kv: k must be a [B, H, Nk, d] tensor")
+    Nk = int(k.shape[2])
+    for name, t, n in (("k", k, Nk), ("v", v, Nk), ("dk", dk, Nk), ("dv", dv, Nk), ("o", o, Nq),
+                       ("dout", dout, Nq), ("dq", dq, Nq)):
+        _check(f"attn_bwd_kv {name}", t, (B, H, n, d), (q.dtype,), q.device)
+    _check("attn_bwd_kv lse", lse, (B, H, Nq), (torch.float32,), q.device)
+    _check_workspace("attn_bwd_kv", workspace, q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().attn_bwd_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                           _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, B, H, Nq, Nk, d,
+                           int(bool(causal)), float(scale), _dtype_code(q), _stream_handle(stream))
+    if rc != 0:
+        raise AttnError(rc, "attn_bwd_kv")
+
+
 def attn_fwd_mx(q8, q_scale, k8, k_scale, v, o, lse, causal: bool, scale: float,
                 stream=None) -> None:
     """Enqueue the forward with Q and K in MXFP8: q8, k8 E4M3 codes [B, H, N,
@@ -328,4 +363,20 @@ def flash_attention_backward(q, k, v, o, lse, dout, causal: bool = False,
                                 dtype=torch.uint8)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal, scale)
+    return dq, dk, dv
+
+
+def flash_attention_backward_kv(q, k, v, o, lse, dout, causal: bool = False,
+                                scale: float | None = None, workspace=None):
+    """Allocate dq, dk, dv (and a workspace if none is given) and run
+    attn_bwd_kv."""
+    B, H, Nq, d = _shape(q)
+    Nk = int(k.shape[2])
+    if scale is None:
+        scale = d ** -0.5
+    if workspace is None:
+        workspace = torch.empty(attn_bwd_kv_workspace_bytes(B, H, Nq, Nk, d, q.dtype),
+                                device=q.device, dtype=torch.uint8)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    attn_bwd_kv(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal, scale)
     return dq, dk, dv

@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 5;
+constexpr int kAbiVersion = 6;
 
 // Device scratch of attn_bwd_noalloc: the D vector (one fp32 per query row)
 // that attn_bwd keeps in the caller's workspace.  16 MiB per GPU, so
@@ -67,8 +67,8 @@ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
 
 namespace attn {
-size_t bwd_delta_bytes(int B, int H, int N) {
-  return round256((size_t)B * (size_t)H * (size_t)N * sizeof(float));
+size_t bwd_delta_bytes(int B, int H, int Nq) {
+  return round256((size_t)B * (size_t)H * (size_t)Nq * sizeof(float));
 }
 }  // namespace attn
 
@@ -143,7 +143,7 @@ static int bwd_common(int phase, const void* q, const void* k, const void* v, co
   const size_t need = attn_bwd_workspace_bytes(B, H, N, d, dtype);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
-  attn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, B, H, N, d,
+  attn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, B, H, N, N, d,
                   causal != 0, scale, stream};
   const hipError_t e = phase < 0 ? attn::launch_bwd(a) : attn::launch_bwd_phase(a, phase);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
@@ -169,7 +169,7 @@ int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
   if (rc != ATTN_OK) return rc;
   // the same three kernels as attn_bwd; phase 0 writes every D entry that
   // phases 1 and 2 read, so nothing in the scratch needs clearing
-  attn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, (float*)ws, B, H, N, d, causal != 0,
+  attn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, (float*)ws, B, H, N, N, d, causal != 0,
                   scale, stream};
   return attn::launch_bwd(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
@@ -223,6 +223,35 @@ int attn_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse
   attn::FwdKvArgs a{q, k, v, o, lse, B, H, Nq, Nk, d, causal != 0, scale, num_splits,
                     workspace, stream};
   return attn::launch_fwd_kv(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+size_t attn_bwd_kv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype) {
+  if (check_kv_shape(B, H, Nq, Nk, d, 0, 0) != ATTN_OK || !attn::bwd_head_dim_supported(d) ||
+      dtype != ATTN_DTYPE_BF16)
+    return 0;
+  return attn::bwd_delta_bytes(B, H, Nq);
+}
+
+int attn_bwd_kv(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                size_t workspace_bytes, int B, int H, int Nq, int Nk, int d, int causal,
+                float scale, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL;
+  int rc = check_kv_shape(B, H, Nq, Nk, d, causal, 0);
+  if (rc != ATTN_OK) return rc;
+  if (!attn::bwd_head_dim_supported(d)) return ATTN_ERR_HEADDIM;
+  if (dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
+  const void* ptrs[] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return ATTN_ERR_ALIGN;
+  if (!aligned4(lse)) return ATTN_ERR_ALIGN;
+  if (!scale_ok(scale)) return ATTN_ERR_SCALE;
+  const size_t need = attn_bwd_kv_workspace_bytes(B, H, Nq, Nk, d, dtype);
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+  attn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, B, H, Nq, Nk, d,
+                  causal != 0, scale, stream};
+  return attn::launch_bwd(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 int attn_fwd_mx(const void* q8, const void* q_scale, const void* k8, const void* k_scale,

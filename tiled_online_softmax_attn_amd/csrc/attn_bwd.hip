@@ -14,6 +14,10 @@
 //            dV of a 128-key block stay in registers for the whole kernel.
 //   phase 2  bwd_dq:    query blocks outside, key/value blocks inside (the
 //            forward's schedule): dQ of a 128-query block stays in registers.
+// The queries may be the last Nq positions of an Nk-key sequence (the
+// backward of attention over a key/value cache): query i then sees keys
+// 0 .. i + off under the causal mask, off = Nk - Nq (0 for square attention).
+//
 // Splitting dQ from dK/dV recomputes S and dP once more (7 block products
 // instead of 5) but removes every cross-workgroup reduction: on this chip a
 // device-wide fp32 atomic add is carried out past the per-XCD L2, and the
@@ -82,8 +86,8 @@ __global__ void __launch_bounds__(kBwdThreads, D <= 64 ? 2 : 1)
 bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 const __bf16* __restrict__ v, const __bf16* __restrict__ dout,
                 const float* __restrict__ lse, const float* __restrict__ delta,
-                __bf16* __restrict__ dk, __bf16* __restrict__ dv, int BH, int N, float scale,
-                float scale_log2) {
+                __bf16* __restrict__ dk, __bf16* __restrict__ dv, int BH, int Nq, int Nk,
+                int off, float scale, float scale_log2) {
   using Tile = SwzTile<tile_width(D), D>;
   static_assert(kKvBQ == Tile::kRows, "query tile is one SwzTile");
   constexpr int KS = D / 16;  // k-steps over d
@@ -107,11 +111,12 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // under the causal mask, so they are issued first
   const int kblk = blockIdx.x / BH;
   const int bh = blockIdx.x - kblk * BH;
-  const int64_t head = (int64_t)bh * N * D;
-  const __bf16* qh = q + head;
-  const __bf16* doh = dout + head;
-  const float* lse_h = lse + (int64_t)bh * N;
-  const float* del_h = delta + (int64_t)bh * N;
+  const int64_t qhead = (int64_t)bh * Nq * D;
+  const int64_t khead = (int64_t)bh * Nk * D;
+  const __bf16* qh = q + qhead;
+  const __bf16* doh = dout + qhead;
+  const float* lse_h = lse + (int64_t)bh * Nq;
+  const float* del_h = delta + (int64_t)bh * Nq;
 
   const int key_wg0 = kblk * kKvBK;
   const int key_w0 = key_wg0 + wave * 32;  // first key of this wave
@@ -121,9 +126,9 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   bf16x8 kf[KS], vf[KS];
   {
     const bf16x8 zero = {};
-    const bool ok = key < N;
-    const __bf16* krow = k + head + (int64_t)(ok ? key : 0) * D + half * 8;
-    const __bf16* vrow = v + head + (int64_t)(ok ? key : 0) * D + half * 8;
+    const bool ok = key < Nk;
+    const __bf16* krow = k + khead + (int64_t)(ok ? key : 0) * D + half * 8;
+    const __bf16* vrow = v + khead + (int64_t)(ok ? key : 0) * D + half * 8;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       kf[s] = ok ? *reinterpret_cast<const bf16x8*>(krow + 16 * s) : zero;
@@ -131,8 +136,9 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
   }
 
-  const int n_qtiles = (N + kKvBQ - 1) / kKvBQ;
-  const int qt_begin = CAUSAL ? key_wg0 / kKvBQ : 0;
+  const int n_qtiles = (Nq + kKvBQ - 1) / kKvBQ;
+  // the first query that sees key key_wg0 is key_wg0 - off
+  const int qt_begin = CAUSAL ? max(key_wg0 - off, 0) / kKvBQ : 0;
 
   // Q and dO tiles go straight to LDS buffer B; L and D pass through one
   // register each on the first 64 threads (L is scaled to log2 units only
@@ -145,12 +151,12 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     return (ATTN_LDS unsigned char*)(decltype(buf_tag)::value ? lds_do1 : lds_do0);
   };
   auto load_tile = [&](int qt, auto buf_tag) {
-    Tile::template load<kBwdThreads / 64>(qh, qt * kKvBQ, N, q_lds(buf_tag), wave, lane);
-    Tile::template load<kBwdThreads / 64>(doh, qt * kKvBQ, N, do_lds(buf_tag), wave, lane);
+    Tile::template load<kBwdThreads / 64>(qh, qt * kKvBQ, Nq, q_lds(buf_tag), wave, lane);
+    Tile::template load<kBwdThreads / 64>(doh, qt * kKvBQ, Nq, do_lds(buf_tag), wave, lane);
     if (tid < kKvBQ) {
       const int qq = qt * kKvBQ + tid;
-      rl = qq < N ? lse_h[qq] : 0.f;
-      rd = qq < N ? del_h[qq] : 0.f;
+      rl = qq < Nq ? lse_h[qq] : 0.f;
+      rd = qq < Nq ? del_h[qq] : 0.f;
     }
   };
   auto store_stats = [&](auto buf_tag) {
@@ -194,15 +200,15 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     if (qt + 1 < n_qtiles) load_tile(qt + 1, Next{});
 
     const int q0 = qt * kKvBQ;
-    // wave-uniform: every query of the tile precedes every key of this wave
-    const bool skip = CAUSAL && (q0 + kKvBQ - 1 < key_w0);
+    // wave-uniform: no query of the tile sees any key of this wave
+    const bool skip = CAUSAL && (q0 + kKvBQ - 1 + off < key_w0);
     if (!skip) {
       const ATTN_LDS unsigned char* qs = q_lds(cur_tag);
       const ATTN_LDS unsigned char* dos = do_lds(cur_tag);
       const float* lq = lds_stats[CUR][0];
       const float* dq_d = lds_stats[CUR][1];
       const bool need_mask =
-          (q0 + kKvBQ > N) || (key_w0 + 32 > N) || (CAUSAL && q0 < key_w0 + 31);
+          (q0 + kKvBQ > Nq) || (key_w0 + 32 > Nk) || (CAUSAL && q0 + off < key_w0 + 31);
 
       // The tile's 64 queries are two 32-query blocks qb = 0, 1.  The issue
       // order is software-pipelined across them so that MFMA and VALU work
@@ -223,9 +229,9 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       struct Stats { float4 l, d; };     // L and D of 4 query rows
       // k-step s of S = Q K^T and dP = dO V^T for block qb
       auto read_row = [&](int qb, int s) {
-        const int off = (rd_base ^ (32 * s)) + qb * 32 * RB;
-        return RowFrag{*reinterpret_cast<const ATTN_LDS bf16x8*>(qs + off),
-                       *reinterpret_cast<const ATTN_LDS bf16x8*>(dos + off)};
+        const int at = (rd_base ^ (32 * s)) + qb * 32 * RB;
+        return RowFrag{*reinterpret_cast<const ATTN_LDS bf16x8*>(qs + at),
+                       *reinterpret_cast<const ATTN_LDS bf16x8*>(dos + at)};
       };
       auto mma_sdp = [&](int qb, int s, const RowFrag& f) {
         sacc[qb] = mfma_32x32x16(f.q, kf[s], sacc[qb]);
@@ -264,7 +270,7 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
           float p = fast_exp2(fmaf(sacc[qb][i], scale_log2, -lv[e]));
           if constexpr (MASK) {
             const int qq = q0 + qb * 32 + r * 8 + half * 4 + e;
-            if (qq >= N || key >= N || (CAUSAL && key > qq)) p = 0.f;
+            if (qq >= Nq || key >= Nk || (CAUSAL && key > qq + off)) p = 0.f;
           }
           // keep the exponential at this point of the issue order
           __asm__ volatile("" ::"v"(p));
@@ -363,10 +369,10 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int kk = key_w0 + (i >> 2) * 8 + half * 4 + (i & 3);
-      if (kk < N) {
-        const int64_t off = head + (int64_t)kk * D + b * 32 + l32;
-        dk[off] = (__bf16)(dk_acc[b][i] * scale);
-        dv[off] = (__bf16)dv_acc[b][i];
+      if (kk < Nk) {
+        const int64_t at = khead + (int64_t)kk * D + b * 32 + l32;
+        dk[at] = (__bf16)(dk_acc[b][i] * scale);
+        dv[at] = (__bf16)dv_acc[b][i];
       }
     }
 }
@@ -380,8 +386,8 @@ __global__ void __launch_bounds__(kBwdThreads, 2)
 bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
               const __bf16* __restrict__ v, const __bf16* __restrict__ dout,
               const float* __restrict__ lse, const float* __restrict__ delta,
-              __bf16* __restrict__ dq, int BH, int N, int n_qtiles, float scale,
-              float scale_log2) {
+              __bf16* __restrict__ dq, int BH, int Nq, int Nk, int off, int n_qtiles,
+              float scale, float scale_log2) {
   using Tile = SwzTile<tile_width(D), D>;
   static_assert(kDqBK == Tile::kRows, "key tile is one SwzTile");
   constexpr int KS = D / 16;
@@ -414,34 +420,37 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int rank = blockIdx.x / BH;
   const int bh = blockIdx.x - rank * BH;
   const int qt = CAUSAL ? (n_qtiles - 1 - rank) : rank;
-  const int64_t head = (int64_t)bh * N * D;
-  const __bf16* kh = k + head;
-  const __bf16* vh = v + head;
+  const int64_t qhead = (int64_t)bh * Nq * D;
+  const int64_t khead = (int64_t)bh * Nk * D;
+  const __bf16* kh = k + khead;
+  const __bf16* vh = v + khead;
 
   const int q_wave0 = qt * kDqBQ + wave * 32;
   const int qry = q_wave0 + l32;
-  const bool qok = qry < N;
+  const bool qok = qry < Nq;
 
   // Q^T and dO^T fragments (B operand): lane holds X[qry][16 s + 8 half + e]
   bf16x8 qf[KS], df[KS];
   {
     const bf16x8 zero = {};
-    const int64_t roff = head + (int64_t)(qok ? qry : 0) * D + half * 8;
+    const int64_t roff = qhead + (int64_t)(qok ? qry : 0) * D + half * 8;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       qf[s] = qok ? *reinterpret_cast<const bf16x8*>(q + roff + 16 * s) : zero;
       df[s] = qok ? *reinterpret_cast<const bf16x8*>(dout + roff + 16 * s) : zero;
     }
   }
-  const float lq2 = qok ? lse[(int64_t)bh * N + qry] * kLog2e : 0.f;
-  const float dlt = qok ? delta[(int64_t)bh * N + qry] : 0.f;
+  const float lq2 = qok ? lse[(int64_t)bh * Nq + qry] * kLog2e : 0.f;
+  const float dlt = qok ? delta[(int64_t)bh * Nq + qry] : 0.f;
 
-  const int kv_end = CAUSAL ? min(N, (qt + 1) * kDqBQ) : N;
+  // keys past the last one the workgroup's last query sees are not visited
+  const int kv_end =
+      CAUSAL ? (int)min((int64_t)Nk, (int64_t)(qt + 1) * kDqBQ + off) : Nk;
   const int n_tiles = (kv_end + kDqBK - 1) / kDqBK;
 
   auto load_tile = [&](int j, auto buf_tag) {
-    Tile::template load<kBwdThreads / 64>(kh, j * kDqBK, N, k_lds(buf_tag), wave, lane);
-    Tile::template load<kBwdThreads / 64>(vh, j * kDqBK, N, v_lds(buf_tag), wave, lane);
+    Tile::template load<kBwdThreads / 64>(kh, j * kDqBK, Nk, k_lds(buf_tag), wave, lane);
+    Tile::template load<kBwdThreads / 64>(vh, j * kDqBK, Nk, v_lds(buf_tag), wave, lane);
   };
   const int rd_base = Tile::row_read_base(l32, half);
   const int tr_lo = Tile::tr_read_base(lane, false);
@@ -461,11 +470,12 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     using Next = std::integral_constant<int, 1 - decltype(cur_tag)::value>;
     if (j + 1 < n_tiles) load_tile(j + 1, Next{});
     const int key0 = j * kDqBK;
-    const bool skip = CAUSAL && key0 > q_wave0 + 31;
+    const bool skip = CAUSAL && key0 > q_wave0 + 31 + off;
     if (!skip) {
       const ATTN_LDS unsigned char* ks = k_lds(cur_tag);
       const ATTN_LDS unsigned char* vs = v_lds(cur_tag);
-      const bool need_mask = (key0 + kDqBK > N) || (CAUSAL && key0 + kDqBK - 1 > q_wave0);
+      const bool need_mask =
+          (key0 + kDqBK > Nk) || (CAUSAL && key0 + kDqBK - 1 > q_wave0 + off);
 
       if constexpr (kPipelineHalves) {
         // The tile's 64 keys are two 32-key halves kb = 0, 1, software-
@@ -482,10 +492,10 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 
         // S^T = K Q^T and dP^T = V dO^T, k-step s of half kb
         auto sdp_step = [&](int kb, int s) {
-          const int off = (rd_base ^ (32 * s)) + kb * 32 * RB;
-          const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(ks + off);
+          const int at = (rd_base ^ (32 * s)) + kb * 32 * RB;
+          const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(ks + at);
           sacc[kb] = mfma_32x32x16(a, qf[s], sacc[kb]);
-          const bf16x8 b = *reinterpret_cast<const ATTN_LDS bf16x8*>(vs + off);
+          const bf16x8 b = *reinterpret_cast<const ATTN_LDS bf16x8*>(vs + at);
           pacc[kb] = mfma_32x32x16(b, df[s], pacc[kb]);
         };
         // P^T = 2^{S^T scale log2e - L}, dS^T = P^T (dP^T - D) for accumulator
@@ -498,7 +508,7 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             float p = fast_exp2(fmaf(sacc[kb][i], scale_log2, -lq2));
             if constexpr (MASK) {
               const int kk = key0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-              if (kk >= N || (CAUSAL && kk > qry)) p = 0.f;
+              if (kk >= Nk || (CAUSAL && kk > qry + off)) p = 0.f;
             }
             // keep the exponential at this point of the issue order
             __asm__ volatile("" ::"v"(p));
@@ -552,9 +562,9 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         struct RowFrag { bf16x8 k, v; };
         auto read_row = [&](int u) {
           const int s = u >> 1, kb = u & 1;
-          const int off = (rd_base ^ (32 * s)) + kb * 32 * RB;
-          return RowFrag{*reinterpret_cast<const ATTN_LDS bf16x8*>(ks + off),
-                         *reinterpret_cast<const ATTN_LDS bf16x8*>(vs + off)};
+          const int at = (rd_base ^ (32 * s)) + kb * 32 * RB;
+          return RowFrag{*reinterpret_cast<const ATTN_LDS bf16x8*>(ks + at),
+                         *reinterpret_cast<const ATTN_LDS bf16x8*>(vs + at)};
         };
         RowFrag rf[2];
         rf[0] = read_row(0);
@@ -576,7 +586,7 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             float p = fast_exp2(fmaf(sacc[kb][i], scale_log2, -lq2));
             if (need_mask) {
               const int kk = key0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-              if (kk >= N || (CAUSAL && kk > qry)) p = 0.f;
+              if (kk >= Nk || (CAUSAL && kk > qry + off)) p = 0.f;
             }
             sf[kb][i >> 3][i & 7] = (__bf16)(p * (pacc[kb][i] - dlt));
           }
@@ -611,7 +621,7 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 
   // ---- dQ = scale * acc: lane holds query qry, d rows b*32 + (i/4)*8 + half*4 + i%4
   if (qok) {
-    __bf16* row = dq + head + (int64_t)qry * D;
+    __bf16* row = dq + qhead + (int64_t)qry * D;
 #pragma unroll
     for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -629,24 +639,25 @@ template <int D>
 hipError_t launch_phase(const BwdArgs& a, int phase) {
   const int BH = a.B * a.H;
   const hipStream_t s = (hipStream_t)a.stream;
+  const int off = a.causal ? a.Nk - a.Nq : 0;
   if (phase == 0) {
-    const int64_t rows = (int64_t)BH * a.N;
+    const int64_t rows = (int64_t)BH * a.Nq;
     hipLaunchKernelGGL(bwd_preprocess_kernel<D>, dim3((unsigned)((rows + 31) / 32)), dim3(256),
                        0, s, (const __bf16*)a.o, (const __bf16*)a.dout, a.delta, rows);
   } else if (phase == 1) {
-    const int nkb = (a.N + kKvBK - 1) / kKvBK;
+    const int nkb = (a.Nk + kKvBK - 1) / kKvBK;
     auto kern = a.causal ? bwd_dkdv_kernel<D, true> : bwd_dkdv_kernel<D, false>;
     hipLaunchKernelGGL(kern, dim3((unsigned)(BH * nkb)), dim3(kBwdThreads), 0, s,
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
                        (const __bf16*)a.dout, a.lse, a.delta, (__bf16*)a.dk, (__bf16*)a.dv, BH,
-                       a.N, a.scale, a.scale * kLog2e);
+                       a.Nq, a.Nk, off, a.scale, a.scale * kLog2e);
   } else {
-    const int nqt = (a.N + kDqBQ - 1) / kDqBQ;
+    const int nqt = (a.Nq + kDqBQ - 1) / kDqBQ;
     auto kern = a.causal ? bwd_dq_kernel<D, true> : bwd_dq_kernel<D, false>;
     hipLaunchKernelGGL(kern, dim3((unsigned)(BH * nqt)), dim3(kBwdThreads), 0, s,
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
-                       (const __bf16*)a.dout, a.lse, a.delta, (__bf16*)a.dq, BH, a.N, nqt,
-                       a.scale, a.scale * kLog2e);
+                       (const __bf16*)a.dout, a.lse, a.delta, (__bf16*)a.dq, BH, a.Nq, a.Nk, off,
+                       nqt, a.scale, a.scale * kLog2e);
   }
   return hipGetLastError();
 }

@@ -28,18 +28,22 @@ struct FwdArgs {
   void* stream;
 };
 
+// Backward of Nq queries against Nk keys and values.  Square attention
+// (attn_bwd) has Nq = Nk = N; the backward of attn_fwd_kv (attn_bwd_kv) has
+// the queries at the last Nq positions, so under the causal mask query i
+// sees keys 0 .. i + Nk - Nq.
 struct BwdArgs {
-  const void* q;
-  const void* k;
-  const void* v;
-  const void* o;
-  const void* dout;
-  const float* lse;
-  void* dq;
-  void* dk;
-  void* dv;
-  float* delta;  // [B][H][N] fp32 workspace: D = rowsum(dO * O)
-  int B, H, N, d;
+  const void* q;     // [B][H][Nq][d]
+  const void* k;     // [B][H][Nk][d]
+  const void* v;     // [B][H][Nk][d]
+  const void* o;     // [B][H][Nq][d]
+  const void* dout;  // [B][H][Nq][d]
+  const float* lse;  // [B][H][Nq]
+  void* dq;          // [B][H][Nq][d]
+  void* dk;          // [B][H][Nk][d]
+  void* dv;          // [B][H][Nk][d]
+  float* delta;  // [B][H][Nq] fp32 workspace: D = rowsum(dO * O)
+  int B, H, Nq, Nk, d;
   int causal;
   float scale;
   void* stream;
@@ -106,7 +110,8 @@ hipError_t launch_bwd(const BwdArgs& a);
 // phase 0 = preprocess (D), 1 = dK and dV, 2 = dQ
 hipError_t launch_bwd_phase(const BwdArgs& a, int phase);
 
-// Workspace of the backward: the D vector, rounded up to 256 bytes.
-size_t bwd_delta_bytes(int B, int H, int N);
+// Workspace of the backward: the D vector (one fp32 per query row), rounded
+// up to 256 bytes.
+size_t bwd_delta_bytes(int B, int H, int Nq);
 
 }  // namespace attn
