@@ -9,8 +9,7 @@ GPU, and resident in HBM before the timed region starts.
 
 With `--workload` naming another attention shape (attn_inputs.WORKLOADS or
 HEADDIM_WORKLOADS, e.g. b4_h16_n4096_d96_causal) a step is the same pass on
-that shape; at d = 256 and in fp32, where no backward is built, the forward
-alone.
+that shape; in fp32, where no backward is built, the forward alone.
 
 With `--workload` naming a key/value-cache shape (attn_inputs.KV_WORKLOADS,
 e.g. decode_b8_h32_nq1_nk8192_d128) a step is instead one attn_fwd_kv call
@@ -708,9 +707,8 @@ def main():
         bench_mx(args, MX_WORKLOADS[args.workload])
         return
     w = {**WORKLOADS, **HEADDIM_WORKLOADS}[args.workload or HEADLINE]
-    # the backward is built for bf16 with d <= 128; otherwise a step is the
-    # forward alone
-    backward = w.d <= 128 and w.dtype == torch.bfloat16
+    # the backward is built for bf16; in fp32 a step is the forward alone
+    backward = w.dtype == torch.bfloat16
     run_kernels = KERNELS if backward else KERNELS[:1]
     T.lib()
     dev = torch.device("cuda:0")

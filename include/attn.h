@@ -28,7 +28,7 @@
  *   and > 0, otherwise ATTN_ERR_SCALE (0, -0.0 and negative values included).
  *   Results are finite as long as scale * |q_i . k_j| fits fp32.
  * - N may be any value >= 1 (no tile multiple is required); d must be 32, 64,
- *   96, 128 or 256 (the backward: 32, 64, 96 or 128).  bf16 is supported by
+ *   96, 128 or 256, in every entry point but attn_fwd_mx.  bf16 is supported by
  *   every entry point; fp32 by the forward only.
  * - The caller owns every buffer (including the backward workspace).  The
  *   library never allocates, frees or synchronises; it enqueues kernels on
@@ -62,7 +62,7 @@ typedef enum {
   ATTN_ERR_NULL = -1,      /* a required pointer is NULL */
   ATTN_ERR_SHAPE = -2,     /* B, H or N < 1, or sizes overflow 64-bit offsets */
   ATTN_ERR_DTYPE = -3,     /* unknown dtype, or dtype not supported by this entry point */
-  ATTN_ERR_HEADDIM = -4,   /* d is not 32, 64, 96, 128 or 256 (backward: <= 128) */
+  ATTN_ERR_HEADDIM = -4,   /* d is not 32, 64, 96, 128 or 256 (attn_fwd_mx: 64, 128) */
   ATTN_ERR_ALIGN = -5,     /* a pointer is not 16-byte aligned (lse: 4-byte) */
   ATTN_ERR_SCALE = -6,     /* scale is not finite, or not > 0 */
   ATTN_ERR_WORKSPACE = -7, /* workspace NULL or smaller than attn_bwd_workspace_bytes() */
@@ -188,7 +188,7 @@ size_t attn_bwd_kv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtyp
  *                    then requires Nk >= Nq; 0 lets every query see every key.
  *   workspace      : at least attn_bwd_kv_workspace_bytes() bytes, caller-
  *                    owned, contents on entry ignored.
- * Nq = Nk is attn_bwd, bit for bit (the same kernels).  d <= 128, bf16.
+ * Nq = Nk is attn_bwd, bit for bit (the same kernels).  bf16.
  * Every output element is written once (no atomics).  Errors: those of
  * attn_fwd_kv and attn_bwd.  Calls that share a workspace must not overlap. */
 int attn_bwd_kv(const void* q, const void* k, const void* v, const void* o, const void* dout,

@@ -84,7 +84,8 @@ def test_workspace_size():
     assert need <= n <= need + 256
     assert lib.attn_bwd_workspace_bytes(0, 1, 1, 64, 1) == 0
     assert lib.attn_bwd_workspace_bytes(1, 1, 1, 80, 1) == 0
-    assert lib.attn_bwd_workspace_bytes(1, 1, 1, 256, 1) == 0  # backward d <= 128
+    assert lib.attn_bwd_workspace_bytes(1, 1, 1, 256, 1) == 256  # d = 256 has a backward
+    assert lib.attn_bwd_workspace_bytes(1, 1, 1, 512, 1) == 0
     assert lib.attn_bwd_workspace_bytes(1, 1, 1, 64, 0) == 0  # fp32 backward unsupported
 
 
@@ -117,7 +118,8 @@ def test_fwd_validation(args, code):
 
 
 @pytest.mark.parametrize("args,code", [
-    (dict(dout=0), -1), (dict(dtype=0), -3), (dict(N=0), -2), (dict(d=80), -4), (dict(d=256), -4),
+    (dict(dout=0), -1), (dict(dtype=0), -3), (dict(N=0), -2), (dict(d=80), -4), (dict(d=512), -4),
+    (dict(d=256, scale=0.0), -6),
     (dict(ws=0), -7), (dict(ws_bytes=16), -7), (dict(dk=FAKE + 4), -5),
     (dict(lse=FAKE + 2), -5),
     (dict(scale=float("-inf")), -6), (dict(scale=0.0), -6), (dict(scale=-0.0), -6),
@@ -137,7 +139,8 @@ def test_bwd_validation(args, code):
 
 @pytest.mark.parametrize("args,code", [
     (dict(dout=0), -1), (dict(lse=0), -1), (dict(dtype=0), -3), (dict(N=0), -2),
-    (dict(d=80), -4), (dict(d=256), -4), (dict(dk=FAKE + 4), -5), (dict(lse=FAKE + 2), -5),
+    (dict(d=80), -4), (dict(d=512), -4), (dict(d=256, scale=0.0), -6), (dict(dk=FAKE + 4), -5),
+    (dict(lse=FAKE + 2), -5),
     (dict(scale=0.0), -6), (dict(scale=float("nan")), -6),
     # above the 16 MiB static scratch (4194304 query rows), refused before any
     # device call
@@ -214,14 +217,15 @@ def test_bwd_kv_workspace_size():
     lib = _lib()
     assert lib.attn_bwd_kv_workspace_bytes(2, 16, 512, 4096, 128, 1) == 2 * 16 * 512 * 4
     assert lib.attn_bwd_kv_workspace_bytes(1, 3, 7, 100, 64, 1) == 256  # 84 bytes, rounded
-    assert lib.attn_bwd_kv_workspace_bytes(1, 1, 7, 100, 256, 1) == 0  # backward d <= 128
+    assert lib.attn_bwd_kv_workspace_bytes(1, 1, 7, 100, 256, 1) == 256
+    assert lib.attn_bwd_kv_workspace_bytes(1, 1, 7, 100, 80, 1) == 0
     assert lib.attn_bwd_kv_workspace_bytes(1, 1, 7, 100, 64, 0) == 0  # bf16 only
     assert lib.attn_bwd_kv_workspace_bytes(1, 1, 0, 100, 64, 1) == 0
 
 
 @pytest.mark.parametrize("args,code", [
     (dict(q=0), -1), (dict(dv=0), -1), (dict(B=0), -2), (dict(Nq=0), -2), (dict(Nk=0), -2),
-    (dict(Nq=20, Nk=10, causal=1), -2), (dict(d=48), -4), (dict(d=256), -4),
+    (dict(Nq=20, Nk=10, causal=1), -2), (dict(d=48), -4), (dict(d=256, scale=0.0), -6),
     (dict(dtype=0), -3), (dict(dk=FAKE + 4), -5), (dict(lse=FAKE + 2), -5),
     (dict(scale=0.0), -6), (dict(scale=-1.0), -6), (dict(scale=float("inf")), -6),
     (dict(lse=FAKE + 4, scale=0.0), -6),

@@ -8,8 +8,7 @@ Coverage:
   shape at d = 96, 32 and 256 (forward only at 256), and B4 H16 N4001 d128
   causal (tail tiles on both loops, forward and backward);
 * ragged N (tails that span several tiles), N = 1, both masks,
-  d = 32 / 64 / 96 / 128 / 256 (forward, fp32 and bf16) and d <= 128
-  (backward);
+  d = 32 / 64 / 96 / 128 / 256 (forward, fp32 and bf16; backward, bf16);
 * closed forms with exactly representable inputs (Q = 0);
 * the dV / dK sum invariants of the backward at full size;
 * scales other than 1/sqrt(d) (1.0 and 0.02) on causal and unmasked ragged
@@ -73,7 +72,7 @@ def test_ragged_forward(N, d, causal, dtype):
 
 
 @pytest.mark.parametrize("N", [1, 17, 100, 257, 1000])
-@pytest.mark.parametrize("d", [32, 64, 96, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_ragged_backward(N, d, causal):
     q, k, v, do = make_inputs(1, 2, N, d, torch.bfloat16, seed=200 + N + d, with_dout=True)
@@ -143,7 +142,7 @@ def test_forward_other_scales_f32(scale, N, d, causal):
 
 
 @pytest.mark.parametrize("scale", [1.0, 0.02])
-@pytest.mark.parametrize("N,d", [(100, 32), (257, 64), (255, 96), (300, 128)])
+@pytest.mark.parametrize("N,d", [(100, 32), (257, 64), (255, 96), (300, 128), (130, 256)])
 @pytest.mark.parametrize("causal", [True, False])
 def test_backward_other_scales(scale, N, d, causal):
     q, k, v, do = make_inputs(1, 2, N, d, torch.bfloat16, seed=500 + N + d, with_dout=True)
@@ -169,7 +168,7 @@ def test_forward_is_deterministic():
     assert torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_backward_is_deterministic(d):
     """attn_bwd writes every gradient element exactly once (no atomics), so
     two calls on the same inputs and workspace agree bit for bit; d = 64 and
@@ -244,6 +243,7 @@ def test_full_size_forward_sampled_rows(name, heads):
     ("b4_h16_n4001_d128_causal", [(1, 6)]),
     ("b4_h16_n4096_d96_causal", [(2, 5)]),
     ("b4_h16_n4096_d32_causal", [(1, 3)]),
+    ("b4_h16_n4096_d256_causal", [(2, 7)]),
 ])
 def test_fwdbwd_workload_backward(name, heads):
     w = {**WORKLOADS, **HEADDIM_WORKLOADS}[name]

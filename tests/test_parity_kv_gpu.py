@@ -9,7 +9,7 @@ tiles, which the library caps), the decode workload at full size, agreement
 with attn_fwd when Nq = Nk, a 131077-key cache, and bitwise determinism.
 
 attn_bwd_kv (the backward of attn_fwd_kv) against oracle_attn_bwd_rect: the
-same (Nq, Nk) shapes and more, d = 32 ... 128, both masks, Nq > Nk without
+same (Nq, Nk) shapes and more, d = 32 ... 256, both masks, Nq > Nk without
 the mask, Nq = Nk bit for bit against attn_bwd, and the prefill workload.
 """
 import numpy as np
@@ -170,7 +170,7 @@ def _check_bwd(q, k, v, causal, tag, seed):
 
 @pytest.mark.parametrize("Nq,Nk", [(7, 100), (64, 64), (128, 1000), (200, 333), (130, 2049),
                                    (1, 65), (33, 4097), (300, 300)])
-@pytest.mark.parametrize("d", [32, 64, 96, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_backward_shapes(Nq, Nk, d, causal):
     """Backward of Nq queries at the end of Nk keys against the oracle's

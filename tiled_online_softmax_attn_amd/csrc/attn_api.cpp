@@ -83,7 +83,7 @@ const char* attn_status_str(int status) {
     case ATTN_ERR_SHAPE: return "B, H and N must be >= 1 and the sizes must fit 64-bit offsets";
     case ATTN_ERR_DTYPE: return "dtype not supported by this entry point";
     case ATTN_ERR_HEADDIM:
-      return "head dimension d must be 32, 64, 96, 128 or 256 (backward: at most 128)";
+      return "head dimension d must be 32, 64, 96, 128 or 256 (attn_fwd_mx: 64 or 128)";
     case ATTN_ERR_ALIGN: return "pointers must be 16-byte aligned (lse: 4-byte)";
     case ATTN_ERR_SCALE: return "scale must be finite and > 0";
     case ATTN_ERR_WORKSPACE:

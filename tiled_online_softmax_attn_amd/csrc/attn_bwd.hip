@@ -79,8 +79,15 @@ bwd_preprocess_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ d
 constexpr int kKvBK = 128;  // keys per workgroup (32 per wave)
 constexpr int kKvBQ = 64;   // queries per inner step (one SwzTile)
 
+// Columns of dK and dV one workgroup accumulates.  Up to d = 128 all of
+// them; at d = 256 the K^T / V^T fragments of S and dP (128 registers) and
+// dK, dV of all 256 columns (256 accumulators) would not fit one wave's 512
+// registers beside S and dP, so two workgroups share a key block, each
+// accumulating 128 columns; both compute S and dP over the full d.
+constexpr int bwd_out_cols(int d) { return d > 128 ? 128 : d; }
+
 // d <= 64 fits two waves per SIMD (256 registers each, a shorter operand
-// ring below); d = 96 and 128 need one wave's whole register file.
+// ring below); d = 96 and above need one wave's whole register file.
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(kBwdThreads, D <= 64 ? 2 : 1)
 bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
@@ -91,7 +98,9 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   using Tile = SwzTile<tile_width(D), D>;
   static_assert(kKvBQ == Tile::kRows, "query tile is one SwzTile");
   constexpr int KS = D / 16;  // k-steps over d
-  constexpr int DB = D / 32;  // 32-wide d blocks
+  constexpr int DO = bwd_out_cols(D);  // dK / dV columns of this workgroup
+  constexpr int NH = D / DO;           // workgroups per key block
+  constexpr int DB = DO / 32;          // 32-wide blocks of those columns
   constexpr int RB = Tile::kRowBytes;
   // One LDS object per buffer: the compiler then knows that the copies into
   // one buffer cannot alias reads of the other and does not wait for them.
@@ -107,10 +116,13 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int l32 = lane & 31;
   const int half = lane >> 5;
 
-  // workgroup id -> (head, key block); low key blocks meet the most queries
-  // under the causal mask, so they are issued first
-  const int kblk = blockIdx.x / BH;
-  const int bh = blockIdx.x - kblk * BH;
+  // workgroup id -> (head, key block, column half); low key blocks meet the
+  // most queries under the causal mask, so they are issued first
+  const int kblk = blockIdx.x / (BH * NH);
+  const int rem = blockIdx.x - kblk * (BH * NH);
+  const int ohalf = NH > 1 ? rem / BH : 0;
+  const int bh = rem - ohalf * BH;
+  const int c0 = ohalf * DO;  // first dK / dV column of this workgroup
   const int64_t qhead = (int64_t)bh * Nq * D;
   const int64_t khead = (int64_t)bh * Nk * D;
   const __bf16* qh = q + qhead;
@@ -169,8 +181,10 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   using Buf1 = std::integral_constant<int, 1>;
 
   const int rd_base = Tile::row_read_base(l32, half);
-  const int tr_lo = Tile::tr_read_base(lane, false);
-  const int tr_hi = Tile::tr_read_base(lane, true);
+  // transpose reads of this workgroup's columns: block b of them is global
+  // block b + ohalf * DB, i.e. chunk offset 64 (b ^ ohalf DB) (no carries)
+  const int tr_lo = Tile::tr_read_base(lane, false) ^ (64 * DB * ohalf);
+  const int tr_hi = Tile::tr_read_base(lane, true) ^ (64 * DB * ohalf);
 
   f32x16 dk_acc[DB], dv_acc[DB];
 #pragma unroll
@@ -370,7 +384,7 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     for (int i = 0; i < 16; ++i) {
       const int kk = key_w0 + (i >> 2) * 8 + half * 4 + (i & 3);
       if (kk < Nk) {
-        const int64_t at = khead + (int64_t)kk * D + b * 32 + l32;
+        const int64_t at = khead + (int64_t)kk * D + c0 + b * 32 + l32;
         dk[at] = (__bf16)(dk_acc[b][i] * scale);
         dv[at] = (__bf16)dv_acc[b][i];
       }
@@ -382,7 +396,7 @@ constexpr int kDqBQ = 128;  // queries per workgroup (32 per wave)
 constexpr int kDqBK = 64;   // keys per K/V tile (one SwzTile)
 
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(kBwdThreads, 2)
+__global__ void __launch_bounds__(kBwdThreads, D > 128 ? 1 : 2)
 bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
               const __bf16* __restrict__ v, const __bf16* __restrict__ dout,
               const float* __restrict__ lse, const float* __restrict__ delta,
@@ -645,7 +659,7 @@ hipError_t launch_phase(const BwdArgs& a, int phase) {
     hipLaunchKernelGGL(bwd_preprocess_kernel<D>, dim3((unsigned)((rows + 31) / 32)), dim3(256),
                        0, s, (const __bf16*)a.o, (const __bf16*)a.dout, a.delta, rows);
   } else if (phase == 1) {
-    const int nkb = (a.Nk + kKvBK - 1) / kKvBK;
+    const int nkb = (a.Nk + kKvBK - 1) / kKvBK * (D / bwd_out_cols(D));
     auto kern = a.causal ? bwd_dkdv_kernel<D, true> : bwd_dkdv_kernel<D, false>;
     hipLaunchKernelGGL(kern, dim3((unsigned)(BH * nkb)), dim3(kBwdThreads), 0, s,
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
@@ -653,11 +667,17 @@ hipError_t launch_phase(const BwdArgs& a, int phase) {
                        a.Nq, a.Nk, off, a.scale, a.scale * kLog2e);
   } else {
     const int nqt = (a.Nq + kDqBQ - 1) / kDqBQ;
-    auto kern = a.causal ? bwd_dq_kernel<D, true> : bwd_dq_kernel<D, false>;
+    // d = 256 without the mask runs the masked kernel with every key visible
+    // (off = Nk): its unmasked instantiation spills registers there
+    const int dq_off = a.causal ? off : a.Nk;
+    auto kern = bwd_dq_kernel<D, true>;
+    if constexpr (D <= 128) {
+      if (!a.causal) kern = bwd_dq_kernel<D, false>;
+    }
     hipLaunchKernelGGL(kern, dim3((unsigned)(BH * nqt)), dim3(kBwdThreads), 0, s,
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
-                       (const __bf16*)a.dout, a.lse, a.delta, (__bf16*)a.dq, BH, a.Nq, a.Nk, off,
-                       nqt, a.scale, a.scale * kLog2e);
+                       (const __bf16*)a.dout, a.lse, a.delta, (__bf16*)a.dq, BH, a.Nq, a.Nk,
+                       dq_off, nqt, a.scale, a.scale * kLog2e);
   }
   return hipGetLastError();
 }
@@ -670,6 +690,7 @@ hipError_t launch_bwd_phase(const BwdArgs& a, int phase) {
     case 64: return launch_phase<64>(a, phase);
     case 96: return launch_phase<96>(a, phase);
     case 128: return launch_phase<128>(a, phase);
+    case 256: return launch_phase<256>(a, phase);
     default: return hipErrorInvalidValue;
   }
 }

@@ -8,12 +8,11 @@
 
 namespace attn {
 
-// Head dimensions the forward kernels are built for (bf16 and fp32 forward,
-// key/value-cache forward), and those the backward is built for.
+// Head dimensions the kernels are built for (every forward and the backward).
 constexpr bool head_dim_supported(int d) {
   return d == 32 || d == 64 || d == 96 || d == 128 || d == 256;
 }
-constexpr bool bwd_head_dim_supported(int d) { return head_dim_supported(d) && d <= 128; }
+constexpr bool bwd_head_dim_supported(int d) { return head_dim_supported(d); }
 
 struct FwdArgs {
   const void* q;
