@@ -237,8 +237,34 @@ def make_mx_inputs(B: int, H: int, N: int, d: int, seed: int = 0, scale_lo: int 
     return q8, qs.to(torch.uint8), k8, ks.to(torch.uint8), v.to(torch.bfloat16)
 
 
+def make_fp8_v(B: int, H: int, N: int, d: int, seed: int = 0, scale_lo: int = 125,
+               scale_hi: int = 129, pad_code: int = 0, pad_scale: int = 127):
+    """CPU tensors for V in the layout of the FP8 forward: vt8 uint8 E4M3
+    codes of V^T [B, H, d, ldv] (ldv = 64 ceil(N / 64); float32 N(0, 1) draws
+    of V [B, H, N, d] cast with torch's float8_e4m3fn conversion, then
+    transposed) and their E8M0 scale codes vt_scale uint8 [B, H, d, ldv / 32]
+    drawn uniformly from [scale_lo, scale_hi], one per 32 keys.  Keys N ..
+    ldv - 1 hold pad_code and blocks wholly past N pad_scale (the kernel must
+    ignore both; tests pass NaN codes 0x7F / 0xFF there).  Draw order: V
+    values, then the scale codes."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    ldv = (N + 63) // 64 * 64
+    v = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
+    sc = torch.randint(scale_lo, scale_hi + 1, (B, H, d, ldv // 32), generator=g,
+                       dtype=torch.int32).to(torch.uint8)
+    vt8 = torch.full((B, H, d, ldv), pad_code, dtype=torch.uint8)
+    vt8[..., :N] = v.to(torch.float8_e4m3fn).view(torch.uint8).transpose(2, 3)
+    first_pad_block = (N + 31) // 32
+    sc[..., first_pad_block:] = pad_scale
+    return vt8.contiguous(), sc.contiguous()
+
+
 # The headline shape with Q and K in MXFP8 (seed 12).
 MX_WORKLOADS = {
     "b4_h16_n4096_d128_causal_mxfp8": Workload("b4_h16_n4096_d128_causal_mxfp8", 4, 16, 4096, 128,
                                                torch.bfloat16, True, 12),
+    # the same with V (and P) in FP8 too (attn_fwd_fp8); V drawn with seed 13
+    "b4_h16_n4096_d128_causal_fp8": Workload("b4_h16_n4096_d128_causal_fp8", 4, 16, 4096, 128,
+                                             torch.bfloat16, True, 12),
 }

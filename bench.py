@@ -565,23 +565,31 @@ def bench_softmax(args, w):
 
 
 def bench_mx(args, w):
-    """One step = attn_fwd_mx (Q, K in MXFP8, V bf16) over the whole workload."""
+    """One step = attn_fwd_mx (Q, K in MXFP8, V bf16) over the whole workload,
+    or, for the *_fp8 workload, attn_fwd_fp8 (Q, K, V in MXFP8, P in E4M3)."""
     import torch
 
     import tiled_online_softmax_attn_amd as T
-    from attn_inputs import make_mx_inputs
+    from attn_inputs import make_fp8_v, make_mx_inputs
 
     T.lib()
+    fp8v = w.name.endswith("_fp8")
     dev = torch.device("cuda:0")
     eprint(f"[bench] generating inputs for {w.name}")
     q8, qs, k8, ks, v = make_mx_inputs(w.B, w.H, w.N, w.d, w.seed)
     q8d, qsd, k8d, ksd, vd = (t.to(dev) for t in (q8, qs, k8, ks, v))
+    if fp8v:
+        vt8, vts = make_fp8_v(w.B, w.H, w.N, w.d, w.seed + 1)
+        vt8d, vtsd = vt8.to(dev), vts.to(dev)
     o = torch.empty_like(vd)
     lse = torch.empty((w.B, w.H, w.N), device=dev, dtype=torch.float32)
     stream = torch.cuda.current_stream()
 
     def step():
-        T.attn_fwd_mx(q8d, qsd, k8d, ksd, vd, o, lse, w.causal, w.scale, stream)
+        if fp8v:
+            T.attn_fwd_fp8(q8d, qsd, k8d, ksd, vt8d, vtsd, o, lse, w.causal, w.scale, stream)
+        else:
+            T.attn_fwd_mx(q8d, qsd, k8d, ksd, vd, o, lse, w.causal, w.scale, stream)
 
     eprint(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -601,13 +609,19 @@ def bench_mx(args, w):
     flops = w.fwd_flops()
     value = flops * args.steps / wall / 1e12
     achieved = flops / (call_ms * 1e-3) / 1e12
-    # half the FLOPs (S = Q K^T) on the FP8 matrix rate, half (P V) on bf16
-    peak = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
-    roofline = {"kernel": "fwd_mx", "bound": "mfma", "achieved": round(achieved, 1),
-                "peak": round(peak, 1), "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": None, "peak_note": "S on FP8 MFMA (5.0 PFLOP/s), P V on bf16 "
-                                              "(2.5 PFLOP/s), half the FLOPs each",
-                "avg_launch_us": round(call_ms * 1e3, 2)}
+    if fp8v:
+        # both products on the FP8 matrix rate
+        peak = PEAK_FP8_TFLOPS
+        note = "S and P V on FP8 MFMA (5.0 PFLOP/s)"
+    else:
+        # half the FLOPs (S = Q K^T) on the FP8 matrix rate, half (P V) on bf16
+        peak = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
+        note = "S on FP8 MFMA (5.0 PFLOP/s), P V on bf16 (2.5 PFLOP/s), half the FLOPs each"
+    roofline = {"kernel": "fwd_fp8" if fp8v else "fwd_mx", "bound": "mfma",
+                "achieved": round(achieved, 1), "peak": round(peak, 1), "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None, "peak_note": note,
+                "avg_launch_us": round(call_ms * 1e3, 2),
+                "vs_bf16_peak": round(achieved / PEAK_BF16_TFLOPS, 4)}
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -618,7 +632,11 @@ def bench_mx(args, w):
             for h in range(w.H):
                 qh = oracle.mx_decode(q8[b, h], qs[b, h], lib=lib)
                 kh = oracle.mx_decode(k8[b, h], ks[b, h], lib=lib)
-                oracle.attn_fwd(qh, kh, v[b, h].double().numpy(), w.causal,
+                if fp8v:
+                    vh = oracle.mx_decode(vt8[b, h], vts[b, h], lib=lib)[:, :w.N].T.copy()
+                else:
+                    vh = v[b, h].double().numpy()
+                oracle.attn_fwd(qh, kh, vh, w.causal,
                                 float(np.float32(w.scale)), lib=lib)
                 heads += 1
                 if time.perf_counter() - t0c >= args.cpu_baseline_seconds:
@@ -632,12 +650,14 @@ def bench_mx(args, w):
                "sample": f"{heads} of {w.B * w.H} heads of {w.name} (decode + fp64 forward "
                          f"per head), {el:.1f} s"}
     out = {
-        "metric": f"fused attention fwd TFLOP/s, Q and K in MXFP8, {w.name}",
+        "metric": (f"fused attention fwd TFLOP/s, Q, K and V in MXFP8, P in E4M3, {w.name}"
+                   if fp8v else f"fused attention fwd TFLOP/s, Q and K in MXFP8, {w.name}"),
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8-e4m3 (Q, K; E8M0 block scales) / bf16 (V, P, O)",
-        "data": "synthetic (seeded N(0,1) cast to E4M3, random E8M0 scales 2^-2..2^2; V bf16)",
+        "dtype": ("fp8-e4m3 (Q, K, V, P; E8M0 block scales) / bf16 (O)" if fp8v
+                  else "fp8-e4m3 (Q, K; E8M0 block scales) / bf16 (V, P, O)"),
+        "data": ("synthetic (seeded N(0,1) cast to E4M3, random E8M0 scales 2^-2..2^2; V^T " + ("E4M3 with scales per 32 keys)" if fp8v else "bf16 V)")),
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "step": "attn_fwd_mx"},
         "roofline": roofline, "cpu_baseline": cpu,

@@ -214,6 +214,28 @@ int attn_fwd_mx(const void* q8, const void* q_scale, const void* k8, const void*
                 const void* v, void* o, float* lse, int B, int H, int N, int d, int causal,
                 float scale, void* stream);
 
+/* FP8 attention forward: Q, K and V all in MXFP8 (CS336 L5 notes section
+ * 6.2: E4M3 values plus one E8M0 scale per 32 elements), S = Q K^T and
+ * P V both on the gfx950 scaled FP8 matrix instruction.  Q and K as in
+ * attn_fwd_mx (blocks along d, the contraction of S).  P V contracts over
+ * the keys, and block scales do not survive a transpose (same section), so V
+ * comes transposed and quantised along the keys:
+ *   vt8      : [B][H][d][ldv] E4M3 codes of V^T, ldv = 64 * ceil(N / 64);
+ *              row c holds V[0..N-1][c]; codes at keys N..ldv-1 are ignored
+ *              (any value, NaN codes included).  16-byte aligned.
+ *   vt_scale : [B][H][d][ldv / 32] E8M0 codes, one per 32 keys of a row:
+ *              V[j][c] = e4m3(vt8[b,h,c,j]) * 2^(vt_scale[b,h,c,j/32] - 127);
+ *              scales of blocks wholly past N are ignored.  2-byte aligned.
+ * P = 2^(s - m) with m the running reference maximum is rounded to E4M3
+ * (round to nearest even; P <= 2^8, so its block scale is 2^0) for P V; the
+ * row sum and lse use P before rounding.  Per element that adds at most
+ * 2^-4 P + 2^-10 (relative to the row's largest P) times |V| to O before
+ * normalisation.  o: bf16 [B][H][N][d]; lse: fp32 [B][H][N].  d: 64 or 128;
+ * N <= 2^26.  Other arguments and errors as attn_fwd_mx. */
+int attn_fwd_fp8(const void* q8, const void* q_scale, const void* k8, const void* k_scale,
+                 const void* vt8, const void* vt_scale, void* o, float* lse, int B, int H, int N,
+                 int d, int causal, float scale, void* stream);
+
 /* Row-wise softmax of an M x N row-major matrix x (PDC notes Lecture 5,
  * section 5.20, fused softmax; CS149 L9 notes section 8):
  *   y_ij = e^{x_ij - max_j x_ij} / sum_j e^{x_ij - max_j x_ij}.
@@ -233,7 +255,7 @@ const char* attn_status_str(int status);
 /* Library ABI version; bumped when an entry point is added or a signature
  * changes (2: attn_fwd_kv and attn_fwd_kv_workspace_bytes; 3: attn_softmax_rows,
  * and head dimensions 32, 96 and 256; 4: attn_fwd_mx; 5: attn_bwd_noalloc; 6: attn_bwd_kv and
- * attn_bwd_kv_workspace_bytes). */
+ * attn_bwd_kv_workspace_bytes; 7: attn_fwd_fp8). */
 int attn_abi_version(void);
 
 #ifdef __cplusplus

@@ -90,7 +90,7 @@ def _declare(lib):
                                          ctypes.c_double, _DP, _DP, _DP]
     lib.oracle_attn_fwd_rows.restype = ctypes.c_int
     lib.oracle_attn_fwd_rows.argtypes = [_DP, _DP, _DP, i64, i64, ctypes.c_int,
-                                         ctypes.c_double, _I64P, i64, _DP, _DP]
+                                         ctypes.c_double, _I64P, i64, _DP, _DP, _DP]
     lib.oracle_attn_fwd_rect.restype = ctypes.c_int
     lib.oracle_attn_fwd_rect.argtypes = [_DP, _DP, _DP, i64, i64, i64, ctypes.c_int,
                                          ctypes.c_double, _DP, _DP]
@@ -177,19 +177,21 @@ def attn_fwd(q, k, v, causal: bool, scale: float, return_p: bool = False, lib=No
     return o, lse
 
 
-def attn_fwd_rows(q, k, v, causal: bool, scale: float, rows, lib=None):
-    """O rows and lse entries of ONE head ([N, d] inputs) for query ``rows``."""
+def attn_fwd_rows(q, k, v, causal: bool, scale: float, rows, return_p: bool = False, lib=None):
+    """O rows and lse entries of ONE head ([N, d] inputs) for query ``rows``
+    (and those rows of P, [len(rows), N], with ``return_p``)."""
     lib = lib or load()
     q, k, v = _f64(q), _f64(k), _f64(v)
     N, d = q.shape
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1))
     o = np.empty((rows.size, d), dtype=np.float64)
     lse = np.empty(rows.size, dtype=np.float64)
+    p = np.empty((rows.size, N), dtype=np.float64) if return_p else None
     rc = lib.oracle_attn_fwd_rows(_ptr(q), _ptr(k), _ptr(v), N, d, int(bool(causal)),
                                   float(scale), rows.ctypes.data_as(_I64P), rows.size,
-                                  _ptr(o), _ptr(lse))
+                                  _ptr(o), _ptr(lse), _ptr(p) if return_p else ctypes.cast(None, _DP))
     _check(rc, "attn_fwd_rows")
-    return o, lse
+    return (o, lse, p) if return_p else (o, lse)
 
 
 def attn_fwd_rect(q, k, v, causal: bool, scale: float, lib=None):

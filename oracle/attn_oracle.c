@@ -142,11 +142,12 @@ int oracle_attn_fwd_head(const double* q, const double* k, const double* v,
 
 /* Forward for selected query rows of one head: the same definition, one row
  * at a time (S row, softmax, P row times V).  rows: nrows query indices in
- * [0, N); o_rows: [nrows][d]; lse_rows: [nrows]. */
+ * [0, N); o_rows: [nrows][d]; lse_rows: [nrows]; p_rows, when not NULL,
+ * [nrows][N] receives each row of P. */
 int oracle_attn_fwd_rows(const double* q, const double* k, const double* v,
                          int64_t N, int64_t d, int causal, double scale,
                          const int64_t* rows, int64_t nrows, double* o_rows,
-                         double* lse_rows) {
+                         double* lse_rows, double* p_rows) {
   if (!q || !k || !v || !rows || !o_rows || !lse_rows) return -1;
   if (N < 1 || d < 1 || nrows < 0) return -2;
   for (int64_t r = 0; r < nrows; ++r)
@@ -167,6 +168,7 @@ int oracle_attn_fwd_rows(const double* q, const double* k, const double* v,
         score_row(q, k, N, d, causal, scale, i, s);
         oracle_softmax_row(s, N, p, &m, &l);
         lse_rows[r] = m + log(l);
+        if (p_rows) memcpy(p_rows + r * N, p, sizeof(double) * (size_t)N);
         double* orow = o_rows + r * d;
         for (int64_t c = 0; c < d; ++c) orow[c] = 0.0;
         for (int64_t j = 0; j < N; ++j) {

@@ -302,6 +302,9 @@ def pin_rows_entry(lib):
         orow, lrow = oracle.attn_fwd_rows(q, k, v, causal, 0.35, rows, lib=lib)
         _assert_close(orow, o[rows], 0, 0, "rows O")
         _assert_close(lrow, lse[rows], 0, 0, "rows lse")
+        _, _, p = oracle.attn_fwd(q, k, v, causal, 0.35, return_p=True, lib=lib)
+        _, _, prow = oracle.attn_fwd_rows(q, k, v, causal, 0.35, rows, return_p=True, lib=lib)
+        _assert_close(prow, p[rows], 0, 0, "rows P")
 
 
 # ---------------------------------------------------------------- backward pins

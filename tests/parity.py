@@ -137,7 +137,7 @@ def describe(err: dict) -> str:
     return f"max_abs={err['max_abs']:.3e} max_rel={err['max_rel']:.3e}"
 
 
-__all__ = ["compare", "bwd_rounding_bound", "gpu_forward", "gpu_backward", "sample_rows", "oracle_full_fwd",
+__all__ = ["compare", "bwd_rounding_bound", "fp8_pv_bound", "gpu_forward_fp8", "decode_fp8_v", "gpu_forward", "gpu_backward", "sample_rows", "oracle_full_fwd",
            "oracle_rows_fwd", "to_np", "f32_scale", "log", "describe", "math"]
 
 
@@ -188,3 +188,41 @@ def gpu_forward_mx(q8, qs, k8, ks, v, causal, scale):
     T.attn_fwd_mx(q8d, qsd, k8d, ksd, vd, o, lse, causal, scale)
     torch.cuda.synchronize()
     return o.cpu(), lse.cpu()
+
+
+def gpu_forward_fp8(q8, qs, k8, ks, vt8, vts, causal, scale):
+    """FP8 inputs (CPU tensors; V transposed, attn_fwd_fp8's layout); runs
+    attn_fwd_fp8 into NaN-poisoned outputs; returns CPU (o, lse)."""
+    dev = torch.device("cuda:0")
+    ts = [t.to(dev) for t in (q8, qs, k8, ks, vt8, vts)]
+    B, H, N, d = q8.shape
+    o = torch.full((B, H, N, d), float("nan"), device=dev, dtype=torch.bfloat16)
+    lse = torch.full((B, H, N), float("nan"), device=dev, dtype=torch.float32)
+    T.attn_fwd_fp8(*ts, o, lse, causal, scale)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def decode_fp8_v(vt8, vts, N):
+    """V [..., N, d] (float64) of attn_fwd_fp8's V^T codes [..., d, ldv] and
+    scales [..., d, ldv / 32], decoded by the oracle (keys past N dropped)."""
+    vt = oracle.mx_decode(vt8, vts)
+    return np.ascontiguousarray(np.swapaxes(vt[..., :N], -1, -2))
+
+
+E4M3_U = 2.0 ** -4      # relative rounding error of a normal E4M3 value (3 mantissa bits)
+E4M3_SUB = 2.0 ** -10   # absolute rounding error below the normal range (half of 2^-9)
+
+
+def fp8_pv_bound(p: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """Elementwise bound on what rounding P to E4M3 adds to O = P V, for one
+    head: p [rows, N] the oracle's probabilities, v [N, d].
+
+    The kernel rounds P_hat = 2^(s - m_ref) to nearest even, with m_ref a
+    running reference within 8 (log2) of the row maximum, so P_hat <= 2^8
+    and the row's largest P_hat is >= 1.  A code's error is at most
+    2^-4 P_hat (normal) or 2^-10 (subnormal, or flushed to 0).  Divided by
+    the row sum l_hat = P_hat_max / p_max >= 1 / p_max:
+        |dO_ic| <= sum_j max(2^-4 p_ij, 2^-10 p_i,max) |V_jc|."""
+    pmax = p.max(axis=1, keepdims=True)
+    return np.maximum(E4M3_U * p, E4M3_SUB * pmax) @ np.abs(v)

@@ -57,6 +57,7 @@ def test_header_declares_expected_entry_points():
                                            "attn_bwd_workspace_bytes", "attn_fwd_kv",
                                            "attn_fwd_kv_workspace_bytes", "attn_bwd_kv",
                                            "attn_bwd_kv_workspace_bytes", "attn_softmax_rows", "attn_fwd_mx",
+                                           "attn_fwd_fp8",
                                            "attn_status_str", "attn_abi_version"])
 
 
@@ -70,7 +71,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = _lib()
-    assert lib.attn_abi_version() == 6
+    assert lib.attn_abi_version() == 7
     for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, 12345]:
         s = lib.attn_status_str(code)
         assert isinstance(s, bytes) and len(s) > 0
@@ -289,3 +290,24 @@ def test_binding_refuses_host_tensors():
         T.attn_fwd(q, q.clone(), q.clone(), torch.empty_like(q), lse, True, 0.125)
     with pytest.raises(ValueError):
         T.attn_softmax_rows(q, torch.empty_like(q))
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(q8=0), -1), (dict(vt8=0), -1), (dict(vt_scale=0), -1), (dict(N=0), -2),
+    (dict(N=(1 << 26) + 1), -2), (dict(d=96), -4), (dict(d=256), -4),
+    (dict(vt8=FAKE + 8), -5), (dict(vt_scale=FAKE + 1), -5), (dict(q_scale=FAKE + 2), -5),
+    (dict(lse=FAKE + 2), -5),
+    (dict(scale=float("nan")), -6), (dict(scale=0.0), -6), (dict(scale=-0.5), -6),
+    # a 2-byte aligned V^T scale pointer and a 4-byte aligned lse pass the
+    # alignment checks; the (later) scale check stops the call
+    (dict(vt_scale=FAKE + 2, lse=FAKE + 4, scale=0.0), -6),
+])
+def test_fwd_fp8_validation(args, code):
+    lib = _lib()
+    a = dict(q8=FAKE, q_scale=FAKE, k8=FAKE, k_scale=FAKE, vt8=FAKE, vt_scale=FAKE, o=FAKE,
+             lse=FAKE, B=1, H=1, N=16, d=128, causal=1, scale=0.1)
+    a.update(args)
+    rc = lib.attn_fwd_fp8(*(a[n] or None for n in ("q8", "q_scale", "k8", "k_scale", "vt8",
+                                                     "vt_scale", "o", "lse")),
+                          a["B"], a["H"], a["N"], a["d"], a["causal"], a["scale"], None)
+    assert rc == code

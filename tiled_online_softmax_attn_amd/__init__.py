@@ -29,7 +29,7 @@ STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR
           -7: "ATTN_ERR_WORKSPACE", -8: "ATTN_ERR_HIP", -9: "ATTN_ERR_SCRATCH"}
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_noalloc", "attn_bwd_phase", "attn_bwd_workspace_bytes",
            "attn_fwd_kv", "attn_fwd_kv_workspace_bytes", "attn_bwd_kv", "attn_bwd_kv_workspace_bytes",
-           "attn_softmax_rows", "attn_fwd_mx",
+           "attn_softmax_rows", "attn_fwd_mx", "attn_fwd_fp8",
            "attn_status_str", "attn_abi_version")
 
 
@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd_kv_workspace_bytes.argtypes = [i, i, i, i, i, i]
         L.attn_fwd_mx.restype = i
         L.attn_fwd_mx.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+        L.attn_fwd_fp8.restype = i
+        L.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
         L.attn_softmax_rows.restype = i
         L.attn_softmax_rows.argtypes = [vp, vp, ctypes.c_longlong, i, i, vp]
         L.attn_status_str.restype = ctypes.c_char_p
@@ -305,6 +307,38 @@ def attn_fwd_mx(q8, q_scale, k8, k_scale, v, o, lse, causal: bool, scale: float,
                            _stream_handle(stream))
     if rc != 0:
         raise AttnError(rc, "attn_fwd_mx")
+
+
+def fp8_v_row_length(N: int) -> int:
+    """Row length (ldv) of the V^T codes attn_fwd_fp8 takes: 64 ceil(N / 64)."""
+    return (int(N) + 63) // 64 * 64
+
+
+def attn_fwd_fp8(q8, q_scale, k8, k_scale, vt8, vt_scale, o, lse, causal: bool, scale: float,
+                 stream=None) -> None:
+    """Enqueue the FP8 forward: q8, k8 E4M3 codes [B, H, N, d] with E8M0
+    scales q_scale, k_scale [B, H, N, d / 32] (as attn_fwd_mx); vt8 the E4M3
+    codes of V^T [B, H, d, ldv] (ldv = fp8_v_row_length(N)) with E8M0 scales
+    vt_scale [B, H, d, ldv / 32] along the keys; o bf16 [B, H, N, d], lse fp32
+    [B, H, N]."""
+    _check_contig(q8, q_scale, k8, k_scale, vt8, vt_scale, o, lse)
+    B, H, N, d = _shape(q8)
+    ldv = fp8_v_row_length(N)
+    codes = (torch.uint8, torch.float8_e4m3fn)
+    dev = q8.device
+    _check("attn_fwd_fp8 q8", q8, (B, H, N, d), codes, dev)
+    _check("attn_fwd_fp8 k8", k8, (B, H, N, d), codes, dev)
+    _check("attn_fwd_fp8 q_scale", q_scale, (B, H, N, d // 32), (torch.uint8,), dev)
+    _check("attn_fwd_fp8 k_scale", k_scale, (B, H, N, d // 32), (torch.uint8,), dev)
+    _check("attn_fwd_fp8 vt8", vt8, (B, H, d, ldv), codes, dev)
+    _check("attn_fwd_fp8 vt_scale", vt_scale, (B, H, d, ldv // 32), (torch.uint8,), dev)
+    _check("attn_fwd_fp8 o", o, (B, H, N, d), (torch.bfloat16,), dev)
+    _check("attn_fwd_fp8 lse", lse, (B, H, N), (torch.float32,), dev)
+    rc = lib().attn_fwd_fp8(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(vt8),
+                            _ptr(vt_scale), _ptr(o), _ptr(lse), B, H, N, d, int(bool(causal)),
+                            float(scale), _stream_handle(stream))
+    if rc != 0:
+        raise AttnError(rc, "attn_fwd_fp8")
 
 
 def attn_softmax_rows(x, y, stream=None) -> None:

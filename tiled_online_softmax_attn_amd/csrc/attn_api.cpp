@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 6;
+constexpr int kAbiVersion = 7;
 
 // Device scratch of attn_bwd_noalloc: the D vector (one fp32 per query row)
 // that attn_bwd keeps in the caller's workspace.  16 MiB per GPU, so
@@ -268,7 +268,31 @@ int attn_fwd_mx(const void* q8, const void* q_scale, const void* k8, const void*
   if ((reinterpret_cast<uintptr_t>(q_scale) & salign) || (reinterpret_cast<uintptr_t>(k_scale) & salign))
     return ATTN_ERR_ALIGN;
   if (!scale_ok(scale)) return ATTN_ERR_SCALE;
-  attn::FwdMxArgs a{q8, q_scale, k8, k_scale, v, o, lse, B, H, N, d, causal != 0, scale, stream};
+  attn::FwdMxArgs a{q8, q_scale, k8, k_scale, v, nullptr, nullptr, o, lse, B, H, N, d,
+                    causal != 0, scale, stream};
+  return attn::launch_fwd_mx(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_fwd_fp8(const void* q8, const void* q_scale, const void* k8, const void* k_scale,
+                 const void* vt8, const void* vt_scale, void* o, float* lse, int B, int H, int N,
+                 int d, int causal, float scale, void* stream) {
+  if (!q8 || !q_scale || !k8 || !k_scale || !vt8 || !vt_scale || !o || !lse) return ATTN_ERR_NULL;
+  int rc = check_shape(B, H, N, d);
+  if (rc != ATTN_OK) return rc;
+  // V^T rows of 64 ceil(N / 64) bytes: 16 rows of them must stay within the
+  // 32-bit offsets of one copy instruction
+  if (N > (1 << 26)) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(vt8) || !aligned16(o) || !aligned4(lse))
+    return ATTN_ERR_ALIGN;
+  const uintptr_t salign = d == 128 ? 3u : 1u;
+  if ((reinterpret_cast<uintptr_t>(q_scale) & salign) ||
+      (reinterpret_cast<uintptr_t>(k_scale) & salign) ||
+      (reinterpret_cast<uintptr_t>(vt_scale) & 1u))
+    return ATTN_ERR_ALIGN;
+  if (!scale_ok(scale)) return ATTN_ERR_SCALE;
+  attn::FwdMxArgs a{q8, q_scale, k8, k_scale, nullptr, vt8, vt_scale, o, lse, B, H, N, d,
+                    causal != 0, scale, stream};
   return attn::launch_fwd_mx(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

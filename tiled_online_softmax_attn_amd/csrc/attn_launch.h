@@ -77,12 +77,17 @@ KvSplit kv_split_plan(int B, int H, int Nq, int Nk, int d, int num_splits);
 
 // Forward with Q and K in MXFP8 (E4M3 codes, one E8M0 scale per 32 elements
 // along d) and V in bf16 (attn_fwd_mx).
+// With vt8 set (attn_fwd_fp8), V arrives transposed in MXFP8 instead: V^T
+// E4M3 codes [B][H][d][ldv] with one E8M0 scale per 32 keys [B][H][d][ldv /
+// 32], ldv = 64 ceil(N / 64); P is rounded to E4M3 for P V.
 struct FwdMxArgs {
   const void* q8;       // [B][H][N][d] E4M3
   const void* q_scale;  // [B][H][N][d / 32] E8M0
   const void* k8;
   const void* k_scale;
-  const void* v;        // [B][H][N][d] bf16
+  const void* v;        // [B][H][N][d] bf16 (attn_fwd_mx)
+  const void* vt8;      // [B][H][d][ldv] E4M3 (attn_fwd_fp8), else null
+  const void* vt_scale; // [B][H][d][ldv / 32] E8M0
   void* o;              // [B][H][N][d] bf16
   float* lse;           // [B][H][N]
   int B, H, N, d;
