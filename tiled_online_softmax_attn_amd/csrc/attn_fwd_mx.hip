@@ -233,15 +233,14 @@ attn_fwd_mx_kernel(const unsigned char* __restrict__ q8, const unsigned char* __
       VTile::template load<kMxThreads / 64>(vh, j * kMxBK, N, dst, wave, lane);
     }
   };
-  // FP8V: the V^T scales of tile j for the lane's rows 32 b + l32 (one
-  // 16-bit word per row: blocks 2 j and 2 j + 1), as loaded; tiles past the
+  // FP8V: the V^T scale the lane supplies for tile j and each of its rows
+  // 32 b + l32: block 2 j + half (keys 64 j + 32 half ..); tiles past the
   // end re-read the last tile's (never used)
   auto load_vsc = [&](int j, int (&dst)[D / 32]) {
     const int jj = min(j, ldv / kMxBK - 1);
 #pragma unroll
     for (int b = 0; b < D / 32; ++b)
-      dst[b] = (int)*reinterpret_cast<const unsigned short*>(
-          vtsh + (int64_t)(32 * b + l32) * (ldv / 32) + 2 * jj);
+      dst[b] = (int)vtsh[(int64_t)(32 * b + l32) * (ldv / 32) + 2 * jj + half];
   };
   // scale words of the lane's two keys of tile j (rows past the end re-read
   // the last row; the mask gives those keys weight 0), as loaded: the shift
@@ -296,6 +295,7 @@ attn_fwd_mx_kernel(const unsigned char* __restrict__ q8, const unsigned char* __
   // 32-row d block.
   const int vt_lo = VtTile<D>::read_lo(l32, half);
   const int vt_hi = VtTile<D>::read_hi(l32, half);
+
   auto step_fp8v = [&](const int j, auto par_tag, f32x16 (&sc)[2], f32x16 (&sn)[2], auto mask_tag,
                        auto next_tag, const float m_off, float& psum) {
     constexpr bool MASK = decltype(mask_tag)::value;
@@ -307,7 +307,7 @@ attn_fwd_mx_kernel(const unsigned char* __restrict__ q8, const unsigned char* __
     // 4 a + 3 of key half kb (a = part % 4, kb = part / 4), the keys 32 kb +
     // 8 a + 4 h + (0..3) of lane (q, h); rounded to E4M3 as one group of four
     // codes right away.
-    int pg[2][4];
+    int pg[2][4];  // E4M3 codes of P^T: [key half][group of four]
     auto exp_part = [&](int part) {
       const int kb = part >> 2, a = part & 3;
       float p[4];
@@ -317,7 +317,10 @@ attn_fwd_mx_kernel(const unsigned char* __restrict__ q8, const unsigned char* __
         __asm__ volatile("" ::"v"(p[c]));  // keep it at this point of the issue order
         psum += p[c];
       }
-      const int r = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+      // the first conversion writes bytes 0-1 and keeps bytes 2-3 of its
+      // input, which the second one overwrites: any input does, so p[0]'s
+      // own register (its last use) is passed rather than a zero to load
+      const int r = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __builtin_bit_cast(int, p[0]), false);
       pg[kb][a] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], r, true);
     };
     // swapping groups 0 <-> 2 and 1 <-> 3 of key half kb across the lane
@@ -337,10 +340,9 @@ attn_fwd_mx_kernel(const unsigned char* __restrict__ q8, const unsigned char* __
       const i32x4 hi = *reinterpret_cast<const ATTN_LDS i32x4*>(vbuf + vt_hi + b * 2048);
       return concat8(lo, hi);
     };
-    // V^T fragments: blocks 0 and 1 read in the last two slots, each later
-    // block while the MFMA of the block before it runs
-    i32x8 vf[2];
-    constexpr int kVtSlot0 = kSlots - 2;
+    // V^T fragments of the DB blocks, read in the last DB slots
+    i32x8 vf[DB];
+    constexpr int kVtSlot0 = kSlots - DB;
     if constexpr (NEXT) {
       using Next = std::integral_constant<int, (T + 1) % 3>;
       const ATTN_LDS unsigned char* kbuf = k_lds(Next{});
@@ -383,15 +385,13 @@ attn_fwd_mx_kernel(const unsigned char* __restrict__ q8, const unsigned char* __
     }
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
-      i32x8 f = vf[b & 1];
-      if (b + 2 < DB) vf[b & 1] = read_vt(b + 2);
-      int vs = vsc[T][b] >> (8 * half);  // byte 0: block 2 j + half
+      int vs = vsc[T][b];  // block 2 j + half
       if constexpr (MASK) {
 #pragma unroll
-        for (int w = 0; w < 8; ++w) f[w] &= vmask[w];
+        for (int w = 0; w < 8; ++w) vf[b][w] &= vmask[w];
         if (key0 + 32 * half >= N) vs = 127;
       }
-      oacc[b] = mfma_mx<0>(f, pb, oacc[b], vs, kScaleOne4);
+      oacc[b] = mfma_mx<0>(vf[b], pb, oacc[b], vs, kScaleOne4);
     }
   };
 
