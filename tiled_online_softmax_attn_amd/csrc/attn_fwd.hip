@@ -165,6 +165,16 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // arithmetic.
   float m_ref = -INFINITY;
   float l_run = 0.f;  // this lane's share of the running sum (its 32 keys per tile)
+  // d <= 64: the row sum runs on the matrix unit instead of the VALU, which
+  // is the busier of the two there (two to four exponentials per MFMA): an
+  // all-ones A operand against P^T adds sum_k P[q][k] (the bf16 P the
+  // numerator uses) to every row of lacc, four MFMAs per tile in place of 32
+  // adds per lane.
+  constexpr bool kSumOnMfma = (D <= 64);
+  f32x16 lacc = {};
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
 
   // Tile j of the softmax pipeline.  On entry `sc` holds S^T of tile j; the
   // step issues S^T of tile j+1 into `sn` (when NEXT) so that those MFMAs run
@@ -201,7 +211,12 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       const float m_new = fmaxf(m_ref, mx);
       const float alpha = (MASK && m_new == -INFINITY) ? 1.f : fast_exp2(m_ref - m_new);
       m_ref = m_new;
-      l_run *= alpha;
+      if constexpr (kSumOnMfma) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) lacc[i] *= alpha;
+      } else {
+        l_run *= alpha;
+      }
 #pragma unroll
       for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -227,7 +242,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         // keep the exponential at this point of the issue order (it would
         // otherwise sink below the MFMAs it is meant to overlap with)
         __asm__ volatile("" ::"v"(p));
-        psum += p;
+        if constexpr (!kSumOnMfma) psum += p;
         pf[kb][i >> 3][i & 7] = (__bf16)p;
       }
     };
@@ -243,6 +258,9 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     auto pv = [&](int u, const bf16x8& vfrag) {
       const int kt = u / DB, b = u % DB;
       oacc[b] = mfma_32x32x16(vfrag, pf[kt >> 1][kt & 1], oacc[b]);
+      if constexpr (kSumOnMfma) {
+        if (b == DB - 1) lacc = mfma_32x32x16(ones, pf[kt >> 1][kt & 1], lacc);
+      }
     };
     constexpr int US = 4 * DB;
     if constexpr (NEXT) {
@@ -384,7 +402,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   }
 
   // ---- epilogue: O = O / l, lse = ln2 * (m + log2 l)
-  const float l_tot = sum_across_halves(l_run);
+  const float l_tot = kSumOnMfma ? lacc[0] : sum_across_halves(l_run);
   const float m_run = m_ref;
   if (qry < N) {
     const float inv = 1.f / l_tot;
