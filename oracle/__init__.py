@@ -21,6 +21,9 @@ that file's header:
   Exercise 9).
 * ``attn_bwd_rect`` - the same gradient for Nq queries at the end of an
   Nk-key sequence (the backward of ``attn_fwd_rect``).
+* ``attn_bwd_dq_rows`` - dQ for selected query rows only (each row of dQ
+  depends on its own rows of P and dP), for sequences too long for the
+  whole N x N gradient.
 * ``mx_decode``     - values of an MXFP8 tensor (E4M3 codes, one E8M0 scale
   per 32 elements of a row; CS336 L5 notes section 6.2); attention of MXFP8
   inputs is ``attn_fwd`` of the decoded values.
@@ -99,6 +102,9 @@ def _declare(lib):
     lib.oracle_attn_bwd_head.restype = ctypes.c_int
     lib.oracle_attn_bwd_head.argtypes = [_DP, _DP, _DP, _DP, i64, i64, ctypes.c_int,
                                          ctypes.c_double, _DP, _DP, _DP, _DP, _DP, _DP]
+    lib.oracle_attn_bwd_dq_rows.restype = ctypes.c_int
+    lib.oracle_attn_bwd_dq_rows.argtypes = [_DP, _DP, _DP, _DP, i64, i64, ctypes.c_int,
+                                            ctypes.c_double, _I64P, i64, _DP]
     lib.oracle_attn_bwd_rect.restype = ctypes.c_int
     lib.oracle_attn_bwd_rect.argtypes = [_DP, _DP, _DP, _DP, i64, i64, i64, ctypes.c_int,
                                          ctypes.c_double, _DP, _DP, _DP, _DP, _DP, _DP]
@@ -284,3 +290,17 @@ def attn_bwd_rect(q, k, v, dout, causal: bool, scale: float, lib=None):
     return {"dq": dq.reshape(lead + (Nq, d)), "dk": dk.reshape(lead + (Nk, d)),
             "dv": dv.reshape(lead + (Nk, d)), "o": o.reshape(lead + (Nq, d)),
             "lse": lse.reshape(lead + (Nq,)), "D": D.reshape(lead + (Nq,))}
+
+
+def attn_bwd_dq_rows(q, k, v, dout, causal: bool, scale: float, rows, lib=None):
+    """dQ rows of ONE head ([N, d] inputs) for query ``rows``."""
+    lib = lib or load()
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    N, d = q.shape
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1))
+    dq = np.empty((rows.size, d), dtype=np.float64)
+    rc = lib.oracle_attn_bwd_dq_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), N, d,
+                                     int(bool(causal)), float(scale), rows.ctypes.data_as(_I64P),
+                                     rows.size, _ptr(dq))
+    _check(rc, "attn_bwd_dq_rows")
+    return dq

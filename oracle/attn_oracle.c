@@ -183,6 +183,63 @@ int oracle_attn_fwd_rows(const double* q, const double* k, const double* v,
   return failed ? -3 : 0;
 }
 
+/* dQ rows of the backward for selected query rows of one head (CS336 L5
+ * notes section 8.4): row i of dQ depends only on row i of P and dP, so it
+ * is computed alone, in O(N d):
+ *   p = softmax of the (masked) score row, o = p V, D = dO_i . o,
+ *   dp_j = dO_i . v_j, ds_j = p_j (dp_j - D), dQ_i = scale sum_j ds_j k_j.
+ * rows: nrows indices in [0, N); dq_rows: [nrows][d]. */
+int oracle_attn_bwd_dq_rows(const double* q, const double* k, const double* v,
+                            const double* dout, int64_t N, int64_t d, int causal,
+                            double scale, const int64_t* rows, int64_t nrows,
+                            double* dq_rows) {
+  if (!q || !k || !v || !dout || !rows || !dq_rows) return -1;
+  if (N < 1 || d < 1 || nrows < 0) return -2;
+  for (int64_t r = 0; r < nrows; ++r)
+    if (rows[r] < 0 || rows[r] >= N) return -2;
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* sr = (double*)malloc(sizeof(double) * (size_t)N);
+    double* pr = (double*)malloc(sizeof(double) * (size_t)N);
+    double* orow = (double*)malloc(sizeof(double) * (size_t)d);
+    if (!sr || !pr || !orow) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t row_i = rows[r];
+        const double* doi = dout + row_i * d;
+        double mr, lr;
+        score_row(q, k, N, d, causal, scale, row_i, sr);
+        oracle_softmax_row(sr, N, pr, &mr, &lr);
+        for (int64_t c = 0; c < d; ++c) {
+          double acc = 0.0;
+          for (int64_t t = 0; t < N; ++t) acc += pr[t] * v[t * d + c];
+          orow[c] = acc;
+        }
+        double Di = 0.0;
+        for (int64_t c = 0; c < d; ++c) Di += doi[c] * orow[c];
+        double* dqi = dq_rows + r * d;
+        for (int64_t c = 0; c < d; ++c) dqi[c] = 0.0;
+        for (int64_t t = 0; t < N; ++t) {
+          if (pr[t] == 0.0) continue;  /* masked keys (and underflow) add nothing */
+          double dpt = 0.0;
+          for (int64_t c = 0; c < d; ++c) dpt += doi[c] * v[t * d + c];
+          const double dst = pr[t] * (dpt - Di);
+          for (int64_t c = 0; c < d; ++c) dqi[c] += dst * k[t * d + c];
+        }
+        for (int64_t c = 0; c < d; ++c) dqi[c] *= scale;
+      }
+    }
+    free(sr);
+    free(pr);
+    free(orow);
+  }
+  return failed ? -3 : 0;
+}
+
 /* Forward for Nq queries against Nk keys of one head (decode- and
  * prefill-shaped attention over a key/value cache: PDC notes Lecture 4,
  * section 4.9; CS336 L5 notes section 5.3).  The queries are the last Nq

@@ -337,6 +337,18 @@ def pin_bwd_finite_differences(lib):
             _assert_close(g["d" + name], fd, 1e-10, 1e-12, f"finite differences d{name}")
 
 
+def pin_bwd_dq_rows(lib):
+    """The row-wise dQ entry point returns the square backward's dQ rows
+    (that backward is pinned by finite differences above)."""
+    rng = _rng(23)
+    for causal in (False, True):
+        q, k, v, do = rng.normal(size=(4, 41, 7))
+        g = oracle.attn_bwd(q, k, v, do, causal, 0.35, lib=lib)
+        rows = np.array([40, 0, 13, 13, 1, 27])
+        dq = oracle.attn_bwd_dq_rows(q, k, v, do, causal, 0.35, rows, lib=lib)
+        _assert_close(dq, g["dq"][rows], 1e-12, 1e-13, "dq rows")
+
+
 def pin_bwd_D_identity(lib):
     """CS336 L5 notes Exercise 9: sum_j P_ij dP_ij = sum_k dO_ik O_ik."""
     rng = _rng(21)
@@ -514,7 +526,8 @@ def pin_mx_scales(lib):
 FORWARD_PINS = [pin_worked_example, pin_blocked_identity, pin_streaming_and_blocked,
                 pin_rows_sum_to_one, pin_constant_v, pin_q_zero, pin_row0_and_single_key,
                 pin_brute_force, pin_large_logits, pin_rows_entry]
-BACKWARD_PINS = [pin_bwd_finite_differences, pin_bwd_D_identity, pin_bwd_invariants]
+BACKWARD_PINS = [pin_bwd_finite_differences, pin_bwd_D_identity, pin_bwd_invariants,
+                 pin_bwd_dq_rows]
 RECT_PINS = [pin_rect_brute_force, pin_rect_q_zero, pin_rect_merge,
              pin_rect_bwd_finite_differences, pin_rect_bwd_invariants, pin_rect_bwd_square]
 MX_PINS = [pin_mx_e4m3_codes, pin_mx_scales]

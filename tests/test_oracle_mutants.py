@@ -47,6 +47,9 @@ MUTANTS = {
     "rect_bwd_dq_no_scale": ("dq[r * d + c] = scale * acc;", "dq[r * d + c] = acc;"),
     "rect_bwd_D_uses_Q": ("dd += dout[r * d + c] * Or[r * d + c];", "dd += dout[r * d + c] * q[r * d + c];"),
     "rect_bwd_dk_wrong_key": ("ak += dSr[r * Nk + t] * q[r * d + c];", "ak += dSr[r * Nk + (Nk - 1 - t)] * q[r * d + c];"),
+    "dq_rows_D_from_dO": ("Di += doi[c] * orow[c];", "Di += doi[c] * doi[c];"),
+    "dq_rows_no_scale": ("for (int64_t c = 0; c < d; ++c) dqi[c] *= scale;", ""),
+    "dq_rows_uses_v": ("dqi[c] += dst * k[t * d + c];", "dqi[c] += dst * v[t * d + c];"),
     "e4m3_bias": ("ldexp(8.0 + m, e - 10)", "ldexp(8.0 + m, e - 11)"),
     "e4m3_subnormal_as_normal": ("(e == 0) ? ldexp((double)m, -9) :", ""),
     "e4m3_no_sign": ("return sign ? -mag : mag;", "return mag;"),
