@@ -96,7 +96,7 @@ def _declare(lib):
                                          ctypes.c_double, _I64P, i64, _DP, _DP, _DP]
     lib.oracle_attn_fwd_rect.restype = ctypes.c_int
     lib.oracle_attn_fwd_rect.argtypes = [_DP, _DP, _DP, i64, i64, i64, ctypes.c_int,
-                                         ctypes.c_double, _DP, _DP]
+                                         ctypes.c_double, _DP, _DP, _DP]
     lib.oracle_mx_decode.restype = ctypes.c_int
     lib.oracle_mx_decode.argtypes = [ctypes.c_void_p, ctypes.c_void_p, i64, i64, _DP]
     lib.oracle_attn_bwd_head.restype = ctypes.c_int
@@ -200,10 +200,11 @@ def attn_fwd_rows(q, k, v, causal: bool, scale: float, rows, return_p: bool = Fa
     return (o, lse, p) if return_p else (o, lse)
 
 
-def attn_fwd_rect(q, k, v, causal: bool, scale: float, lib=None):
+def attn_fwd_rect(q, k, v, causal: bool, scale: float, return_p: bool = False, lib=None):
     """O and lse of Nq queries ([..., Nq, d]) against Nk keys and values
     ([..., Nk, d]); the queries are the last Nq positions, so under the causal
-    mask query i sees keys 0 .. i + Nk - Nq."""
+    mask query i sees keys 0 .. i + Nk - Nq.  With ``return_p`` also P
+    ([..., Nq, Nk])."""
     lib = lib or load()
     qh, lead = _heads(q)
     kh, _ = _heads(k)
@@ -212,10 +213,14 @@ def attn_fwd_rect(q, k, v, causal: bool, scale: float, lib=None):
     Nk = kh.shape[1]
     o = np.empty_like(qh)
     lse = np.empty((G, Nq), dtype=np.float64)
+    p = np.empty((G, Nq, Nk), dtype=np.float64) if return_p else None
     for g in range(G):
         rc = lib.oracle_attn_fwd_rect(_ptr(qh[g]), _ptr(kh[g]), _ptr(vh[g]), Nq, Nk, d,
-                                      int(bool(causal)), float(scale), _ptr(o[g]), _ptr(lse[g]))
+                                      int(bool(causal)), float(scale), _ptr(o[g]), _ptr(lse[g]),
+                                      _ptr(p[g]) if return_p else ctypes.cast(None, _DP))
         _check(rc, "attn_fwd_rect")
+    if return_p:
+        return o.reshape(lead + (Nq, d)), lse.reshape(lead + (Nq,)), p.reshape(lead + (Nq, Nk))
     return o.reshape(lead + (Nq, d)), lse.reshape(lead + (Nq,))
 
 

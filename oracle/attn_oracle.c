@@ -247,10 +247,11 @@ int oracle_attn_bwd_dq_rows(const double* q, const double* k, const double* v,
  * the causal mask it sees keys 0 .. i + Nk - Nq.  Nq = Nk is the square case
  * of oracle_attn_fwd_head.  q: [Nq][d], k, v: [Nk][d]; o: [Nq][d], lse: [Nq].
  * With causal, Nk >= Nq is required (every query then sees key 0).  Same
- * definition as above: score row, safe softmax, P row times V. */
+ * definition as above: score row, safe softmax, P row times V.  p_out, when
+ * not NULL, [Nq][Nk] receives P. */
 int oracle_attn_fwd_rect(const double* q, const double* k, const double* v,
                          int64_t Nq, int64_t Nk, int64_t d, int causal, double scale,
-                         double* o, double* lse) {
+                         double* o, double* lse, double* p_out) {
   if (!q || !k || !v || !o || !lse) return -1;
   if (Nq < 1 || Nk < 1 || d < 1 || (causal && Nk < Nq)) return -2;
   const int64_t offset = Nk - Nq;
@@ -279,6 +280,7 @@ int oracle_attn_fwd_rect(const double* q, const double* k, const double* v,
         double m, l;
         oracle_softmax_row(s, Nk, p, &m, &l);
         lse[i] = log(l) + m;
+        if (p_out) memcpy(p_out + i * Nk, p, sizeof(double) * (size_t)Nk);
         double* oi = o + i * d;
         for (int64_t c = 0; c < d; ++c) oi[c] = 0.0;
         for (int64_t j = 0; j < Nk; ++j) {

@@ -411,7 +411,9 @@ def pin_rect_merge(lib):
     Nq, Nk, d = 3, 23, 5
     q = rng.normal(size=(Nq, d))
     k, v = rng.normal(size=(2, Nk, d))
-    o, lse = oracle.attn_fwd_rect(q, k, v, False, 0.6, lib=lib)
+    o, lse, p = oracle.attn_fwd_rect(q, k, v, False, 0.6, return_p=True, lib=lib)
+    _assert_close(p @ v, o, 1e-13, 1e-14, "rect O = P V")
+    _assert_close(p.sum(-1), np.ones(Nq), 1e-14, 0, "rect P rows sum to 1")
     edges = [0, 4, 11, 12, 23]
     parts = [oracle.attn_fwd_rect(q, k[a:b], v[a:b], False, 0.6, lib=lib)
              for a, b in zip(edges[:-1], edges[1:])]

@@ -62,7 +62,8 @@ BF16_U = 2.0 ** -8  # unit roundoff of bf16 (8 significant bits, round to neares
 
 def bwd_rounding_bound(q, k, v, dout, causal, scale) -> dict:
     """Elementwise bound on what the bf16 rounding points of the backward add
-    to dQ, dK and dV, from the oracle's fp64 P (one head, [N, d] inputs).
+    to dQ, dK and dV, from the oracle's fp64 P (one head, [N, d] inputs, or
+    q, dout [Nq, d] at the end of k, v [Nk, d]).
 
     The kernels round four quantities to bf16 (u = 2^-8 relative each): O
     in the forward, which also carries the rounding of P before P V, so
@@ -78,7 +79,10 @@ def bwd_rounding_bound(q, k, v, dout, causal, scale) -> dict:
     Q, K, V, dO = (np.asarray(to_np(t) if hasattr(t, "detach") else t, dtype=np.float64)
                    for t in (q, k, v, dout))
     sc = f32_scale(scale)
-    _, _, P = oracle.attn_fwd(Q, K, V, causal, sc, return_p=True)
+    if Q.shape[0] == K.shape[0]:
+        _, _, P = oracle.attn_fwd(Q, K, V, causal, sc, return_p=True)
+    else:  # Nq queries at the end of Nk keys
+        _, _, P = oracle.attn_fwd_rect(Q, K, V, causal, sc, return_p=True)
     O = P @ V
     dS = P * (dO @ V.T - (dO * O).sum(1)[:, None])
     u = BF16_U

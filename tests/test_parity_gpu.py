@@ -14,7 +14,8 @@ Coverage:
 * scales other than 1/sqrt(d) (1.0 and 0.02) on causal and unmasked ragged
   shapes, forward (bf16 and fp32) and backward;
 * determinism of the forward and of the backward; lse at a 4-byte offset;
-* a long sequence (N = 65573, both masks) on sampled rows;
+* a long sequence (N = 65573, both masks) on sampled rows, forward and backward (dQ rows
+  against the oracle's row-wise dQ, dV / dK sum invariants over every key);
 * many heads (B = 6, H = 37) of a short sequence, forward and backward.
 """
 import numpy as np
@@ -309,3 +310,27 @@ def test_long_sequence_forward_sampled_rows(causal):
         eo = compare(to_np(o[0, h])[rows], o_ref, torch.bfloat16, f"N={N} O h{h}")
         el = compare(to_np(lse[0, h])[rows], l_ref, torch.bfloat16, f"N={N} lse h{h}")
         log(f"    h{h} O {describe(eo)} | lse {describe(el)}")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_long_sequence_backward(causal):
+    """N = 65573 (ragged; 513 query tiles and 513 key blocks per head, offsets
+    far beyond the workload sizes): dQ on sampled rows against the oracle's
+    row-wise dQ, and the dV / dK sum invariants over every key."""
+    N, d = 65573, 128
+    q, k, v, do = make_inputs(1, 1, N, d, torch.bfloat16, seed=23, with_dout=True)
+    scale = d ** -0.5
+    log(f"[bwd] long sequence N={N} d={d} causal={causal}")
+    o, lse = gpu_forward(q, k, v, causal, scale)
+    dq, dk, dv = gpu_backward(q, k, v, o, lse, do, causal, scale)
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
+    sdv, sdo = dv.double().sum(2), do.double().sum(2)
+    assert torch.allclose(sdv, sdo, atol=2e-2 * N ** 0.5, rtol=1e-2)
+    sdk = dk.double().sum(2)
+    assert (sdk.abs() <= 2e-2 * N ** 0.5 + 1e-2 * dk.double().abs().sum(2)).all()
+    rows = sample_rows(N, 24, seed=41 + causal)
+    ref = oracle.attn_bwd_dq_rows(to_np(q[0, 0]), to_np(k[0, 0]), to_np(v[0, 0]), to_np(do[0, 0]),
+                                  causal, f32_scale(scale), rows)
+    e = compare(to_np(dq[0, 0])[rows], ref, torch.bfloat16, f"N={N} dq rows")
+    log(f"    dq rows={len(rows)} {describe(e)}")

@@ -9,7 +9,7 @@ tiles, which the library caps), the decode workload at full size, agreement
 with attn_fwd when Nq = Nk, a 131077-key cache, and bitwise determinism.
 
 attn_bwd_kv (the backward of attn_fwd_kv) against oracle_attn_bwd_rect: the
-same (Nq, Nk) shapes and more, d = 32 ... 256, both masks, Nq > Nk without
+same (Nq, Nk) shapes and more, d = 32 ... 256, both masks, scales 1.0 and 0.02, Nq > Nk without
 the mask, Nq = Nk bit for bit against attn_bwd, and the prefill workload.
 """
 import numpy as np
@@ -18,8 +18,8 @@ import torch
 
 import oracle
 from attn_inputs import KV_WORKLOADS, kv_workload_inputs, make_kv_inputs
-from tests.parity import (compare, describe, f32_scale, gpu_backward, gpu_forward, gpu_forward_kv,
-                          log, to_np)
+from tests.parity import (bwd_rounding_bound, compare, describe, f32_scale, gpu_backward,
+                          gpu_forward, gpu_forward_kv, log, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -155,17 +155,25 @@ def _dout(B, H, Nq, d, seed):
     return torch.randn(B, H, Nq, d, generator=g).to(torch.bfloat16)
 
 
-def _check_bwd(q, k, v, causal, tag, seed):
+def _check_bwd(q, k, v, causal, tag, seed, scale=None):
     d = q.shape[-1]
-    scale = d ** -0.5
+    default = scale is None
+    scale = d ** -0.5 if default else scale
     do = _dout(*q.shape, seed)
-    log(f"[bwd_kv] {tag} q={tuple(q.shape)} k={tuple(k.shape)} causal={causal}")
+    log(f"[bwd_kv] {tag} q={tuple(q.shape)} k={tuple(k.shape)} causal={causal} scale={scale:.4g}")
     o, lse = gpu_forward_kv(q, k, v, causal, scale, 0)
     dq, dk, dv = gpu_backward_kv(q, k, v, o, lse, do, causal, scale)
     ref = oracle.attn_bwd_rect(to_np(q), to_np(k), to_np(v), to_np(do), causal, f32_scale(scale))
-    for name, got in (("dq", dq), ("dk", dk), ("dv", dv)):
-        e = compare(to_np(got), ref[name], torch.bfloat16, f"{tag} {name}")
-        log(f"    {name} {describe(e)}")
+    for b in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            # at scales other than 1/sqrt(d) the stated tolerance plus the
+            # bound the bf16 rounding points of the backward give
+            bnd = None if default else bwd_rounding_bound(q[b, h], k[b, h], v[b, h], do[b, h],
+                                                          causal, scale)
+            for name, got in (("dq", dq), ("dk", dk), ("dv", dv)):
+                e = compare(to_np(got[b, h]), ref[name][b, h], torch.bfloat16, f"{tag} {name} h{h}",
+                            extra=None if bnd is None else bnd[name])
+                log(f"    {name} h{h} {describe(e)}")
 
 
 @pytest.mark.parametrize("Nq,Nk", [(7, 100), (64, 64), (128, 1000), (200, 333), (130, 2049),
@@ -178,6 +186,15 @@ def test_backward_shapes(Nq, Nk, d, causal):
     ragged tails on both sides, a single query."""
     q, k, v = make_kv_inputs(1, 2, Nq, Nk, d, seed=600 + Nq + Nk + d)
     _check_bwd(q, k, v, causal, f"Nq={Nq} Nk={Nk} d={d}", seed=610 + Nq + d)
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.02])
+@pytest.mark.parametrize("Nq,Nk,d", [(7, 100, 64), (130, 2049, 128), (200, 333, 256)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_other_scales(scale, Nq, Nk, d, causal):
+    q, k, v = make_kv_inputs(1, 2, Nq, Nk, d, seed=640 + Nq + d)
+    _check_bwd(q, k, v, causal, f"scale={scale} Nq={Nq} Nk={Nk} d={d}", seed=645 + Nq,
+               scale=scale)
 
 
 @pytest.mark.parametrize("Nq,Nk", [(300, 100), (129, 64)])
