@@ -273,15 +273,25 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         return Stats{*reinterpret_cast<const float4*>(lq + qrow0),
                      *reinterpret_cast<const float4*>(dq_d + qrow0)};
       };
-      // P = 2^{S scale log2e - L log2e} and dS = P (dP - D) for those rows
-      auto soft_part = [&](int qb, int r, const Stats& st4, auto mask_tag) {
+      // Entries [lo, hi) of block qb: P = 2^{S scale log2e - L log2e} and
+      // dS = P (dP - D), each bf16 pair converted as soon as both are done.
+      // Entry i belongs to query row qb*32 + (i/4)*8 + half*4 + i%4; its L and
+      // D are part i/4 of the block, held in sv[(i/4) & 1] and read one part
+      // ahead (the last part of block 0 reads the first of block 1).
+      Stats sv[2];
+      auto soft_range = [&](int qb, int lo, int hi, auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
-        const float lv[4] = {st4.l.x, st4.l.y, st4.l.z, st4.l.w};
-        const float dv4[4] = {st4.d.x, st4.d.y, st4.d.z, st4.d.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = r * 4 + e;
-          float p = fast_exp2(fmaf(sacc[qb][i], scale_log2, -lv[e]));
+        for (int i = lo; i < hi; ++i) {
+          const int r = i >> 2, e = i & 3;
+          if (e == 0) {
+            if (r + 1 < 4) sv[(r + 1) & 1] = read_stats(qb, r + 1);
+            else if (qb == 0) sv[0] = read_stats(1, 0);
+          }
+          const Stats& st4 = sv[r & 1];
+          const float lv = e == 0 ? st4.l.x : e == 1 ? st4.l.y : e == 2 ? st4.l.z : st4.l.w;
+          const float dv1 = e == 0 ? st4.d.x : e == 1 ? st4.d.y : e == 2 ? st4.d.z : st4.d.w;
+          float p = fast_exp2(fmaf(sacc[qb][i], scale_log2, -lv));
           if constexpr (MASK) {
             const int qq = q0 + qb * 32 + r * 8 + half * 4 + e;
             if (qq >= Nq || key >= Nk || (CAUSAL && key > qq + off)) p = 0.f;
@@ -289,25 +299,24 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
           // keep the exponential at this point of the issue order
           __asm__ volatile("" ::"v"(p));
           sacc[qb][i] = p;
-          pacc[qb][i] = p * (pacc[qb][i] - dv4[e]);
-        }
-      };
-      // P^T and dS^T of block qb as bf16 A operands (16 queries per t)
-      auto to_bf16 = [&](int qb) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            pa[qb][t][e] = (__bf16)sacc[qb][t * 8 + e];
-            sa[qb][t][e] = (__bf16)pacc[qb][t * 8 + e];
+          pacc[qb][i] = p * (pacc[qb][i] - dv1);
+          if (i & 1) {
+            pa[qb][i >> 3][(i & 7) - 1] = (__bf16)sacc[qb][i - 1];
+            pa[qb][i >> 3][i & 7] = (__bf16)sacc[qb][i];
+            sa[qb][i >> 3][(i & 7) - 1] = (__bf16)pacc[qb][i - 1];
+            sa[qb][i >> 3][i & 7] = (__bf16)pacc[qb][i];
           }
+        }
       };
 
       // The tile is one sequence of steps g: KS row steps of block 0 (A), KS
       // of block 1 (B), 2*DB transposed steps of block 0 (C) and of block 1
       // (D).  Both kinds read two bf16x8 fragments, so one ring of registers
       // holds the fragments of the next kPrefetch steps (two at d <= 64, where
-      // the second wave of the SIMD also hides LDS latency).
+      // the second wave of the SIMD also hides LDS latency).  The softmax of
+      // block 0 is spread evenly over the steps of B and that of block 1 over
+      // the steps of C, so that every step carries about the same VALU work
+      // beside its two MFMAs.
       constexpr int US = 2 * DB;
       constexpr int NSTEPS = 2 * KS + 2 * US;
       constexpr int kPrefetch = D <= 64 ? 2 : 3;
@@ -319,7 +328,6 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       };
       auto body = [&](auto mask_tag) {
         TrFrag ring[kPrefetch + 1];
-        Stats sv[2];
 #pragma unroll
         for (int g = 0; g < kPrefetch; ++g) ring[g] = read_step(g);
 #pragma clang loop unroll(full)
@@ -331,29 +339,15 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             mma_sdp(0, g, RowFrag{f.d, f.q});
             if (g == KS - 1) sv[0] = read_stats(0, 0);
           } else if (g < 2 * KS) {
-            // B: S, dP of block 1 | softmax part r of block 0 after step r*KS/4
+            // B: S, dP of block 1 | entries 16s/KS .. 16(s+1)/KS of block 0
             const int s = g - KS;
             mma_sdp(1, s, RowFrag{f.d, f.q});
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (r * KS / 4 == s) {
-                const Stats cur = sv[r & 1];
-                sv[(r + 1) & 1] = (r + 1 < 4) ? read_stats(0, r + 1) : read_stats(1, 0);
-                soft_part(0, r, cur, mask_tag);
-              }
-            if (s == KS - 1) to_bf16(0);
+            soft_range(0, 16 * s / KS, 16 * (s + 1) / KS, mask_tag);
           } else if (g < 2 * KS + US) {
-            // C: dV, dK of block 0 | softmax part r of block 1 after step r*US/4
+            // C: dV, dK of block 0 | entries 16u/US .. 16(u+1)/US of block 1
             const int u = g - 2 * KS;
             mma_dvdk(0, u, f);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (r * US / 4 == u) {
-                const Stats cur = sv[r & 1];
-                if (r + 1 < 4) sv[(r + 1) & 1] = read_stats(1, r + 1);
-                soft_part(1, r, cur, mask_tag);
-              }
-            if (u == US - 1) to_bf16(1);
+            soft_range(1, 16 * u / US, 16 * (u + 1) / US, mask_tag);
           } else {
             // D: dV, dK of block 1
             mma_dvdk(1, g - 2 * KS - US, f);
