@@ -205,12 +205,18 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   auto tile = [&](const int qt, auto cur_tag) {
     constexpr int CUR = decltype(cur_tag)::value;
     using Next = std::integral_constant<int, 1 - CUR>;
-    // Hold dK and dV in accumulation registers across the whole tile.
-    // Without this the register allocator moves all 128 values out to
+    // d >= 96: hold dK and dV in accumulation registers across the whole
+    // tile.  Without this the register allocator moves all 128 values out to
     // ordinary registers while S and dP occupy the accumulation registers
     // and back before dV += P^T dO, about 250 extra moves per tile.
+    // d <= 64: everything fits the 256 ordinary registers of a wave at two
+    // waves per SIMD; with no accumulation registers in the kernel every MFMA
+    // writes ordinary registers, and the softmax reads S and dP without the
+    // two v_accvgpr_read per entry (a third fewer VALU instructions per tile).
+    if constexpr (D > 64) {
 #pragma unroll
-    for (int b = 0; b < DB; ++b) __asm__ volatile("" : "+a"(dk_acc[b]), "+a"(dv_acc[b]));
+      for (int b = 0; b < DB; ++b) __asm__ volatile("" : "+a"(dk_acc[b]), "+a"(dv_acc[b]));
+    }
     if (qt + 1 < n_qtiles) load_tile(qt + 1, Next{});
 
     const int q0 = qt * kKvBQ;
