@@ -456,6 +456,21 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   }
   const float lq2 = qok ? lse[(int64_t)bh * Nq + qry] * kLog2e : 0.f;
   const float dlt = qok ? delta[(int64_t)bh * Nq + qry] : 0.f;
+  // d <= 64: dP^T - D on the matrix unit.  One more k-step of dP^T = V dO^T
+  // with an all-ones column pair in V (A operand) against -D split into two
+  // bf16 parts in dO (B operand) subtracts D_hi + D_lo = D (to 2^-16
+  // relative) from every entry of the lane's query, in place of 16 VALU
+  // subtractions per 32-key half.
+  constexpr bool kFoldD = D <= 64;
+  bf16x8 ones_x = {}, negd_x = {};
+  if (kFoldD && half == 0) {
+    const __bf16 dhi = (__bf16)(-dlt);
+    const __bf16 dlo = (__bf16)(-dlt - (float)dhi);
+    ones_x[0] = (__bf16)1.f;
+    ones_x[1] = (__bf16)1.f;
+    negd_x[0] = dhi;
+    negd_x[1] = dlo;
+  }
 
   // keys past the last one the workgroup's last query sees are not visited
   const int kv_end =
@@ -510,6 +525,7 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
           const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(ks + at);
           sacc[kb] = mfma_32x32x16(a, qf[s], sacc[kb]);
           const bf16x8 b = *reinterpret_cast<const ATTN_LDS bf16x8*>(vs + at);
+          if (kFoldD && s == 0) pacc[kb] = mfma_32x32x16(ones_x, negd_x, pacc[kb]);
           pacc[kb] = mfma_32x32x16(b, df[s], pacc[kb]);
         };
         // P^T = 2^{S^T scale log2e - L}, dS^T = P^T (dP^T - D) for accumulator
@@ -526,7 +542,7 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             }
             // keep the exponential at this point of the issue order
             __asm__ volatile("" ::"v"(p));
-            sf[kb][i >> 3][i & 7] = (__bf16)(p * (pacc[kb][i] - dlt));
+            sf[kb][i >> 3][i & 7] = (__bf16)(p * (kFoldD ? pacc[kb][i] : pacc[kb][i] - dlt));
           }
         };
         // dQ^T += K^T dS^T for 16 keys (t) and 32 d rows (b) of half kb
