@@ -63,11 +63,13 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   constexpr int RB = Tile::kRowBytes;
   constexpr int KS = D / 16;  // k-steps of the S^T MFMA
   constexpr int DB = D / 32;  // 32-wide d blocks of O^T
-  // d = 128: S^T of tile j+1 is computed during the softmax of tile j (the
-  // MFMA work per tile is large enough to hide the exponentials).  Other d:
+  // d = 128 and 256: S^T of tile j+1 is computed during the softmax of tile
+  // j (the MFMA work per tile is large enough to hide the exponentials; at
+  // d = 256, one wave per SIMD, it is the only overlap there is).  Other d:
   // S^T of a tile is computed at the start of its own step, which keeps the
-  // register count low (d = 64: low enough for more waves per SIMD).
-  constexpr bool kPipelineQK = (D == 128);
+  // register count low (d = 64: low enough for more waves per SIMD; d = 96
+  // has six k-steps, which do not split the 32 scores evenly).
+  constexpr bool kPipelineQK = (D == 128 || D == 256);
   // K and V tiles of 64 keys (SwzTile layout), two buffers each.  One LDS
   // object per buffer: the compiler then knows that the copies into one
   // buffer cannot alias reads of another and does not wait for them.
@@ -265,17 +267,19 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     constexpr int US = 4 * DB;
     if constexpr (NEXT) {
       // k-step s issues the two MFMAs of S^T of tile j+1 for that step, the
-      // exponentials of 32 / KS scores of tile j and, from s = 2 on, two
-      // steps of O^T += V^T P^T of tile j: PV step u needs the scores of its
-      // 16 keys, which exp parts 2 kt and 2 kt + 1 produce, and is issued at
-      // k-step 2 + u / 2 >= 2 kt + 2.  The last four PV steps follow the
-      // loop.  MFMA and VALU work are thus spread evenly over the step.
-      static_assert(KS == 8 && US == 16, "schedule written for d = 128");
+      // exponentials of 32 / KS scores of tile j and, from s = kPvStart on,
+      // two steps of O^T += V^T P^T of tile j: PV step u needs the scores of
+      // its 16 keys kt = u / DB, which the exp parts up to (8 kt + 7) / (32 /
+      // KS) produce, and is issued at k-step kPvStart + u / 2, which is later
+      // (d = 128: parts of 4 scores, start 2; d = 256: parts of 2, start 4).
+      // The last 2 kPvStart PV steps follow the loop.  MFMA and VALU work are
+      // thus spread evenly over the step.
+      static_assert(32 % KS == 0 && US == 2 * KS, "two PV steps per k-step");
       // While in this loop the wave takes issue priority over the other wave
       // of its SIMD (which may be issuing copies or a row maximum), so that
       // the matrix unit stays fed.
       __builtin_amdgcn_s_setprio(1);
-      constexpr int kPvStart = 2;
+      constexpr int kPvStart = 7 / (32 / KS) + 1;  // k-step after the part holding score 7
       constexpr int kPvInLoop = 2 * (KS - kPvStart);
       const ATTN_LDS unsigned char* kbuf = k_lds(Other{});
       sn[0] = f32x16{};
