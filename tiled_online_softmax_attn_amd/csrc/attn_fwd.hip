@@ -52,12 +52,21 @@ __device__ __forceinline__ void fwd_tile_coords(int bid, int BH, int n_qtiles, b
 // One code path serves both masks: query i sees keys j with j - i <= off,
 // off = 0 under the causal mask and off = N without it (every key visible).
 // A separate unmasked instantiation spilled registers at d = 96 and 128.
-template <int D>
+//
+// PARTIAL: the same computation for Nq queries against Nk keys (the queries
+// are the last Nq positions: off = Nk - Nq under the causal mask, Nk without
+// it), with the keys cut into chunks of `chunk` keys (a multiple of the tile
+// size).  Workgroup (split, query tile, head) walks chunk `split` only and
+// writes that chunk's partial result for the merge: O_c normalised by the
+// chunk's own sum (fp32, [split][bh][Nq][D]) and lse_c over the chunk's keys
+// ([split][bh][Nq], natural log, -inf with O_c = 0 where no key of the chunk
+// is visible).  Without PARTIAL: Nq = Nk = N, one chunk, bf16 O and lse.
+template <int D, bool PARTIAL>
 __global__ void __launch_bounds__(kFwdThreads, D > 128 ? 1 : 2)
 attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-                     const __bf16* __restrict__ v, __bf16* __restrict__ o,
-                     float* __restrict__ lse, int BH, int N, int n_qtiles, int off,
-                     float scale_log2) {
+                     const __bf16* __restrict__ v, void* __restrict__ o_out,
+                     float* __restrict__ lse, int BH, int Nq, int Nk, int n_qtiles, int off,
+                     int chunk, float scale_log2) {
   using Tile = SwzTile<tile_width(D), D>;
   static_assert(kFwdBK == Tile::kRows, "K/V tile is one SwzTile");
   constexpr int RB = Tile::kRowBytes;
@@ -93,12 +102,17 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int l32 = lane & 31;
   const int half = lane >> 5;
 
-  int bh, qt;
-  fwd_tile_coords(blockIdx.x, BH, n_qtiles, true, bh, qt);
-  const int64_t head = (int64_t)bh * N * D;
-  const __bf16* qh = q + head;
-  const __bf16* kh = k + head;
-  const __bf16* vh = v + head;
+  // workgroup id -> (head, query tile, key chunk); heavy causal query tiles
+  // first, consecutive ids on different heads (see fwd_tile_coords)
+  const int rank = blockIdx.x / BH;
+  const int bh = blockIdx.x - rank * BH;
+  const int split = PARTIAL ? rank / n_qtiles : 0;
+  const int qt = n_qtiles - 1 - (rank - split * n_qtiles);
+  const int64_t qhead = (int64_t)bh * Nq * D;
+  const int64_t khead = (int64_t)bh * Nk * D;
+  const __bf16* qh = q + qhead;
+  const __bf16* kh = k + khead;
+  const __bf16* vh = v + khead;
 
   const int q_wave0 = qt * kFwdBQ + wave * 32;  // first query of this wave
   const int qry = q_wave0 + l32;                 // this lane's query
@@ -107,17 +121,22 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   bf16x8 qf[KS];
   {
     const bf16x8 zero = {};
-    const __bf16* qrow = qh + (int64_t)(qry < N ? qry : 0) * D + half * 8;
+    const __bf16* qrow = qh + (int64_t)(qry < Nq ? qry : 0) * D + half * 8;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      qf[s] = (qry < N) ? *reinterpret_cast<const bf16x8*>(qrow + 16 * s) : zero;
+      qf[s] = (qry < Nq) ? *reinterpret_cast<const bf16x8*>(qrow + 16 * s) : zero;
   }
 
-  const int kv_end = (int)min((int64_t)N, (int64_t)(qt + 1) * kFwdBQ + off);
-  const int n_tiles = (kv_end + kFwdBK - 1) / kFwdBK;
+  // Key tiles t_begin .. t_begin + n_tiles - 1: the chunk's keys, up to the
+  // last one the workgroup's last query sees.
+  const int key_begin = PARTIAL ? split * chunk : 0;
+  const int64_t chunk_end = PARTIAL ? min((int64_t)Nk, (int64_t)key_begin + chunk) : (int64_t)Nk;
+  const int kv_end = (int)min(chunk_end, (int64_t)min(Nq, (qt + 1) * kFwdBQ) + off);
+  const int t_begin = key_begin / kFwdBK;
+  const int n_tiles = kv_end > key_begin ? (kv_end + kFwdBK - 1) / kFwdBK - t_begin : 0;
 
   auto load_tile = [&](const __bf16* src, int j, ATTN_LDS unsigned char* dst) {
-    Tile::template load<kFwdThreads / 64>(src, j * kFwdBK, N, dst, wave, lane);
+    Tile::template load<kFwdThreads / 64>(src, j * kFwdBK, Nk, dst, wave, lane);
   };
   // per-lane LDS read offsets: K rows (A operand of S^T) and V transpose reads
   const int k_base = Tile::row_read_base(l32, half);
@@ -196,7 +215,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = key0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-          if (key >= N || key - qry > off) sc[kb][i] = -INFINITY;
+          if (key >= Nk || key - qry > off) sc[kb][i] = -INFINITY;
         }
     }
 
@@ -350,10 +369,13 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
   };
 
-  // Last tile this wave computes: under the causal mask, later tiles lie
-  // wholly in the future of all 32 of its queries (wave-uniform).
+  // Last tile (counted from t_begin) this wave computes: under the causal
+  // mask, later tiles lie wholly in the future of all of its queries; a wave
+  // whose queries all lie past Nq computes none (wave-uniform).
   const int last_tile =
-      (int)min((int64_t)n_tiles - 1, ((int64_t)q_wave0 + 31 + off) / kFwdBK);
+      q_wave0 >= Nq ? -1
+                    : (int)min((int64_t)n_tiles - 1,
+                               ((int64_t)min(Nq - 1, q_wave0 + 31) + off) / kFwdBK - t_begin);
 
   // One iteration of the workgroup loop.  Buffers, pipelined: in iteration j
   // the K tile j+1 and the V tile j are read; the copies of K tile j+2 (into
@@ -365,22 +387,23 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   auto iteration = [&](const int j, auto par_tag, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
     using Other = std::integral_constant<int, 1 - decltype(par_tag)::value>;
     if constexpr (kPipelineQK) {
-      if (j + 2 < n_tiles) load_tile(kh, j + 2, k_lds(par_tag));
+      if (j + 2 < n_tiles) load_tile(kh, t_begin + j + 2, k_lds(par_tag));
     } else {
-      if (j + 1 < n_tiles) load_tile(kh, j + 1, k_lds(Other{}));
+      if (j + 1 < n_tiles) load_tile(kh, t_begin + j + 1, k_lds(Other{}));
     }
-    if (j + 1 < n_tiles) load_tile(vh, j + 1, v_lds(Other{}));
+    if (j + 1 < n_tiles) load_tile(vh, t_begin + j + 1, v_lds(Other{}));
     if (j <= last_tile) {
-      const int key0 = j * kFwdBK;
+      const int jt = t_begin + j;  // tile index in the sequence
+      const int key0 = jt * kFwdBK;
       const bool need_mask =
-          (key0 + kFwdBK > N) || ((int64_t)key0 + kFwdBK - 1 > (int64_t)q_wave0 + off);
+          (key0 + kFwdBK > Nk) || ((int64_t)key0 + kFwdBK - 1 > (int64_t)q_wave0 + off);
       const bool next = j < last_tile;
       if (need_mask) {
-        if (next) step(j, par_tag, sc, sn, std::true_type{}, std::true_type{});
-        else step(j, par_tag, sc, sn, std::true_type{}, std::false_type{});
+        if (next) step(jt, par_tag, sc, sn, std::true_type{}, std::true_type{});
+        else step(jt, par_tag, sc, sn, std::true_type{}, std::false_type{});
       } else {
-        if (next) step(j, par_tag, sc, sn, std::false_type{}, std::true_type{});
-        else step(j, par_tag, sc, sn, std::false_type{}, std::false_type{});
+        if (next) step(jt, par_tag, sc, sn, std::false_type{}, std::true_type{});
+        else step(jt, par_tag, sc, sn, std::false_type{}, std::false_type{});
       }
     }
     wait_vmem();
@@ -389,9 +412,9 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 
   // prologue: K tiles 0 and 1 and V tile 0 in LDS (and, pipelined, S^T of
   // tile 0 in registers)
-  load_tile(kh, 0, k_lds(Par0{}));
-  load_tile(vh, 0, v_lds(Par0{}));
-  if (kPipelineQK && n_tiles > 1) load_tile(kh, 1, k_lds(Par1{}));
+  load_tile(kh, t_begin, k_lds(Par0{}));
+  load_tile(vh, t_begin, v_lds(Par0{}));
+  if (kPipelineQK && n_tiles > 1) load_tile(kh, t_begin + 1, k_lds(Par1{}));
   wait_vmem();
   __syncthreads();
   f32x16 s_even[2], s_odd[2];
@@ -408,19 +431,36 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // ---- epilogue: O = O / l, lse = ln2 * (m + log2 l)
   const float l_tot = kSumOnMfma ? lacc[0] : sum_across_halves(l_run);
   const float m_run = m_ref;
-  if (qry < N) {
-    const float inv = 1.f / l_tot;
-    __bf16* orow = o + head + (int64_t)qry * D;
+  if (qry < Nq) {
+    if constexpr (PARTIAL) {
+      // chunk `split`'s partial result (l = 0: no key of the chunk visible)
+      const int64_t prow = ((int64_t)split * BH + bh) * Nq + qry;
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      float* orow = (float*)o_out + prow * D;
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
+      for (int b = 0; b < DB; ++b)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        bf16x4 w;
+        for (int r = 0; r < 4; ++r) {
+          f32x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(oacc[b][r * 4 + e] * inv);
-        *reinterpret_cast<bf16x4*>(orow + b * 32 + r * 8 + half * 4) = w;
-      }
-    if (half == 0) lse[(int64_t)bh * N + qry] = kLn2 * (m_run + fast_log2(l_tot));
+          for (int e = 0; e < 4; ++e) w[e] = oacc[b][r * 4 + e] * inv;
+          *reinterpret_cast<f32x4*>(orow + b * 32 + r * 8 + half * 4) = w;
+        }
+      if (half == 0) lse[prow] = l_tot > 0.f ? kLn2 * (m_run + fast_log2(l_tot)) : -INFINITY;
+    } else {
+      const float inv = 1.f / l_tot;
+      __bf16* orow = (__bf16*)o_out + qhead + (int64_t)qry * D;
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          bf16x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(oacc[b][r * 4 + e] * inv);
+          *reinterpret_cast<bf16x4*>(orow + b * 32 + r * 8 + half * 4) = w;
+        }
+      if (half == 0) lse[(int64_t)bh * Nq + qry] = kLn2 * (m_run + fast_log2(l_tot));
+    }
   }
 }
 
@@ -524,10 +564,23 @@ template <int D>
 hipError_t launch_bf16(const FwdArgs& a) {
   const int n_qtiles = (a.N + kFwdBQ - 1) / kFwdBQ;
   const int BH = a.B * a.H;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D>), dim3((unsigned)(BH * n_qtiles)),
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false>), dim3((unsigned)(BH * n_qtiles)),
                      dim3(kFwdThreads), 0, (hipStream_t)a.stream, (const __bf16*)a.q,
-                     (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse, BH, a.N,
-                     n_qtiles, a.causal ? 0 : a.N, a.scale * kLog2e);
+                     (const __bf16*)a.k, (const __bf16*)a.v, a.o, a.lse, BH, a.N, a.N,
+                     n_qtiles, a.causal ? 0 : a.N, 0, a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_partial(const FwdKvArgs& a, const KvSplit& sp, float* o_part,
+                          float* lse_part) {
+  const int n_qtiles = (a.Nq + kFwdBQ - 1) / kFwdBQ;
+  const int BH = a.B * a.H;
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true>),
+                     dim3((unsigned)((int64_t)BH * n_qtiles * sp.splits)), dim3(kFwdThreads), 0,
+                     (hipStream_t)a.stream, (const __bf16*)a.q, (const __bf16*)a.k,
+                     (const __bf16*)a.v, (void*)o_part, lse_part, BH, a.Nq, a.Nk, n_qtiles,
+                     a.causal ? a.Nk - a.Nq : a.Nk, sp.chunk, a.scale * kLog2e);
   return hipGetLastError();
 }
 
@@ -550,6 +603,18 @@ hipError_t launch_fwd_d(const FwdArgs& a) {
 }
 
 }  // namespace
+
+hipError_t launch_fwd_kv_partial(const FwdKvArgs& a, const KvSplit& sp, float* o_part,
+                                 float* lse_part) {
+  switch (a.d) {
+    case 32: return launch_partial<32>(a, sp, o_part, lse_part);
+    case 64: return launch_partial<64>(a, sp, o_part, lse_part);
+    case 96: return launch_partial<96>(a, sp, o_part, lse_part);
+    case 128: return launch_partial<128>(a, sp, o_part, lse_part);
+    case 256: return launch_partial<256>(a, sp, o_part, lse_part);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_fwd(const FwdArgs& a) {
   switch (a.d) {

@@ -74,6 +74,11 @@ struct KvSplit {
   size_t lse_part_bytes;  // fp32 [splits][B*H][Nq], rounded up to 256
 };
 KvSplit kv_split_plan(int B, int H, int Nq, int Nk, int d, int num_splits);
+// The forward kernel of attn_fwd over chunk `split` of the keys, for every
+// chunk (B*H*ceil(Nq/128)*splits workgroups): each chunk's O_c (fp32,
+// normalised by the chunk's own sum) and lse_c into o_part / lse_part.
+hipError_t launch_fwd_kv_partial(const FwdKvArgs& a, const KvSplit& sp, float* o_part,
+                                 float* lse_part);
 
 // Forward with Q and K in MXFP8 (E4M3 codes, one E8M0 scale per 32 elements
 // along d) and V in bf16 (attn_fwd_mx).
