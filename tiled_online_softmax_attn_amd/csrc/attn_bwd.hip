@@ -530,10 +530,10 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         };
         // P^T = 2^{S^T scale log2e - L}, dS^T = P^T (dP^T - D) for accumulator
         // entries 4 r .. 4 r + 3 of half kb, as bf16 B operand
-        auto soft_part = [&](int kb, int r, auto mask_tag) {
+        auto soft_part = [&](int kb, int r, int e0, int e1, auto mask_tag) {
           constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
+          for (int e = e0; e < e1; ++e) {
             const int i = r * 4 + e;
             float p = fast_exp2(fmaf(sacc[kb][i], scale_log2, -lq2));
             if constexpr (MASK) {
@@ -545,12 +545,27 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             sf[kb][i >> 3][i & 7] = (__bf16)(p * (kFoldD ? pacc[kb][i] : pacc[kb][i] - dlt));
           }
         };
-        // dQ^T += K^T dS^T for 16 keys (t) and 32 d rows (b) of half kb
-        auto dq_step = [&](int kb, int t, int b) {
+        // K^T fragment of dQ^T step g: steps 0 .. 2DB-1 are half 0 (C),
+        // 2DB .. 4DB-1 half 1 (D); step u of a half covers 16 keys (t) and
+        // 32 d rows (b)
+        constexpr int UQ = 2 * DB;
+        auto read_kt = [&](int g) {
+          const int kb = g / UQ, u = g % UQ, t = u / DB, b = u % DB;
           const int roff = (kb * 32 + t * 16) * RB;
-          const bf16x8 ka = concat4(lds_read_tr4((const ATTN_LDS __bf16*)(ks + (tr_lo ^ (64 * b)) + roff)),
-                                    lds_read_tr4((const ATTN_LDS __bf16*)(ks + (tr_hi ^ (64 * b)) + roff)));
+          return concat4(lds_read_tr4((const ATTN_LDS __bf16*)(ks + (tr_lo ^ (64 * b)) + roff)),
+                         lds_read_tr4((const ATTN_LDS __bf16*)(ks + (tr_hi ^ (64 * b)) + roff)));
+        };
+        auto dq_step = [&](int g, const bf16x8& ka) {
+          const int kb = g / UQ, u = g % UQ, t = u / DB, b = u % DB;
           dq_acc[b] = mfma_32x32x16(ka, sf[kb][t], dq_acc[b]);
+        };
+        // softmax entries [lo, hi) of half kb
+        auto soft_range = [&](int kb, int lo, int hi, auto mask_tag) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int a = max(lo, 4 * r), z = min(hi, 4 * r + 4);
+            if (a < z) soft_part(kb, r, a - 4 * r, z - 4 * r, mask_tag);
+          }
         };
 
         auto body = [&](auto mask_tag) {
@@ -558,27 +573,24 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
           for (int s = 0; s < KS; ++s) sdp_step(0, s);
           __builtin_amdgcn_sched_barrier(0);
-          // B: softmax part r of half 0 after k-step r*KS/4 of half 1
+          // B: entries 16s/KS .. 16(s+1)/KS of half 0's softmax per k-step
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
             sdp_step(1, s);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (r * KS / 4 == s) soft_part(0, r, mask_tag);
+            soft_range(0, 16 * s / KS, 16 * (s + 1) / KS, mask_tag);
             __builtin_amdgcn_sched_barrier(0);
           }
-          // C: softmax part r of half 1 after dQ step r*2*DB/4 of half 0
+          // C, D: dQ^T steps of half 0 then half 1, each step's K^T fragment
+          // read one step ahead; C carries half 1's softmax, spread evenly
+          bf16x8 kr[2];
+          kr[0] = read_kt(0);
 #pragma unroll
-          for (int u = 0; u < 2 * DB; ++u) {
-            dq_step(0, u / DB, u % DB);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (r * 2 * DB / 4 == u) soft_part(1, r, mask_tag);
+          for (int g = 0; g < 2 * UQ; ++g) {
+            if (g + 1 < 2 * UQ) kr[(g + 1) & 1] = read_kt(g + 1);
+            dq_step(g, kr[g & 1]);
+            if (g < UQ) soft_range(1, 16 * g / UQ, 16 * (g + 1) / UQ, mask_tag);
             __builtin_amdgcn_sched_barrier(0);
           }
-          // D
-#pragma unroll
-          for (int u = 0; u < 2 * DB; ++u) dq_step(1, u / DB, u % DB);
         };
         if (need_mask)
           body(std::true_type{});
