@@ -86,10 +86,12 @@ constexpr int kKvBQ = 64;   // queries per inner step (one SwzTile)
 // accumulating 128 columns; both compute S and dP over the full d.
 constexpr int bwd_out_cols(int d) { return d > 128 ? 128 : d; }
 
-// d <= 64 fits two waves per SIMD (256 registers each, a shorter operand
-// ring below); d = 96 and above need one wave's whole register file.
+// d = 32 fits three waves per SIMD (168 registers each, a one-step operand
+// ring below: 186.8 -> 172.1 us against two waves on B4 H16 N4096 d32
+// causal), d = 64 two (256 registers each, a two-step ring); d = 96 and above
+// need one wave's whole register file.
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(kBwdThreads, D <= 64 ? 2 : 1)
+__global__ void __launch_bounds__(kBwdThreads, D <= 32 ? 3 : D <= 64 ? 2 : 1)
 bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 const __bf16* __restrict__ v, const __bf16* __restrict__ dout,
                 const float* __restrict__ lse, const float* __restrict__ delta,
@@ -318,14 +320,14 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       // The tile is one sequence of steps g: KS row steps of block 0 (A), KS
       // of block 1 (B), 2*DB transposed steps of block 0 (C) and of block 1
       // (D).  Both kinds read two bf16x8 fragments, so one ring of registers
-      // holds the fragments of the next kPrefetch steps (two at d <= 64, where
-      // the second wave of the SIMD also hides LDS latency).  The softmax of
-      // block 0 is spread evenly over the steps of B and that of block 1 over
-      // the steps of C, so that every step carries about the same VALU work
-      // beside its two MFMAs.
+      // holds the fragments of the next kPrefetch steps (one at d = 32 and two
+      // at d = 64, where the other waves of the SIMD also hide LDS latency).
+      // The softmax of block 0 is spread evenly over the steps of B and that
+      // of block 1 over the steps of C, so that every step carries about the
+      // same VALU work beside its two MFMAs.
       constexpr int US = 2 * DB;
       constexpr int NSTEPS = 2 * KS + 2 * US;
-      constexpr int kPrefetch = D <= 64 ? 2 : 3;
+      constexpr int kPrefetch = D <= 32 ? 1 : D <= 64 ? 2 : 3;
       auto read_step = [&](int g) {
         if (g < KS) { const RowFrag f = read_row(0, g); return TrFrag{f.q, f.d}; }
         if (g < 2 * KS) { const RowFrag f = read_row(1, g - KS); return TrFrag{f.q, f.d}; }
