@@ -49,6 +49,29 @@ __device__ __forceinline__ void fwd_tile_coords(int bid, int BH, int n_qtiles, b
   qt = causal ? (n_qtiles - 1 - rank) : rank;
 }
 
+// Interleaved schedule of the pipelined forward (KS k-steps, exponentials of
+// scores [32 s / KS, 32 (s + 1) / KS) in k-step s, two PV steps per k-step
+// from kPvStart on): the part holding score e, and the first k-step from
+// which every PV step issued in the loop finds the 8 scores of its 16 keys
+// (kt = u / DB) exponentiated in an earlier k-step.
+constexpr int exp_part_of(int e, int ks) {
+  int p = 0;
+  while (32 * (p + 1) / ks <= e) ++p;
+  return p;
+}
+constexpr int pv_start(int ks, int db) {
+  for (int start = 1; start < ks; ++start) {
+    bool ok = true;
+    for (int s = start; s < ks; ++s)
+      for (int j = 0; j < 2; ++j)
+        if (exp_part_of(8 * ((2 * (s - start) + j) / db) + 7, ks) >= s) ok = false;
+    if (ok) return start;
+  }
+  return ks;
+}
+static_assert(pv_start(8, 4) == 2 && pv_start(16, 8) == 4 && pv_start(6, 3) == 2,
+              "PV start of d = 128, 256 and 96");
+
 // One code path serves both masks: query i sees keys j with j - i <= off,
 // off = 0 under the causal mask and off = N without it (every key visible).
 // A separate unmasked instantiation spilled registers at d = 96 and 128.
@@ -72,13 +95,12 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   constexpr int RB = Tile::kRowBytes;
   constexpr int KS = D / 16;  // k-steps of the S^T MFMA
   constexpr int DB = D / 32;  // 32-wide d blocks of O^T
-  // d = 128 and 256: S^T of tile j+1 is computed during the softmax of tile
-  // j (the MFMA work per tile is large enough to hide the exponentials; at
-  // d = 256, one wave per SIMD, it is the only overlap there is).  Other d:
-  // S^T of a tile is computed at the start of its own step, which keeps the
-  // register count low (d = 64: low enough for more waves per SIMD; d = 96
-  // has six k-steps, which do not split the 32 scores evenly).
-  constexpr bool kPipelineQK = (D == 128 || D == 256);
+  // d >= 96: S^T of tile j+1 is computed during the softmax of tile j (the
+  // MFMA work per tile is large enough to hide the exponentials; at d = 256,
+  // one wave per SIMD, it is the only overlap there is).  d <= 64: S^T of a
+  // tile is computed at the start of its own step, which keeps the register
+  // count low enough for more waves per SIMD (measured faster there).
+  constexpr bool kPipelineQK = (D == 96 || D == 128 || D == 256);
   // K and V tiles of 64 keys (SwzTile layout), two buffers each.  One LDS
   // object per buffer: the compiler then knows that the copies into one
   // buffer cannot alias reads of another and does not wait for them.
@@ -251,13 +273,12 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     // one step earlier) and then the exponentials of 32 / KS scores.
     float psum = 0.f;
     bf16x8 pf[2][2];
-    // the 32 scores of the lane in kExpParts equal parts
-    constexpr int kExpParts = (32 % KS == 0) ? KS : 8;
+    // the 32 scores of the lane in kExpParts parts (one per k-step of the
+    // pipelined loop; of 5 or 6 scores at d = 96)
+    constexpr int kExpParts = (32 % KS == 0 || kPipelineQK) ? KS : 8;
     auto exp_part = [&](int part) {
-      constexpr int PER = 32 / kExpParts;
 #pragma unroll
-      for (int u = 0; u < PER; ++u) {
-        const int e = part * PER + u;
+      for (int e = 32 * part / kExpParts; e < 32 * (part + 1) / kExpParts; ++e) {
         const int kb = e >> 4, i = e & 15;
         const float p = fast_exp2(fmaf(sc[kb][i], scale_log2, -m_off));
         // keep the exponential at this point of the issue order (it would
@@ -286,19 +307,19 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     constexpr int US = 4 * DB;
     if constexpr (NEXT) {
       // k-step s issues the two MFMAs of S^T of tile j+1 for that step, the
-      // exponentials of 32 / KS scores of tile j and, from s = kPvStart on,
-      // two steps of O^T += V^T P^T of tile j: PV step u needs the scores of
-      // its 16 keys kt = u / DB, which the exp parts up to (8 kt + 7) / (32 /
-      // KS) produce, and is issued at k-step kPvStart + u / 2, which is later
-      // (d = 128: parts of 4 scores, start 2; d = 256: parts of 2, start 4).
-      // The last 2 kPvStart PV steps follow the loop.  MFMA and VALU work are
-      // thus spread evenly over the step.
-      static_assert(32 % KS == 0 && US == 2 * KS, "two PV steps per k-step");
+      // exponentials of scores [32 s / KS, 32 (s + 1) / KS) of tile j and,
+      // from s = kPvStart on, two steps of O^T += V^T P^T of tile j: PV step u
+      // needs the 8 scores of its 16 keys kt = u / DB, and kPvStart is the
+      // first k-step for which every PV step issued in the loop finds them
+      // exponentiated in an earlier k-step (pv_start: 2 at d = 96 and 128, 4
+      // at d = 256).  The last 2 kPvStart PV steps follow the loop.  MFMA and
+      // VALU work are thus spread evenly over the step.
+      static_assert(US == 2 * KS, "two PV steps per k-step");
       // While in this loop the wave takes issue priority over the other wave
       // of its SIMD (which may be issuing copies or a row maximum), so that
       // the matrix unit stays fed.
       __builtin_amdgcn_s_setprio(1);
-      constexpr int kPvStart = 7 / (32 / KS) + 1;  // k-step after the part holding score 7
+      constexpr int kPvStart = pv_start(KS, DB);
       constexpr int kPvInLoop = 2 * (KS - kPvStart);
       const ATTN_LDS unsigned char* kbuf = k_lds(Other{});
       sn[0] = f32x16{};
