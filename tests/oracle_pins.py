@@ -158,49 +158,52 @@ def pin_blocked_identity(lib):
         _assert_close(p, ref, 1e-14, 1e-300, "softmax definition")
 
 
-def _stream_one_key(q, k, v, causal, scale):
-    """PDC notes 4.13.3: keys one at a time with a running (m, l, o)."""
-    N, d = q.shape
-    O = np.zeros((N, d))
-    for i in range(N):
-        m, l, o = -math.inf, 0.0, np.zeros(d)
-        for j in range(N if not causal else i + 1):
-            x = scale * float(q[i] @ k[j])
-            m_new = max(m, x)
-            l = l * math.exp(m - m_new) + math.exp(x - m_new)
-            o = o * math.exp(m - m_new) + math.exp(x - m_new) * v[j]
-            m = m_new
-        O[i] = o / l
-    return O
+def _merge_states(a, b):
+    """Combine the softmax states of two disjoint key sets, for every query
+    row at once: a state is (m, l, o) with m the row maximum of the scores,
+    l = sum e^{s - m} and o = sum e^{s - m} v over its keys (CS149 L9 notes
+    section 9, the blocked-softmax identity).  m = -inf, l = 0, o = 0 is the
+    state of no visible key and leaves the other operand unchanged."""
+    ma, la, oa = a
+    mb, lb, ob = b
+    m = np.maximum(ma, mb)
+    base = np.where(np.isfinite(m), m, 0.0)
+
+    def weight(mx):
+        return np.where(np.isfinite(mx), np.exp(np.where(np.isfinite(mx), mx, 0.0) - base), 0.0)
+
+    wa, wb = weight(ma), weight(mb)
+    return m, la * wa + lb * wb, oa * wa[:, None] + ob * wb[:, None]
 
 
-def _blocked_alpha_beta(q, k, v, causal, scale, bq, bk):
-    """CS149 L9 notes Example 4 structure: Q blocks outside, K/V blocks
-    inside, per-block max and alpha/beta rescale, normalise at the end."""
-    N, d = q.shape
-    O = np.zeros((N, d))
-    m_run = np.full(N, -np.inf)
-    l_run = np.zeros(N)
-    for i0 in range(0, N, bq):
-        qi = q[i0:i0 + bq]
-        rows = np.arange(i0, min(N, i0 + bq))
-        for j0 in range(0, N, bk):
-            cols = np.arange(j0, min(N, j0 + bk))
-            s = scale * (qi @ k[j0:j0 + bk].T)
-            if causal:
-                s = np.where(cols[None, :] > rows[:, None], -np.inf, s)
-            m_blk = s.max(axis=1)
-            live = np.isfinite(m_blk)
-            m_blk_safe = np.where(live, m_blk, 0.0)
-            p = np.where(live[:, None], np.exp(s - m_blk_safe[:, None]), 0.0)
-            l_blk = p.sum(axis=1)
-            m_new = np.maximum(m_run[rows], np.where(live, m_blk, -np.inf))
-            alpha = np.where(np.isfinite(m_run[rows]), np.exp(m_run[rows] - m_new), 0.0)
-            beta = np.where(live, np.exp(m_blk_safe - m_new), 0.0)
-            O[rows] = O[rows] * alpha[:, None] + (p * beta[:, None]) @ v[j0:j0 + bk]
-            l_run[rows] = l_run[rows] * alpha + l_blk * beta
-            m_run[rows] = m_new
-    return O / l_run[:, None], m_run + np.log(l_run)
+def _key_range_state(q, k, v, causal, scale, j0, j1):
+    """State (m, l, o) of keys j0 .. j1-1 for every query (query i sees key j
+    when j <= i under the causal mask)."""
+    s = scale * (q @ k[j0:j1].T)
+    if causal:
+        s = np.where(np.arange(j0, j1)[None, :] > np.arange(q.shape[0])[:, None], -np.inf, s)
+    m = s.max(axis=1)
+    base = np.where(np.isfinite(m), m, 0.0)
+    p = np.where(np.isfinite(s), np.exp(s - base[:, None]), 0.0)
+    return m, p.sum(axis=1), p @ v[j0:j1]
+
+
+def _attention_by_merging(q, k, v, causal, scale, bk, tree):
+    """O and lse from the states of key blocks of bk keys, merged left to
+    right (tree=False; bk = 1 is the key-at-a-time online softmax of the PDC
+    notes section 4.13.3) or pairwise as a balanced tree (tree=True)."""
+    n = k.shape[0]
+    states = [_key_range_state(q, k, v, causal, scale, j0, min(n, j0 + bk)) for j0 in range(0, n, bk)]
+    if tree:
+        while len(states) > 1:
+            states = [_merge_states(states[i], states[i + 1]) if i + 1 < len(states) else states[i]
+                      for i in range(0, len(states), 2)]
+        m, l, o = states[0]
+    else:
+        m, l, o = states[0]
+        for st in states[1:]:
+            m, l, o = _merge_states((m, l, o), st)
+    return o / l[:, None], m + np.log(l)
 
 
 def pin_streaming_and_blocked(lib):
@@ -209,11 +212,14 @@ def pin_streaming_and_blocked(lib):
         q, k, v = rng.normal(size=(3, N, d))
         scale = 1 / math.sqrt(d)
         o, lse = oracle.attn_fwd(q, k, v, causal, scale, lib=lib)
-        _assert_close(_stream_one_key(q, k, v, causal, scale), o, 1e-12, 1e-13, "streaming")
-        for bq, bk in [(4, 4), (5, 7), (16, 3), (N, N), (1, 1)]:
-            ob, lb = _blocked_alpha_beta(q, k, v, causal, scale, bq, bk)
-            _assert_close(ob, o, 1e-12, 1e-13, f"blocked {bq}x{bk}")
-            _assert_close(lb, lse, 1e-13, 1e-13, f"blocked lse {bq}x{bk}")
+        os_, ls_ = _attention_by_merging(q, k, v, causal, scale, 1, tree=False)
+        _assert_close(os_, o, 1e-12, 1e-13, "streaming")
+        _assert_close(ls_, lse, 1e-13, 1e-13, "streaming lse")
+        for bk in (3, 4, 7, N):
+            for tree in (False, True):
+                ob, lb = _attention_by_merging(q, k, v, causal, scale, bk, tree)
+                _assert_close(ob, o, 1e-12, 1e-13, f"blocked {bk} tree={tree}")
+                _assert_close(lb, lse, 1e-13, 1e-13, f"blocked lse {bk} tree={tree}")
 
 
 def pin_rows_sum_to_one(lib):
