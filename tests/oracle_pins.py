@@ -11,10 +11,11 @@ What pins what:
   softmax over [1, 3 | 2, 5] with printed m and l after each block.
 * blocked identities - CS149 Lecture 9 notes (Efficiently Evaluating DNNs on
   GPUs), section 9: m = max of block maxima, l = sum_b e^{m_b - m} l_b.
-* streaming and blocked loops - PDC notes Lecture 4, section 4.13.3 (one key
-  at a time with a running o) and CS149 L9 notes Example 4 (blocked loops
-  with per-block max and alpha/beta rescale), re-derived here independently;
-  block sizes that do not divide N as CS336 L5 notes Exercise 10 asks.
+* streaming and blocked evaluation - what PDC notes Lecture 4, section 4.13.3
+  (one key at a time with a running o) and CS149 L9 notes Example 4 (key
+  blocks with a per-block max) compute, done here with a vectorised merge of
+  partial softmax states folded left to right or as a tree; block sizes that
+  do not divide N as CS336 L5 notes Exercise 10 asks.
 * brute force - the textbook formula O_i = sum_j e^{s_ij} V_j / sum_j e^{s_ij}
   (no max subtraction) in 50-digit decimal arithmetic.
 * closed forms - Q = 0, constant V, causal row 0, N = 1.
