@@ -172,8 +172,12 @@ int attn_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse
                 int num_splits, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace attn_bwd_kv needs: the D vector (B*H*Nq fp32),
- * rounded up to a multiple of 256.  Returns 0 for invalid sizes, d above
- * 128 or an unsupported dtype. */
+ * rounded up to a multiple of 256, plus, when dQ is split over the keys,
+ * s partial results (s*B*H*Nq*d fp32, rounded up to a multiple of 256).  dQ
+ * is split when Nq < Nk and the w = B*H*ceil(Nq/128) query tiles are too few
+ * for the chip: s = number of chunks of ceil(T / m) key tiles, T = ceil(Nk/64),
+ * m = min(ceil(512 / w), max(1, floor(T / 8))), when that is above 1.
+ * Returns 0 for invalid sizes, an unsupported d or dtype. */
 size_t attn_bwd_kv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype);
 
 /* Backward of attn_fwd_kv (CS336 L5 notes section 8.4 with the mask of a
@@ -189,7 +193,9 @@ size_t attn_bwd_kv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtyp
  *   workspace      : at least attn_bwd_kv_workspace_bytes() bytes, caller-
  *                    owned, contents on entry ignored.
  * Nq = Nk is attn_bwd, bit for bit (the same kernels).  bf16.
- * Every output element is written once (no atomics).  Errors: those of
+ * With few queries the dQ sums over the keys run in chunks on separate
+ * workgroups and are added in chunk order, so results still do not depend on
+ * timing.  Every output element is written once (no atomics).  Errors: those of
  * attn_fwd_kv and attn_bwd.  Calls that share a workspace must not overlap. */
 int attn_bwd_kv(const void* q, const void* k, const void* v, const void* o, const void* dout,
                 const float* lse, void* dq, void* dk, void* dv, void* workspace,

@@ -216,7 +216,28 @@ def test_kv_validation(args, code):
 
 def test_bwd_kv_workspace_size():
     lib = _lib()
-    assert lib.attn_bwd_kv_workspace_bytes(2, 16, 512, 4096, 128, 1) == 2 * 16 * 512 * 4
+    r256 = lambda x: (x + 255) // 256 * 256
+
+    def expect(B, H, Nq, Nk, d):
+        # D, plus the fp32 dQ partials when dQ is split over the keys (attn.h)
+        n = r256(B * H * Nq * 4)
+        if Nq < Nk:
+            w = B * H * -(-Nq // 128)
+            T = -(-Nk // 64)
+            m = min(-(-512 // w), max(1, T // 8))
+            if m > 1:
+                per = -(-T // m)
+                s = -(-T // per)
+                if s > 1:
+                    n += r256(s * B * H * Nq * d * 4)
+        return n
+
+    for shape in ((2, 16, 512, 4096, 128), (1, 3, 7, 100, 64), (1, 1, 7, 100, 256),
+                  (1, 2, 128, 1000, 64), (1, 2, 130, 2049, 128), (8, 32, 512, 4096, 128),
+                  (1, 1, 300, 300, 64)):
+        assert lib.attn_bwd_kv_workspace_bytes(*shape, 1) == expect(*shape), shape
+    # the chunked-prefill shape splits dQ four ways; square and tiny shapes do not
+    assert lib.attn_bwd_kv_workspace_bytes(2, 16, 512, 4096, 128, 1) == 2 * 16 * 512 * 4 + 4 * 2 * 16 * 512 * 128 * 4
     assert lib.attn_bwd_kv_workspace_bytes(1, 3, 7, 100, 64, 1) == 256  # 84 bytes, rounded
     assert lib.attn_bwd_kv_workspace_bytes(1, 1, 7, 100, 256, 1) == 256
     assert lib.attn_bwd_kv_workspace_bytes(1, 1, 7, 100, 80, 1) == 0

@@ -229,7 +229,7 @@ size_t attn_bwd_kv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtyp
   if (check_kv_shape(B, H, Nq, Nk, d, 0, 0) != ATTN_OK || !attn::bwd_head_dim_supported(d) ||
       dtype != ATTN_DTYPE_BF16)
     return 0;
-  return attn::bwd_delta_bytes(B, H, Nq);
+  return attn::bwd_delta_bytes(B, H, Nq) + attn::bwd_dq_split_plan(B, H, Nq, Nk, d).part_bytes;
 }
 
 int attn_bwd_kv(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -251,6 +251,12 @@ int attn_bwd_kv(const void* q, const void* k, const void* v, const void* o, cons
   if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
   attn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, B, H, Nq, Nk, d,
                   causal != 0, scale, stream};
+  const attn::BwdDqSplit sp = attn::bwd_dq_split_plan(B, H, Nq, Nk, d);
+  if (sp.splits > 1) {
+    a.dq_part = (float*)((char*)workspace + attn::bwd_delta_bytes(B, H, Nq));
+    a.dq_splits = sp.splits;
+    a.dq_chunk = sp.chunk;
+  }
   return attn::launch_bwd(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

@@ -40,6 +40,8 @@
 #include "device_common.h"
 #include "attn_launch.h"
 
+#include <algorithm>
+
 #include <type_traits>
 
 namespace attn {
@@ -397,13 +399,16 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 constexpr int kDqBQ = 128;  // queries per workgroup (32 per wave)
 constexpr int kDqBK = 64;   // keys per K/V tile (one SwzTile)
 
-template <int D, bool CAUSAL>
+// PARTIAL: workgroup (split, query tile, head) sums dS K over key chunk
+// `split` only (chunk keys, a multiple of the tile) and writes scale * that
+// sum in fp32 to dq_part[split][bh][Nq][D] for bwd_dq_reduce_kernel.
+template <int D, bool CAUSAL, bool PARTIAL = false>
 __global__ void __launch_bounds__(kBwdThreads, D > 128 ? 1 : 2)
 bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
               const __bf16* __restrict__ v, const __bf16* __restrict__ dout,
               const float* __restrict__ lse, const float* __restrict__ delta,
               __bf16* __restrict__ dq, int BH, int Nq, int Nk, int off, int n_qtiles,
-              float scale, float scale_log2) {
+              float scale, float scale_log2, float* __restrict__ dq_part, int chunk) {
   using Tile = SwzTile<tile_width(D), D>;
   static_assert(kDqBK == Tile::kRows, "key tile is one SwzTile");
   constexpr int KS = D / 16;
@@ -432,10 +437,12 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int l32 = lane & 31;
   const int half = lane >> 5;
 
-  // workgroup id -> (head, query tile), heavy causal tiles first
+  // workgroup id -> (head, query tile[, key chunk]), heavy causal tiles first
   const int rank = blockIdx.x / BH;
   const int bh = blockIdx.x - rank * BH;
-  const int qt = CAUSAL ? (n_qtiles - 1 - rank) : rank;
+  const int split = PARTIAL ? rank / n_qtiles : 0;
+  const int qrank = rank - split * n_qtiles;
+  const int qt = CAUSAL ? (n_qtiles - 1 - qrank) : qrank;
   const int64_t qhead = (int64_t)bh * Nq * D;
   const int64_t khead = (int64_t)bh * Nk * D;
   const __bf16* kh = k + khead;
@@ -474,10 +481,13 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     negd_x[1] = dlo;
   }
 
-  // keys past the last one the workgroup's last query sees are not visited
-  const int kv_end =
-      CAUSAL ? (int)min((int64_t)Nk, (int64_t)(qt + 1) * kDqBQ + off) : Nk;
-  const int n_tiles = (kv_end + kDqBK - 1) / kDqBK;
+  // keys past the last one the workgroup's last query sees are not visited;
+  // a split visits only its chunk (key tiles t_begin .. t_begin + n_tiles - 1)
+  const int kv_all = CAUSAL ? (int)min((int64_t)Nk, (int64_t)(qt + 1) * kDqBQ + off) : Nk;
+  const int key_begin = PARTIAL ? split * chunk : 0;
+  const int kv_end = PARTIAL ? (int)min((int64_t)kv_all, (int64_t)key_begin + chunk) : kv_all;
+  const int t_begin = key_begin / kDqBK;
+  const int n_tiles = kv_end > key_begin ? (kv_end + kDqBK - 1) / kDqBK - t_begin : 0;
 
   auto load_tile = [&](int j, auto buf_tag) {
     Tile::template load<kBwdThreads / 64>(kh, j * kDqBK, Nk, k_lds(buf_tag), wave, lane);
@@ -491,16 +501,16 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
   for (int b = 0; b < DB; ++b) dq_acc[b] = f32x16{};
 
-  load_tile(0, Buf0{});
+  if (n_tiles > 0) load_tile(t_begin, Buf0{});
   wait_vmem();
   __syncthreads();
 
-  // One K/V tile j, held in buffer CUR; the copies of tile j+1 go to the
-  // other buffer meanwhile.
+  // One K/V tile t_begin + j, held in buffer CUR; the copies of the next go to
+  // the other buffer meanwhile.
   auto tile = [&](const int j, auto cur_tag) {
     using Next = std::integral_constant<int, 1 - decltype(cur_tag)::value>;
-    if (j + 1 < n_tiles) load_tile(j + 1, Next{});
-    const int key0 = j * kDqBK;
+    if (j + 1 < n_tiles) load_tile(t_begin + j + 1, Next{});
+    const int key0 = (t_begin + j) * kDqBK;
     const bool skip = CAUSAL && key0 > q_wave0 + 31 + off;
     if (!skip) {
       const ATTN_LDS unsigned char* ks = k_lds(cur_tag);
@@ -664,7 +674,18 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   }
 
   // ---- dQ = scale * acc: lane holds query qry, d rows b*32 + (i/4)*8 + half*4 + i%4
-  if (qok) {
+  if (PARTIAL && qok) {
+    float* row = dq_part + (((int64_t)split * BH + bh) * Nq + qry) * D;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = dq_acc[b][r * 4 + e] * scale;
+        *reinterpret_cast<f32x4*>(row + b * 32 + r * 8 + half * 4) = w;
+      }
+  } else if (qok) {
     __bf16* row = dq + qhead + (int64_t)qry * D;
 #pragma unroll
     for (int b = 0; b < DB; ++b)
@@ -676,6 +697,29 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         *reinterpret_cast<bf16x4*>(row + b * 32 + r * 8 + half * 4) = w;
       }
   }
+}
+
+// dQ = sum over the splits of the fp32 partials, in split order (so the
+// result does not depend on which workgroup finished first), as bf16; eight
+// consecutive elements per thread.
+__global__ void __launch_bounds__(256)
+bwd_dq_reduce_kernel(const float* __restrict__ part, __bf16* __restrict__ dq, int64_t n,
+                     int splits) {
+  const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (e0 >= n) return;
+  f32x4 a = {}, b = {};
+  for (int s = 0; s < splits; ++s) {
+    const float* src = part + (int64_t)s * n + e0;
+    a += *reinterpret_cast<const f32x4*>(src);
+    b += *reinterpret_cast<const f32x4*>(src + 4);
+  }
+  bf16x8 w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    w[e] = (__bf16)a[e];
+    w[e + 4] = (__bf16)b[e];
+  }
+  *reinterpret_cast<bf16x8*>(dq + e0) = w;
 }
 
 // ---------------------------------------------------------------- launchers
@@ -700,6 +744,19 @@ hipError_t launch_phase(const BwdArgs& a, int phase) {
     // d = 256 without the mask runs the masked kernel with every key visible
     // (off = Nk): its unmasked instantiation spills registers there
     const int dq_off = a.causal ? off : a.Nk;
+    if (a.dq_splits > 1) {
+      // key chunks: the masked instantiation for either mask (off = Nk shows
+      // every key), then the reduction
+      hipLaunchKernelGGL((bwd_dq_kernel<D, true, true>), dim3((unsigned)((int64_t)BH * nqt * a.dq_splits)),
+                         dim3(kBwdThreads), 0, s, (const __bf16*)a.q, (const __bf16*)a.k,
+                         (const __bf16*)a.v, (const __bf16*)a.dout, a.lse, a.delta, (__bf16*)a.dq,
+                         BH, a.Nq, a.Nk, dq_off, nqt, a.scale, a.scale * kLog2e, a.dq_part,
+                         a.dq_chunk);
+      const int64_t n = (int64_t)BH * a.Nq * D;
+      hipLaunchKernelGGL(bwd_dq_reduce_kernel, dim3((unsigned)((n / 8 + 255) / 256)), dim3(256), 0, s,
+                         (const float*)a.dq_part, (__bf16*)a.dq, n, a.dq_splits);
+      return hipGetLastError();
+    }
     auto kern = bwd_dq_kernel<D, true>;
     if constexpr (D <= 128) {
       if (!a.causal) kern = bwd_dq_kernel<D, false>;
@@ -707,7 +764,7 @@ hipError_t launch_phase(const BwdArgs& a, int phase) {
     hipLaunchKernelGGL(kern, dim3((unsigned)(BH * nqt)), dim3(kBwdThreads), 0, s,
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
                        (const __bf16*)a.dout, a.lse, a.delta, (__bf16*)a.dq, BH, a.Nq, a.Nk,
-                       dq_off, nqt, a.scale, a.scale * kLog2e);
+                       dq_off, nqt, a.scale, a.scale * kLog2e, (float*)nullptr, 0);
   }
   return hipGetLastError();
 }
@@ -723,6 +780,24 @@ hipError_t launch_bwd_phase(const BwdArgs& a, int phase) {
     case 256: return launch_phase<256>(a, phase);
     default: return hipErrorInvalidValue;
   }
+}
+
+BwdDqSplit bwd_dq_split_plan(int B, int H, int Nq, int Nk, int d) {
+  BwdDqSplit sp{1, 0, 0};
+  if (Nq >= Nk) return sp;  // square calls run attn_bwd's kernels unchanged
+  const int64_t base = (int64_t)B * H * ((Nq + kDqBQ - 1) / kDqBQ);
+  const int64_t tiles = (Nk + kDqBK - 1) / kDqBK;
+  // about two workgroups per CU in all, each chunk at least eight key tiles
+  int64_t want = (512 + base - 1) / base;
+  want = std::min<int64_t>(want, std::max<int64_t>(1, tiles / 8));
+  if (want <= 1) return sp;
+  const int64_t per = (tiles + want - 1) / want;
+  sp.splits = (int)((tiles + per - 1) / per);
+  if (sp.splits <= 1) return BwdDqSplit{1, 0, 0};
+  sp.chunk = (int)(per * kDqBK);
+  sp.part_bytes = ((size_t)sp.splits * (size_t)B * H * (size_t)Nq * (size_t)d * sizeof(float) + 255) &
+                  ~(size_t)255;
+  return sp;
 }
 
 hipError_t launch_bwd(const BwdArgs& a) {

@@ -46,7 +46,23 @@ struct BwdArgs {
   int causal;
   float scale;
   void* stream;
+  // dQ split over the keys (bwd_dq_split_plan): dq_splits chunks of dq_chunk
+  // keys, fp32 partials [dq_splits][B*H*Nq][d] in dq_part, summed into dq.
+  float* dq_part = nullptr;
+  int dq_splits = 1;
+  int dq_chunk = 0;
 };
+
+// How the dQ phase cuts the keys: with few queries (Nq < Nk) a head has too
+// few 128-query workgroups to fill the chip, so `splits` workgroups share a
+// query tile, each summing dS K over `chunk` keys (whole 64-key tiles) into
+// an fp32 partial; part_bytes is their workspace, rounded up to 256.
+struct BwdDqSplit {
+  int splits;
+  int chunk;
+  size_t part_bytes;
+};
+BwdDqSplit bwd_dq_split_plan(int B, int H, int Nq, int Nk, int d);
 
 // Nq queries (the last Nq positions) against Nk keys, the keys cut into
 // chunks processed by separate workgroups and merged (attn_fwd_kv).
