@@ -220,6 +220,30 @@ def test_backward_square_equals_attn_bwd(causal, d):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
 
+@pytest.mark.parametrize("Nq,Nk,d", [(130, 2049, 128), (128, 1000, 64), (33, 4097, 256)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_split_dq_deterministic(Nq, Nk, d, causal):
+    """Shapes whose dQ is split over the keys (the workspace holds the fp32
+    partials): two calls give the same bits, and dQ matches the oracle."""
+    from tiled_online_softmax_attn_amd import attn_bwd_kv_workspace_bytes
+    B, H = 1, 2
+    ws = attn_bwd_kv_workspace_bytes(B, H, Nq, Nk, d)
+    assert ws > B * H * Nq * 4 + 256, "this shape is meant to split dQ"
+    q, k, v = make_kv_inputs(B, H, Nq, Nk, d, seed=680 + Nq + d)
+    do = _dout(B, H, Nq, d, 685 + Nq + d)
+    scale = d ** -0.5
+    log(f"[bwd_kv] split dQ Nq={Nq} Nk={Nk} d={d} causal={causal} workspace={ws}")
+    o, lse = gpu_forward_kv(q, k, v, causal, scale, 0)
+    a = gpu_backward_kv(q, k, v, o, lse, do, causal, scale)
+    b = gpu_backward_kv(q, k, v, o, lse, do, causal, scale)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+    ref = oracle.attn_bwd_rect(to_np(q), to_np(k), to_np(v), to_np(do), causal, f32_scale(scale))
+    for h in range(H):
+        e = compare(to_np(a[0][0, h]), ref["dq"][0, h], torch.bfloat16, f"split dq h{h}")
+        log(f"    dq h{h} {describe(e)}")
+
+
 def test_backward_prefill_workload():
     """The prefill workload (B2 H16 Nq512 Nk4096 d128 causal): the sum
     invariants on every head, the oracle on two whole heads."""
