@@ -734,11 +734,21 @@ hipError_t launch_phase(const BwdArgs& a, int phase) {
                        0, s, (const __bf16*)a.o, (const __bf16*)a.dout, a.delta, rows);
   } else if (phase == 1) {
     const int nkb = (a.Nk + kKvBK - 1) / kKvBK * (D / bwd_out_cols(D));
-    auto kern = a.causal ? bwd_dkdv_kernel<D, true> : bwd_dkdv_kernel<D, false>;
+    // d = 32 without the mask runs the masked kernel with every key visible
+    // (off = Nk): its unmasked instantiation spills registers at three waves
+    // per SIMD
+    auto kern = bwd_dkdv_kernel<D, true>;
+    int kv_off = a.causal ? off : a.Nk;
+    if constexpr (D != 32) {
+      if (!a.causal) {
+        kern = bwd_dkdv_kernel<D, false>;
+        kv_off = 0;
+      }
+    }
     hipLaunchKernelGGL(kern, dim3((unsigned)(BH * nkb)), dim3(kBwdThreads), 0, s,
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
                        (const __bf16*)a.dout, a.lse, a.delta, (__bf16*)a.dk, (__bf16*)a.dv, BH,
-                       a.Nq, a.Nk, off, a.scale, a.scale * kLog2e);
+                       a.Nq, a.Nk, kv_off, a.scale, a.scale * kLog2e);
   } else {
     const int nqt = (a.Nq + kDqBQ - 1) / kDqBQ;
     // d = 256 without the mask runs the masked kernel with every key visible
