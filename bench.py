@@ -42,6 +42,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_F32_VALU_TFLOPS = 157.3  # MI355X fp32 vector (packed FMAs; 78.6 without them)
 KERNELS = ("fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq")  # one step, in launch order
 COUNTED_KERNELS = KERNELS + ("softmax_rows",)  # kernels the HBM byte counters cover
 CSRC = os.path.join(ROOT, "tiled_online_softmax_attn_amd", "csrc")
@@ -86,9 +87,11 @@ def algorithmic(w, kernel: str):
     (S, dP, dV, dK), dQ runs three (S, dP, dQ).  The step value uses the
     formula count (2.5x the forward for the whole backward), so the extra
     recompute lowers `value` but not these per-kernel rates."""
+    import torch
     BHN = w.B * w.H * w.N
     if kernel == "fwd":
-        return w.fwd_flops(), "flop", "mfma"
+        # the fp32 forward runs on plain fp32 FMAs (VALU), not the matrix unit
+        return w.fwd_flops(), "flop", "alu" if w.dtype == torch.float32 else "mfma"
     if kernel == "bwd_dkdv":
         return w.fwd_flops() * 4 / 2, "flop", "mfma"
     if kernel == "bwd_dq":
@@ -556,8 +559,9 @@ def bench_softmax(args, w):
         "metric": f"fused row softmax, HBM bytes (one read + one write) per second, {w.name}",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) bf16 scores)",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
+        "data": f"synthetic (seeded N(0,1) {'bf16' if w.dtype == torch.bfloat16 else 'fp32'} scores)",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "step": "attn_softmax_rows"},
         "roofline": roofline, "cpu_baseline": cpu,
     }
@@ -791,7 +795,8 @@ def main():
         avg_ms = per_kernel_ms[kn] / args.steps
         amount, unit, bound = algorithmic(w, kn)
         if unit == "flop":
-            achieved, peak, u = amount / (avg_ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+            achieved, u = amount / (avg_ms * 1e-3) / 1e12, "TFLOP/s"
+            peak = PEAK_F32_VALU_TFLOPS if bound == "alu" else PEAK_BF16_TFLOPS
         else:
             achieved, peak, u = amount / (avg_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
         srt = sorted(samples[kn])
@@ -846,8 +851,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) bf16 Q, K, V, dO)",
+        "dtype": "f32" if w.dtype == torch.float32 else "bf16",
+        "data": (f"synthetic (seeded N(0,1) {'fp32' if w.dtype == torch.float32 else 'bf16'} "
+                 f"Q, K, V{', dO' if backward else ''})"),
         "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
                    "step": "forward + backward" if backward else "forward"},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),

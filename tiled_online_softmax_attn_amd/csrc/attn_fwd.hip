@@ -24,7 +24,7 @@
 //     tile j+1 are in flight while tile j is computed.
 //   * The exponentials run in base 2 with scale*log2(e) folded into one FMA.
 //
-// fp32 path: plain fp32 FMAs (no bf16 rounding anywhere), 2 threads per query.
+// fp32 path: plain fp32 FMAs (no bf16 rounding anywhere), 8 threads per query.
 #include "device_common.h"
 #include "attn_launch.h"
 
@@ -488,8 +488,10 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 // ---------------------------------------------------------------- fp32 path
 constexpr int kF32Threads = 256;
 constexpr int kF32BK = 32;
-// threads per query (each owns d / TPQ dims) and queries per workgroup
-template <int D> constexpr int kF32Tpq = D > 128 ? 4 : 2;
+// threads per query (each owns d / TPQ dims) and queries per workgroup: 8
+// threads per query give the small fp32 shapes (one head of 256 queries) 8
+// workgroups instead of 2, each thread a quarter of the serial work
+template <int D> constexpr int kF32Tpq = 8;
 template <int D> constexpr int kF32BQ = kF32Threads / kF32Tpq<D>;
 
 template <int D, bool CAUSAL>
@@ -504,7 +506,7 @@ attn_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
   __shared__ __attribute__((aligned(16))) float vs[kF32BK * D];
 
   const int tid = threadIdx.x;
-  const int pair_half = tid % TPQ;  // this thread's share of the query's dims
+  const int dpart = tid % TPQ;  // this thread's share of the query's dims
   int bh, qt;
   fwd_tile_coords(blockIdx.x, BH, n_qtiles, CAUSAL, bh, qt);
   const int64_t head = (int64_t)bh * N * D;
@@ -512,7 +514,7 @@ attn_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
   const int q_block_last = min(N, (qt + 1) * BQ) - 1;
 
   float qr[DH], oa[DH];
-  const float* qrow = q + head + (int64_t)(qry < N ? qry : 0) * D + pair_half * DH;
+  const float* qrow = q + head + (int64_t)(qry < N ? qry : 0) * D + dpart * DH;
 #pragma unroll
   for (int c = 0; c < DH; ++c) {
     qr[c] = (qry < N) ? qrow[c] : 0.f;
@@ -541,12 +543,13 @@ attn_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
     float mx = -INFINITY;
 #pragma unroll
     for (int jj = 0; jj < kF32BK; ++jj) {
-      const float* kr = ks + jj * D + pair_half * DH;
+      const float* kr = ks + jj * D + dpart * DH;
       float part = 0.f;
 #pragma unroll
       for (int c = 0; c < DH; ++c) part = fmaf(qr[c], kr[c], part);
-      float dot = part + __shfl_xor(part, 1);
-      if constexpr (TPQ == 4) dot += __shfl_xor(dot, 2);
+      float dot = part;
+#pragma unroll
+      for (int o = 1; o < TPQ; o <<= 1) dot += __shfl_xor(dot, o);
       const int key = key0 + jj;
       if (key >= N || (CAUSAL && key > qry)) dot = -INFINITY;
       s[jj] = dot;
@@ -563,7 +566,7 @@ attn_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
     for (int jj = 0; jj < kF32BK; ++jj) {
       const float p = fast_exp2(fmaf(s[jj], scale_log2, -m_use));
       psum += p;
-      const float* vr = vs + jj * D + pair_half * DH;
+      const float* vr = vs + jj * D + dpart * DH;
 #pragma unroll
       for (int c = 0; c < DH; ++c) oa[c] = fmaf(p, vr[c], oa[c]);
     }
@@ -572,12 +575,12 @@ attn_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
 
   if (qry < N) {
     const float inv = 1.f / l_run;
-    float* orow = o + head + (int64_t)qry * D + pair_half * DH;
+    float* orow = o + head + (int64_t)qry * D + dpart * DH;
 #pragma unroll
     for (int c = 0; c < DH; c += 4)
       *reinterpret_cast<float4*>(orow + c) =
           make_float4(oa[c] * inv, oa[c + 1] * inv, oa[c + 2] * inv, oa[c + 3] * inv);
-    if (pair_half == 0) lse[(int64_t)bh * N + qry] = kLn2 * (m_run + fast_log2(l_run));
+    if (dpart == 0) lse[(int64_t)bh * N + qry] = kLn2 * (m_run + fast_log2(l_run));
   }
 }
 
