@@ -107,6 +107,10 @@ FAKE = 1 << 20  # a 16-byte aligned non-null address, never dereferenced on erro
     # lse needs 4-byte alignment only: this call passes the alignment check and
     # stops at the (later) scale check, so nothing is launched
     (dict(lse=FAKE + 4, scale=0.0), -6),
+    # one workgroup per 32 query rows must fit a 32-bit grid: 2^16 heads of
+    # 2^20 rows need 2^31 workgroups (refused), 2^20 - 32 rows 2^31 - 2^16
+    (dict(H=1 << 16, N=1 << 20), -2),
+    (dict(H=1 << 16, N=(1 << 20) - 32, scale=0.0), -6),
 ])
 def test_fwd_validation(args, code):
     lib = _lib()
@@ -202,6 +206,10 @@ def test_kv_workspace_size():
     (dict(scale=0.0), -6), (dict(scale=-0.0), -6), (dict(scale=-2.0), -6),
     (dict(lse=FAKE + 4, scale=0.0), -6),
     (dict(ws=0), -7), (dict(ws_bytes=8), -7), (dict(ws=FAKE + 8), -5),
+    # the merge's grid (one workgroup per 4 query rows) must fit 32 bits too:
+    # 2^16 heads of 2^17 queries against 64 keys need 2^31 of them
+    (dict(H=1 << 16, Nq=1 << 17, Nk=64, causal=0), -2),
+    (dict(H=1 << 16, Nq=(1 << 17) - 4, Nk=64, causal=0, scale=0.0), -6),
 ])
 def test_kv_validation(args, code):
     lib = _lib()

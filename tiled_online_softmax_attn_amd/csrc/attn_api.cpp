@@ -51,13 +51,14 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 bool scale_ok(float scale) { return isfinite(scale) && scale > 0.f; }
 
 // Shape checks shared by every entry point.  Element counts must fit in
-// int64 offsets and the workgroup count in a 32-bit grid.
+// int64 offsets and the workgroup count in a 32-bit grid: the finest grid is
+// the fp32 forward's and the preprocess's, one workgroup per 32 query rows.
 int check_shape(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
   if (!attn::head_dim_supported(d)) return ATTN_ERR_HEADDIM;
   const int64_t bh = (int64_t)B * (int64_t)H;
   if (bh > (int64_t)1 << 31) return ATTN_ERR_SHAPE;
-  const int64_t tiles = bh * (((int64_t)N + 63) / 64);
+  const int64_t tiles = bh * (((int64_t)N + 31) / 32);
   if (tiles > (int64_t)INT32_MAX) return ATTN_ERR_SHAPE;
   return ATTN_OK;
 }
@@ -194,6 +195,8 @@ static int check_kv_shape(int B, int H, int Nq, int Nk, int d, int causal, int n
   if (rc != ATTN_OK) return rc;
   const int64_t wgs = (int64_t)B * H * (((int64_t)Nq + 127) / 128) * (((int64_t)Nk + 63) / 64);
   if (wgs > (int64_t)INT32_MAX) return ATTN_ERR_SHAPE;
+  // the merge runs one workgroup per 4 query rows
+  if (((int64_t)B * H * Nq + 3) / 4 > (int64_t)INT32_MAX) return ATTN_ERR_SHAPE;
   return ATTN_OK;
 }
 
