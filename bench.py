@@ -14,11 +14,14 @@ that shape; in fp32, where no backward is built, the forward alone.
 With `--workload` naming a key/value-cache shape (attn_inputs.KV_WORKLOADS,
 e.g. decode_b8_h32_nq1_nk8192_d128) a step is instead one attn_fwd_kv call
 (per-chunk partial kernel + merge kernel) and `value` is the K/V bytes read
-per second, the quantity that bounds decode.  With a row-softmax shape
-(attn_inputs.SOFTMAX_WORKLOADS, softmax_m65536_n4096_bf16) a step is one
-attn_softmax_rows call and `value` is the bytes it must move (one read and
-one write of every element) per second.  With the MXFP8 shape
-(attn_inputs.MX_WORKLOADS) a step is one attn_fwd_mx call.
+per second, the quantity that bounds decode; the chunked-prefill training
+shape (prefill_b2_h16_nq512_nk4096_d128_fwdbwd) times attn_fwd_kv plus
+attn_bwd_kv, in TFLOP/s over the visible query-key pairs.  With a
+row-softmax shape (attn_inputs.SOFTMAX_WORKLOADS, softmax_m65536_n4096_bf16)
+a step is one attn_softmax_rows call and `value` is the bytes it must move
+(one read and one write of every element) per second.  With the FP8 shapes
+(attn_inputs.MX_WORKLOADS) a step is one attn_fwd_mx (`..._mxfp8`) or
+attn_fwd_fp8 (`..._fp8`) call.
 
 Prints ONE JSON line.  `value` is fwd+bwd TFLOP/s by the formula
 4*B*H*N^2*d (halved for causal) for the forward plus 2.5x that for the
