@@ -28,8 +28,11 @@
  *   and > 0, otherwise ATTN_ERR_SCALE (0, -0.0 and negative values included).
  *   Results are finite as long as scale * |q_i . k_j| fits fp32.
  * - N may be any value >= 1 (no tile multiple is required); d must be 32, 64,
- *   96, 128 or 256, in every entry point but attn_fwd_mx.  bf16 is supported by
- *   every entry point; fp32 by the forward only.
+ *   96, 128 or 256 (64 or 128 in the FP8 forwards attn_fwd_mx and
+ *   attn_fwd_fp8).  bf16 is supported by every entry point; fp32 by the
+ *   forward only.  B * H * ceil(N / 32) must not exceed 2^31 - 1 (the finest
+ *   grid launched has one workgroup per 32 query rows); ATTN_ERR_SHAPE
+ *   otherwise.
  * - The caller owns every buffer (including the backward workspace).  The
  *   library never allocates, frees or synchronises; it enqueues kernels on
  *   `stream` (a hipStream_t, NULL = the default stream) and returns.  Results
@@ -39,7 +42,8 @@
  *   non-zero return nothing was written.  Outputs must not alias inputs.
  * - Tensor pointers must be 16-byte aligned (the kernels use 128-bit
  *   accesses); lse, read and written one float at a time, 4-byte aligned.
- * - Calls are thread-safe: the library keeps no per-call global state.
+ * - Calls are thread-safe: the library keeps no per-call global state (the
+ *   device array of attn_bwd_noalloc aside, see there).
  */
 #ifndef ATTN_H_
 #define ATTN_H_
