@@ -72,6 +72,17 @@ def test_ragged_forward(N, d, causal, dtype):
     _fwd_full_check(q, k, v, causal, d ** -0.5, dtype, f"ragged N={N} d={d}")
 
 
+@pytest.mark.parametrize("N", [31, 32, 33, 63, 65, 129])
+@pytest.mark.parametrize("d", [32, 96, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_f32_forward_at_workgroup_edges(N, d, causal):
+    """The fp32 forward gives each workgroup 32 queries (8 threads per query):
+    lengths on either side of one, two and four workgroups, against the fp32
+    tolerance."""
+    q, k, v = make_inputs(1, 3, N, d, torch.float32, seed=300 + N + d)
+    _fwd_full_check(q, k, v, causal, d ** -0.5, torch.float32, f"fp32 edge N={N} d={d}")
+
+
 @pytest.mark.parametrize("N", [1, 17, 100, 257, 1000])
 @pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
