@@ -704,7 +704,7 @@ def main():
         sys.exit(cpu_baseline_all(args.cpu_baseline_seconds))
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        eprint("bench.py: this build runs on exactly one GPU; multi-GPU runs are not "
+        eprint("bench.py: the library runs on exactly one GPU; multi-GPU runs are not "
                "supported (heads would shard across GPUs with no exchange).")
         sys.exit(2)
 
