@@ -20,8 +20,12 @@
 //     accumulator (bf16-rounded), and V^T comes from row-major V in LDS via
 //     ds_read_b64_tr_b16.  The O^T accumulator keeps one query per lane, so
 //     the e^{m - m'} rescale and the final 1/l are per-lane scalars.
-//   * K and V tiles (64 keys) are double-buffered in LDS; the global loads of
-//     tile j+1 are in flight while tile j is computed.
+//   * K and V tiles (64 keys) are double-buffered in LDS; the copies of the
+//     next tiles are in flight while tile j is computed (at d = 96, 128 and
+//     256, where S^T of tile j+1 is computed during the softmax of tile j, K
+//     runs one tile ahead of V).
+//   * The row sum runs on the matrix unit at d <= 64 (an all-ones operand
+//     against P^T), on the VALU above.
 //   * The exponentials run in base 2 with scale*log2(e) folded into one FMA.
 //
 // fp32 path: plain fp32 FMAs (no bf16 rounding anywhere), 8 threads per query.
