@@ -146,7 +146,9 @@ int attn_bwd_phase(int phase, const void* q, const void* k, const void* v, const
 /* Bytes of device workspace attn_fwd_kv needs for these sizes and this
  * num_splits (0 = the library's choice, the same one attn_fwd_kv makes): fp32
  * partial O and lse of every key chunk, each part rounded up to a multiple of
- * 256.  Returns 0 for invalid sizes or an unsupported dtype. */
+ * 256, when the keys are cut into two or more chunks.  Returns 0 when they
+ * are not (one chunk needs no workspace), and 0 for invalid sizes or an
+ * unsupported dtype, which attn_fwd_kv reports with its own error code. */
 size_t attn_fwd_kv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits,
                                    int dtype);
 
@@ -165,10 +167,13 @@ size_t attn_fwd_kv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_
  *                ceil(Nk / 64) are capped.  It changes rounding only.
  *   workspace  : device scratch of at least attn_fwd_kv_workspace_bytes()
  *                bytes with the same num_splits, caller-owned; contents on
- *                entry are ignored.
+ *                entry are ignored.  When that size is 0 (one chunk) the
+ *                workspace and workspace_bytes are not read (NULL is fine).
  *   dtype      : ATTN_DTYPE_BF16 only (ATTN_ERR_DTYPE otherwise).
- * Nq = Nk computes what attn_fwd computes, by a different kernel.  Calls that
- * share a workspace must not overlap in time.  Returns ATTN_OK or an error:
+ * With one chunk the forward kernel of attn_fwd walks all keys and writes o
+ * and lse itself (no merge); Nq = Nk then gives attn_fwd's results bit for
+ * bit.  Calls that share a workspace must not overlap in time.  Returns
+ * ATTN_OK or an error:
  * those of attn_fwd, plus ATTN_ERR_SHAPE for Nq or Nk < 1, Nk < Nq with
  * causal, or num_splits < 0, and ATTN_ERR_WORKSPACE. */
 int attn_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -262,10 +267,11 @@ int attn_softmax_rows(const void* x, void* y, long long M, int N, int dtype, voi
 /* Static, human-readable text for a return code (never NULL). */
 const char* attn_status_str(int status);
 
-/* Library ABI version; bumped when an entry point is added or a signature
- * changes (2: attn_fwd_kv and attn_fwd_kv_workspace_bytes; 3: attn_softmax_rows,
- * and head dimensions 32, 96 and 256; 4: attn_fwd_mx; 5: attn_bwd_noalloc; 6: attn_bwd_kv and
- * attn_bwd_kv_workspace_bytes; 7: attn_fwd_fp8). */
+/* Library ABI version; bumped when an entry point is added or a signature or
+ * a calling contract changes (2: attn_fwd_kv and attn_fwd_kv_workspace_bytes;
+ * 3: attn_softmax_rows, and head dimensions 32, 96 and 256; 4: attn_fwd_mx;
+ * 5: attn_bwd_noalloc; 6: attn_bwd_kv and attn_bwd_kv_workspace_bytes;
+ * 7: attn_fwd_fp8; 8: attn_fwd_kv with one key chunk needs no workspace). */
 int attn_abi_version(void);
 
 #ifdef __cplusplus

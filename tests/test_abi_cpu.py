@@ -71,7 +71,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = _lib()
-    assert lib.attn_abi_version() == 7
+    assert lib.attn_abi_version() == 8
     for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, 12345]:
         s = lib.attn_status_str(code)
         assert isinstance(s, bytes) and len(s) > 0
@@ -175,22 +175,26 @@ def test_bwd_phase_validation():
 
 def test_kv_workspace_size():
     """Partial O (d floats) and lse (one float) per split, head and query,
-    each part rounded up to 256 bytes; the automatic split count depends
-    only on the shape."""
+    each part rounded up to 256 bytes, when there are two or more chunks;
+    none for one chunk.  The automatic split count depends only on the
+    shape: about 512 workgroups in all, at least four key tiles a chunk."""
     lib = _lib()
-    for B, H, Nq, Nk, d, splits in ((1, 1, 1, 100, 64, 1), (2, 3, 7, 1000, 128, 5),
-                                    (8, 32, 1, 8192, 128, 0), (1, 2, 300, 300, 64, 0)):
+    r256 = lambda x: (x + 255) // 256 * 256
+    for B, H, Nq, Nk, d, splits in ((1, 1, 1, 100, 64, 1), (1, 1, 1, 100, 64, 2),
+                                    (2, 3, 7, 1000, 128, 5), (1, 1, 5, 64, 32, 9)):
         n = lib.attn_fwd_kv_workspace_bytes(B, H, Nq, Nk, d, splits, 1)
         tiles = (Nk + 63) // 64
-        if splits == 0:
-            assert n == lib.attn_fwd_kv_workspace_bytes(B, H, Nq, Nk, d, 0, 1)
-            assert n > 0
-            continue
         per = -(-tiles // min(splits, tiles))
         eff = -(-tiles // per)
         rows = eff * B * H * Nq
-        r256 = lambda x: (x + 255) // 256 * 256
-        assert n == r256(rows * d * 4) + r256(rows * 4)
+        assert n == (r256(rows * d * 4) + r256(rows * 4) if eff > 1 else 0), (Nk, splits)
+    # automatic plans: decode B8 H32 against 8192 keys (256 query tiles) takes
+    # 2 chunks; 300 keys (5 tiles) or 1024 query tiles (B2 H16 N4096) take one
+    for B, H, Nq, Nk, d, eff in ((8, 32, 1, 8192, 128, 2), (1, 2, 300, 300, 64, 1),
+                                 (2, 16, 4096, 4096, 64, 1), (1, 1, 1, 8192, 128, 32)):
+        n = lib.attn_fwd_kv_workspace_bytes(B, H, Nq, Nk, d, 0, 1)
+        rows = eff * B * H * Nq
+        assert n == (r256(rows * d * 4) + r256(rows * 4) if eff > 1 else 0), (B, H, Nq, Nk)
     assert lib.attn_fwd_kv_workspace_bytes(1, 1, 0, 10, 64, 0, 1) == 0
     assert lib.attn_fwd_kv_workspace_bytes(1, 1, 4, 10, 80, 0, 1) == 0
     assert lib.attn_fwd_kv_workspace_bytes(1, 1, 4, 10, 64, -1, 1) == 0
@@ -205,7 +209,8 @@ def test_kv_workspace_size():
     (dict(k=FAKE + 4), -5), (dict(lse=FAKE + 1), -5), (dict(scale=float("nan")), -6),
     (dict(scale=0.0), -6), (dict(scale=-0.0), -6), (dict(scale=-2.0), -6),
     (dict(lse=FAKE + 4, scale=0.0), -6),
-    (dict(ws=0), -7), (dict(ws_bytes=8), -7), (dict(ws=FAKE + 8), -5),
+    (dict(ws=0, splits=2), -7), (dict(ws_bytes=8, splits=2), -7),
+    (dict(ws=FAKE + 8, splits=2), -5),
     # the merge's grid (one workgroup per 4 query rows) must fit 32 bits too:
     # 2^16 heads of 2^17 queries against 64 keys need 2^31 of them
     (dict(H=1 << 16, Nq=1 << 17, Nk=64, causal=0), -2),

@@ -6,7 +6,9 @@ Coverage: decode (Nq = 1) and chunked prefill shapes, key counts that are not
 tile multiples, Nq = Nk, Nq > 128 (several query tiles), both masks,
 d = 32, 64, 96, 128 and 256, scales 1.0 and 0.02 besides 1/sqrt(d), automatic and explicit split counts (including more splits than
 tiles, which the library caps), the decode workload at full size, agreement
-with attn_fwd when Nq = Nk, a 131077-key cache, and bitwise determinism.
+with attn_fwd when Nq = Nk (bit for bit with one key chunk, which runs
+attn_fwd's kernel with no workspace), a 131077-key cache, and bitwise
+determinism.
 
 attn_bwd_kv (the backward of attn_fwd_kv) against oracle_attn_bwd_rect: the
 same (Nq, Nk) shapes and more, d = 32 ... 256, both masks, scales 1.0 and 0.02, Nq > Nk without
@@ -87,14 +89,46 @@ def test_split_count_changes_rounding_only():
     assert float((l1 - l9).abs().max()) < 1e-4
 
 
-def test_square_matches_attn_fwd():
-    """Nq = Nk: the same attention as attn_fwd, by a different kernel."""
-    q, k, v = make_kv_inputs(1, 4, 257, 257, 128, seed=402)
+@pytest.mark.parametrize("d", [64, 128])
+def test_square_matches_attn_fwd(d):
+    """Nq = Nk: the same attention as attn_fwd.  One chunk (the automatic
+    plan here: 5 key tiles) runs attn_fwd's kernel, bit for bit; three
+    chunks run the partial-result kernel and the merge."""
+    q, k, v = make_kv_inputs(1, 4, 257, 257, d, seed=402)
     for causal in (False, True):
-        o_kv, l_kv = _check(q, k, v, causal, 0, f"square causal={causal}")
-        o_f, l_f = gpu_forward(q, k, v, causal, 128 ** -0.5)
-        assert float((o_kv.float() - o_f.float()).abs().max()) < 2e-2
-        assert float((l_kv - l_f).abs().max()) < 1e-3
+        o_f, l_f = gpu_forward(q, k, v, causal, d ** -0.5)
+        o1, l1 = _check(q, k, v, causal, 0, f"square d={d} causal={causal} one chunk")
+        assert torch.equal(o1, o_f) and torch.equal(l1, l_f)
+        o3, l3 = _check(q, k, v, causal, 3, f"square d={d} causal={causal} 3 chunks")
+        assert float((o3.float() - o_f.float()).abs().max()) < 2e-2
+        assert float((l3 - l_f).abs().max()) < 1e-3
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_one_chunk_plan_without_workspace(causal):
+    """B2 H16 N4096 d64 has 1024 query tiles, so the automatic plan is one
+    chunk: no workspace (None is passed), no merge, and attn_fwd's results
+    bit for bit; heads 0 and last also against the oracle."""
+    import tiled_online_softmax_attn_amd as T
+    B, H, N, d = 2, 16, 4096, 64
+    assert T.attn_fwd_kv_workspace_bytes(B, H, N, N, d, 0) == 0
+    q, k, v = make_kv_inputs(B, H, N, N, d, seed=404)
+    log(f"[kv] one-chunk plan B{B} H{H} N{N} d{d} causal={causal}, no workspace")
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.full_like(qd, float("nan"))
+    lse = torch.full((B, H, N), float("nan"), device=dev, dtype=torch.float32)
+    T.attn_fwd_kv(qd, kd, vd, o, lse, causal, d ** -0.5, 0, None)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    o_f, l_f = gpu_forward(q, k, v, causal, d ** -0.5)
+    assert torch.equal(o, o_f) and torch.equal(lse, l_f)
+    for b, h in [(0, 0), (B - 1, H - 1)]:
+        o_ref, lse_ref = oracle.attn_fwd_rect(q[b, h].double().numpy(), k[b, h].double().numpy(),
+                                              v[b, h].double().numpy(), causal,
+                                              f32_scale(d ** -0.5))
+        compare(to_np(o[b, h]), o_ref, torch.bfloat16, f"one chunk O[{b},{h}]")
+        compare(to_np(lse[b, h]), lse_ref, torch.bfloat16, f"one chunk lse[{b},{h}]")
 
 
 def test_decode_workload_full():

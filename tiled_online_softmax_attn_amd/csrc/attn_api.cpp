@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 7;
+constexpr int kAbiVersion = 8;
 
 // Device scratch of attn_bwd_noalloc: the D vector (one fp32 per query row)
 // that attn_bwd keeps in the caller's workspace.  16 MiB per GPU, so
@@ -221,8 +221,10 @@ int attn_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse
   if (!aligned4(lse)) return ATTN_ERR_ALIGN;
   if (!scale_ok(scale)) return ATTN_ERR_SCALE;
   const size_t need = attn_fwd_kv_workspace_bytes(B, H, Nq, Nk, d, num_splits, dtype);
-  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+  if (need > 0) {  // one chunk needs none and ignores the workspace arguments
+    if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+  }
   attn::FwdKvArgs a{q, k, v, o, lse, B, H, Nq, Nk, d, causal != 0, scale, num_splits,
                     workspace, stream};
   return attn::launch_fwd_kv(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;

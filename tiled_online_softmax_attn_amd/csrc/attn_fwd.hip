@@ -87,7 +87,8 @@ static_assert(pv_start(8, 4) == 2 && pv_start(16, 8) == 4 && pv_start(6, 3) == 2
 // writes that chunk's partial result for the merge: O_c normalised by the
 // chunk's own sum (fp32, [split][bh][Nq][D]) and lse_c over the chunk's keys
 // ([split][bh][Nq], natural log, -inf with O_c = 0 where no key of the chunk
-// is visible).  Without PARTIAL: Nq = Nk = N, one chunk, bf16 O and lse.
+// is visible).  Without PARTIAL: all Nk keys in one pass, bf16 O and lse
+// (attn_fwd: Nq = Nk = N).
 template <int D, bool PARTIAL>
 __global__ void __launch_bounds__(kFwdThreads, D > 128 ? 1 : 2)
 attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
@@ -588,15 +589,28 @@ attn_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
   }
 }
 
+// All Nk keys in one pass per query tile: bf16 O and lse written directly.
+template <int D>
+hipError_t launch_whole(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int BH, int Nq, int Nk, int off, float scale, void* stream) {
+  const int n_qtiles = (Nq + kFwdBQ - 1) / kFwdBQ;
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false>), dim3((unsigned)(BH * n_qtiles)),
+                     dim3(kFwdThreads), 0, (hipStream_t)stream, (const __bf16*)q,
+                     (const __bf16*)k, (const __bf16*)v, o, lse, BH, Nq, Nk, n_qtiles, off, 0,
+                     scale * kLog2e);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_bf16(const FwdArgs& a) {
-  const int n_qtiles = (a.N + kFwdBQ - 1) / kFwdBQ;
-  const int BH = a.B * a.H;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false>), dim3((unsigned)(BH * n_qtiles)),
-                     dim3(kFwdThreads), 0, (hipStream_t)a.stream, (const __bf16*)a.q,
-                     (const __bf16*)a.k, (const __bf16*)a.v, a.o, a.lse, BH, a.N, a.N,
-                     n_qtiles, a.causal ? 0 : a.N, 0, a.scale * kLog2e);
-  return hipGetLastError();
+  return launch_whole<D>(a.q, a.k, a.v, a.o, a.lse, a.B * a.H, a.N, a.N, a.causal ? 0 : a.N,
+                         a.scale, a.stream);
+}
+
+template <int D>
+hipError_t launch_kv_whole(const FwdKvArgs& a) {
+  return launch_whole<D>(a.q, a.k, a.v, a.o, a.lse, a.B * a.H, a.Nq, a.Nk,
+                         a.causal ? a.Nk - a.Nq : a.Nk, a.scale, a.stream);
 }
 
 template <int D>
@@ -640,6 +654,17 @@ hipError_t launch_fwd_kv_partial(const FwdKvArgs& a, const KvSplit& sp, float* o
     case 96: return launch_partial<96>(a, sp, o_part, lse_part);
     case 128: return launch_partial<128>(a, sp, o_part, lse_part);
     case 256: return launch_partial<256>(a, sp, o_part, lse_part);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_fwd_kv_whole(const FwdKvArgs& a) {
+  switch (a.d) {
+    case 32: return launch_kv_whole<32>(a);
+    case 64: return launch_kv_whole<64>(a);
+    case 96: return launch_kv_whole<96>(a);
+    case 128: return launch_kv_whole<128>(a);
+    case 256: return launch_kv_whole<256>(a);
     default: return hipErrorInvalidValue;
   }
 }

@@ -16,7 +16,8 @@
 // partial-result instantiation: section 8.3 of the CS336 notes, S^T = K Q^T
 // on MFMA with the lane owning one query, a lazily moved reference maximum,
 // base-2 exponentials and O^T += V^T P^T); this file holds the split plan and
-// the merge.
+// the merge.  A plan of one chunk (many query tiles already fill the chip)
+// skips both: the forward kernel walks all keys and writes O and lse.
 #include "device_common.h"
 #include "attn_launch.h"
 
@@ -66,6 +67,9 @@ attn_fwd_kv_merge_kernel(const float* __restrict__ o_part, const float* __restri
 
 template <int D>
 hipError_t launch_kv(const FwdKvArgs& a, const KvSplit& sp) {
+  // one chunk: partials and a merge would only copy O through fp32 (B2 H16
+  // N4096 d64, 1024 query tiles: 199 us that way, 179 direct; causal 120, 98)
+  if (sp.splits == 1) return launch_fwd_kv_whole(a);
   const int BH = a.B * a.H;
   const hipStream_t s = (hipStream_t)a.stream;
   float* o_part = (float*)a.workspace;
@@ -101,6 +105,7 @@ KvSplit kv_split_plan(int B, int H, int Nq, int Nk, int d, int num_splits) {
   const int64_t tiles_per_chunk = (tiles + want - 1) / want;
   sp.chunk = (int)(tiles_per_chunk * kKvBK);
   sp.splits = (int)((tiles + tiles_per_chunk - 1) / tiles_per_chunk);
+  if (sp.splits == 1) return sp;  // the forward kernel writes O and lse itself
   const size_t rows = (size_t)sp.splits * (size_t)BH * (size_t)Nq;
   sp.o_part_bytes = (rows * (size_t)d * sizeof(float) + 255) & ~(size_t)255;
   sp.lse_part_bytes = (rows * sizeof(float) + 255) & ~(size_t)255;

@@ -76,18 +76,18 @@ struct FwdKvArgs {
   int causal;
   float scale;
   int num_splits;   // 0 = chosen from the shape
-  void* workspace;  // kv_split_plan(...).o_part_bytes + lse_part_bytes
+  void* workspace;  // kv_split_plan(...).o_part_bytes + lse_part_bytes (0 for one chunk)
   void* stream;
 };
 
 // How attn_fwd_kv cuts the keys: `splits` chunks of `chunk` keys (a multiple
 // of the 64-key tile; the last chunk may be shorter), and the workspace it
-// needs for the partial results.
+// needs for the partial results (none with one chunk).
 struct KvSplit {
   int splits;
   int chunk;
-  size_t o_part_bytes;    // fp32 [splits][B*H][Nq][d], rounded up to 256
-  size_t lse_part_bytes;  // fp32 [splits][B*H][Nq], rounded up to 256
+  size_t o_part_bytes;    // fp32 [splits][B*H][Nq][d], rounded up to 256; 0 if splits == 1
+  size_t lse_part_bytes;  // fp32 [splits][B*H][Nq], rounded up to 256; 0 if splits == 1
 };
 KvSplit kv_split_plan(int B, int H, int Nq, int Nk, int d, int num_splits);
 // The forward kernel of attn_fwd over chunk `split` of the keys, for every
@@ -95,6 +95,9 @@ KvSplit kv_split_plan(int B, int H, int Nq, int Nk, int d, int num_splits);
 // normalised by the chunk's own sum) and lse_c into o_part / lse_part.
 hipError_t launch_fwd_kv_partial(const FwdKvArgs& a, const KvSplit& sp, float* o_part,
                                  float* lse_part);
+// One chunk: the same kernel over all Nk keys (B*H*ceil(Nq/128) workgroups)
+// writes bf16 O and lse itself; no partial results, no merge.
+hipError_t launch_fwd_kv_whole(const FwdKvArgs& a);
 
 // Forward with Q and K in MXFP8 (E4M3 codes, one E8M0 scale per 32 elements
 // along d) and V in bf16 (attn_fwd_mx).
