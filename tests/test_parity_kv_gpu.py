@@ -3,7 +3,8 @@ range split over workgroups and merged) against the fp64 oracle's
 oracle_attn_fwd_rect on the same seeded inputs.
 
 Coverage: decode (Nq = 1) and chunked prefill shapes, key counts that are not
-tile multiples, Nq = Nk, Nq > 128 (several query tiles), both masks,
+tile multiples, Nq = Nk, Nq > 128 (several query tiles), Nq > Nk without the
+mask (one chunk and two), both masks,
 d = 32, 64, 96, 128 and 256, scales 1.0 and 0.02 besides 1/sqrt(d), automatic and explicit split counts (including more splits than
 tiles, which the library caps), the decode workload at full size, agreement
 with attn_fwd when Nq = Nk (bit for bit with one key chunk, which runs
@@ -62,6 +63,17 @@ def test_decode_shapes(Nk, d, causal):
 def test_prefill_shapes(Nq, Nk, d, causal):
     q, k, v = make_kv_inputs(1, 2, Nq, Nk, d, seed=200 + Nq + Nk + d)
     _check(q, k, v, causal, 0, f"prefill Nq={Nq} Nk={Nk} d={d}")
+
+
+@pytest.mark.parametrize("Nq,Nk", [(300, 100), (129, 64), (1000, 129)])
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
+@pytest.mark.parametrize("splits", [0, 2])
+def test_more_queries_than_keys(Nq, Nk, d, splits):
+    """Without the mask Nq may exceed Nk: every query sees all keys.  The
+    automatic plan is one chunk here (the forward kernel alone); two chunks
+    take the partial results and the merge (capped at one for Nk = 64)."""
+    q, k, v = make_kv_inputs(1, 2, Nq, Nk, d, seed=270 + Nq + Nk + d)
+    _check(q, k, v, False, splits, f"Nq={Nq} > Nk={Nk} d={d}")
 
 
 @pytest.mark.parametrize("scale", [1.0, 0.02])
