@@ -50,7 +50,7 @@ KERNELS = ("fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq")  # one step, in launch
 COUNTED_KERNELS = KERNELS + ("softmax_rows",)  # kernels the HBM byte counters cover
 CSRC = os.path.join(ROOT, "tiled_online_softmax_attn_amd", "csrc")
 KERNEL_SOURCES = {"fwd": "attn_fwd.hip", "bwd_preprocess": "attn_bwd.hip",
-                  "bwd_dkdv": "attn_bwd.hip", "bwd_dq": "attn_bwd.hip",
+                  "bwd_dkdv": "attn_bwd_dkdv.hip", "bwd_dq": "attn_bwd.hip",
                   "softmax_rows": "softmax_rows.hip"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 PROBE_LIB = os.path.join(ROOT, "tiled_online_softmax_attn_amd", "libattn_probe.so")
@@ -61,10 +61,15 @@ def eprint(*a):
 
 
 def source_digest(kernel: str) -> str:
+    """Digest of what a kernel's machine code is built from: its source, the
+    shared device header and the compiler flags of that source."""
+    from tiled_online_softmax_attn_amd import build as hip_build
     h = hashlib.sha256()
     for name in (KERNEL_SOURCES[kernel], "device_common.h"):
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
+    flags = hip_build.FLAGS + hip_build.source_flags(KERNEL_SOURCES[kernel])
+    h.update(" ".join(f for f in flags if not f.startswith("-I")).encode())  # paths vary
     return h.hexdigest()[:16]
 
 

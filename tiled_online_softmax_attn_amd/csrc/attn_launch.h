@@ -137,6 +137,8 @@ hipError_t launch_fwd_kv(const FwdKvArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
 // phase 0 = preprocess (D), 1 = dK and dV, 2 = dQ
 hipError_t launch_bwd_phase(const BwdArgs& a, int phase);
+// phase 1 alone (dK and dV; attn_bwd_dkdv.hip)
+hipError_t launch_bwd_dkdv(const BwdArgs& a);
 
 // Workspace of the backward: the D vector (one fp32 per query row), rounded
 // up to 256 bytes.
