@@ -2,9 +2,9 @@
 """Throughput of the fused attention hot path on one MI355X.
 
 One step = one pass of the whole path over one batch of synthetic input:
-the forward (attn_fwd: O and lse) and the backward (attn_bwd's three phases:
-preprocess D, dK/dV, dQ) on the causal B=4 H=16 N=4096 d=128 bf16
-workload.  Inputs are generated on the host from a fixed seed, copied to the
+the forward (attn_fwd: O and lse) and the backward (attn_bwd's two launches:
+dQ, which also forms D = rowsum(dO * O), then dK/dV) on the causal B=4 H=16
+N=4096 d=128 bf16 workload.  Inputs are generated on the host from a fixed seed, copied to the
 GPU, and resident in HBM before the timed region starts.
 
 With `--workload` naming another attention shape (attn_inputs.WORKLOADS or
@@ -46,8 +46,9 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_F32_VALU_TFLOPS = 157.3  # MI355X fp32 vector (packed FMAs; 78.6 without them)
-KERNELS = ("fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq")  # one step, in launch order
-COUNTED_KERNELS = KERNELS + ("softmax_rows",)  # kernels the HBM byte counters cover
+KERNELS = ("fwd", "bwd_dq", "bwd_dkdv")  # one step, in launch order
+BWD_PHASES = (3, 1)  # attn_bwd_phase numbers of the backward kernels above
+COUNTED_KERNELS = KERNELS + ("bwd_preprocess", "softmax_rows",)  # kernels the HBM byte counters cover
 CSRC = os.path.join(ROOT, "tiled_online_softmax_attn_amd", "csrc")
 KERNEL_SOURCES = {"fwd": "attn_fwd.hip", "bwd_preprocess": "attn_bwd.hip",
                   "bwd_dkdv": "attn_bwd_dkdv.hip", "bwd_dq": "attn_bwd.hip",
@@ -763,11 +764,11 @@ def main():
             events[1].record(stream)
         if not backward:
             return
-        for ph in range(3):
+        for i, ph in enumerate(BWD_PHASES):
             T.attn_bwd_phase(ph, qd, kd, vd, o, dod, lse, dq, dk, dv, ws, w.causal, w.scale,
                              stream)
             if events is not None:
-                events[2 + ph].record(stream)
+                events[2 + i].record(stream)
 
     copy_reference(args.copy_mib)
 

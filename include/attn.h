@@ -127,17 +127,21 @@ int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
                      int B, int H, int N, int d, int causal, float scale, int dtype,
                      void* stream);
 
-/* One phase of attn_bwd, for callers that schedule or time the phases
- * separately.  attn_bwd(...) is exactly phases 0, 1, 2 in this order on one
- * stream, with the same arguments:
+/* One phase of the backward, for callers that schedule or time the phases
+ * separately.  attn_bwd(...) is exactly phase 3 then phase 1 on one stream,
+ * with the same arguments:
  *   0  preprocess: D = rowsum(dO * O) into the workspace (CS336 L5 notes
  *      section 8.4 and Exercise 9)
  *   1  dK and dV: key blocks outside, query blocks inside; writes dk, dv
  *   2  dQ: query blocks outside, key blocks inside; writes dq
- * Phases 1 and 2 only read what phase 0 wrote, not each other's output.
+ *   3  phases 0 and 2 in one launch: the dQ kernel forms each query's D from
+ *      its own dO and O rows, writes it to the workspace and writes dq
+ * Phases 1 and 2 read D from the workspace, as phase 0 or 3 left it, not
+ * each other's output.  0, 1, 2 in order give the results of attn_bwd within
+ * the fp32 rounding of D (phase 0 sums its terms in another order).
  * A phase reads what the earlier phases left in the workspace; running them
  * out of order gives undefined results (no fault).  Errors as attn_bwd, plus
- * ATTN_ERR_SHAPE for a phase outside 0..2. */
+ * ATTN_ERR_SHAPE for a phase outside 0..3. */
 int attn_bwd_phase(int phase, const void* q, const void* k, const void* v, const void* o,
                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
                    void* workspace, size_t workspace_bytes, int B, int H, int N, int d,

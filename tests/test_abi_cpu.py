@@ -166,7 +166,7 @@ def test_bwd_noalloc_validation(args, code):
 def test_bwd_phase_validation():
     lib = _lib()
     args = [FAKE] * 10 + [1 << 30, 1, 1, 16, 64, 1, 0.125, 1, None]
-    assert lib.attn_bwd_phase(3, *args) == -2
+    assert lib.attn_bwd_phase(4, *args) == -2
     assert lib.attn_bwd_phase(-1, *args) == -2
     bad = list(args)
     bad[9] = None  # workspace

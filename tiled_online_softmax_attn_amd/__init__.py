@@ -214,8 +214,9 @@ def attn_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, causal: bool, scale: flo
 
 def attn_bwd_phase(phase: int, q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool,
                    scale: float, stream=None) -> None:
-    """Enqueue one phase of attn_bwd (0: D = rowsum(dO * O) into the
-    workspace; 1: dK and dV; 2: dQ)."""
+    """Enqueue one phase of the backward (0: D = rowsum(dO * O) into the
+    workspace; 1: dK and dV; 2: dQ; 3: dQ forming D itself, i.e. 0 and 2 in
+    one launch).  attn_bwd runs phase 3, then phase 1."""
     _check_contig(q, k, v, o, dout, lse, dq, dk, dv)
     B, H, N, d = _shape(q)
     _check_bwd(f"attn_bwd_phase({phase})", q, k, v, o, dout, lse, dq, dk, dv, workspace)

@@ -125,7 +125,7 @@ static int bwd_check(int phase, const void* q, const void* k, const void* v, con
   int rc = check_shape(B, H, N, d);
   if (rc != ATTN_OK) return rc;
   if (!attn::bwd_head_dim_supported(d)) return ATTN_ERR_HEADDIM;
-  if (phase < -1 || phase > 2) return ATTN_ERR_SHAPE;
+  if (phase < -1 || phase > 3) return ATTN_ERR_SHAPE;
   if (dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
   const void* ptrs[] = {q, k, v, o, dout, dq, dk, dv};
   for (const void* p : ptrs)
@@ -168,8 +168,8 @@ int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
   void* ws = nullptr;
   rc = noalloc_scratch(&ws);
   if (rc != ATTN_OK) return rc;
-  // the same three kernels as attn_bwd; phase 0 writes every D entry that
-  // phases 1 and 2 read, so nothing in the scratch needs clearing
+  // the same kernels as attn_bwd; the dQ kernel writes every D entry that
+  // the dK/dV kernel reads, so nothing in the scratch needs clearing
   attn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, (float*)ws, B, H, N, N, d, causal != 0,
                   scale, stream};
   return attn::launch_bwd(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
@@ -179,7 +179,7 @@ int attn_bwd_phase(int phase, const void* q, const void* k, const void* v, const
                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
                    void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
                    int causal, float scale, int dtype, void* stream) {
-  if (phase < 0 || phase > 2) return ATTN_ERR_SHAPE;
+  if (phase < 0 || phase > 3) return ATTN_ERR_SHAPE;
   return bwd_common(phase, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H,
                     N, d, causal, scale, dtype, stream);
 }

@@ -81,13 +81,17 @@ constexpr int kDqBK = 64;   // keys per K/V tile (one SwzTile)
 // PARTIAL: workgroup (split, query tile, head) sums dS K over key chunk
 // `split` only (chunk keys, a multiple of the tile) and writes scale * that
 // sum in fp32 to dq_part[split][bh][Nq][D] for bwd_dq_reduce_kernel.
-template <int D, bool CAUSAL, bool PARTIAL = false>
+// FORM_D: D = rowsum(dO * O) is formed here instead of read from the
+// preprocess kernel's output, and written to `delta` for the dK/dV kernel,
+// which then runs after this one (phase 3: phases 0 and 2 in one launch).
+template <int D, bool CAUSAL, bool PARTIAL = false, bool FORM_D = false>
 __global__ void __launch_bounds__(kBwdThreads, D > 128 ? 1 : 2)
 bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
               const __bf16* __restrict__ v, const __bf16* __restrict__ dout,
-              const float* __restrict__ lse, const float* __restrict__ delta,
-              __bf16* __restrict__ dq, int BH, int Nq, int Nk, int off, int n_qtiles,
-              float scale, float scale_log2, float* __restrict__ dq_part, int chunk) {
+              const __bf16* __restrict__ o, const float* __restrict__ lse,
+              float* __restrict__ delta, __bf16* __restrict__ dq, int BH, int Nq, int Nk, int off,
+              int n_qtiles, float scale, float scale_log2, float* __restrict__ dq_part, int chunk) {
+  static_assert(!(PARTIAL && FORM_D), "a key chunk does not see the whole row of dO * O");
   using Tile = SwzTile<tile_width(D), D>;
   static_assert(kDqBK == Tile::kRows, "key tile is one SwzTile");
   constexpr int KS = D / 16;
@@ -143,7 +147,26 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
   }
   const float lq2 = qok ? lse[(int64_t)bh * Nq + qry] * kLog2e : 0.f;
-  const float dlt = qok ? delta[(int64_t)bh * Nq + qry] : 0.f;
+  // D of the lane's query.  FORM_D: from the dO^T fragments already in
+  // registers and the same columns of the query's O row, then one add across
+  // the two lane halves (both halves get the same sum); half 0 stores it.
+  float dlt;
+  if constexpr (FORM_D) {
+    float part = 0.f;
+    if (qok) {
+      const __bf16* orow = o + qhead + (int64_t)qry * D + half * 8;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8 of = *reinterpret_cast<const bf16x8*>(orow + 16 * s);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part = fmaf((float)of[e], (float)df[s][e], part);
+      }
+    }
+    dlt = sum_across_halves(part);
+    if (qok && half == 0) delta[(int64_t)bh * Nq + qry] = dlt;
+  } else {
+    dlt = qok ? delta[(int64_t)bh * Nq + qry] : 0.f;
+  }
   // d <= 64: dP^T - D on the matrix unit.  One more k-step of dP^T = V dO^T
   // with an all-ones column pair in V (A operand) against -D split into two
   // bf16 parts in dO (B operand) subtracts D_hi + D_lo = D (to 2^-16
@@ -414,6 +437,13 @@ hipError_t launch_phase(const BwdArgs& a, int phase) {
   } else if (phase == 1) {
     return launch_bwd_dkdv(a);
   } else {
+    const bool form_d = phase == 3;
+    if (form_d && a.dq_splits > 1) {
+      // key chunks each see part of a row only: D from the preprocess kernel
+      const hipError_t e = launch_phase<D>(a, 0);
+      if (e != hipSuccess) return e;
+      return launch_phase<D>(a, 2);
+    }
     const int nqt = (a.Nq + kDqBQ - 1) / kDqBQ;
     // d = 256 without the mask runs the masked kernel with every key visible
     // (off = Nk): its unmasked instantiation spills registers there
@@ -423,22 +453,22 @@ hipError_t launch_phase(const BwdArgs& a, int phase) {
       // every key), then the reduction
       hipLaunchKernelGGL((bwd_dq_kernel<D, true, true>), dim3((unsigned)((int64_t)BH * nqt * a.dq_splits)),
                          dim3(kBwdThreads), 0, s, (const __bf16*)a.q, (const __bf16*)a.k,
-                         (const __bf16*)a.v, (const __bf16*)a.dout, a.lse, a.delta, (__bf16*)a.dq,
-                         BH, a.Nq, a.Nk, dq_off, nqt, a.scale, a.scale * kLog2e, a.dq_part,
-                         a.dq_chunk);
+                         (const __bf16*)a.v, (const __bf16*)a.dout, (const __bf16*)a.o, a.lse,
+                         a.delta, (__bf16*)a.dq, BH, a.Nq, a.Nk, dq_off, nqt, a.scale,
+                         a.scale * kLog2e, a.dq_part, a.dq_chunk);
       const int64_t n = (int64_t)BH * a.Nq * D;
       hipLaunchKernelGGL(bwd_dq_reduce_kernel, dim3((unsigned)((n / 8 + 255) / 256)), dim3(256), 0, s,
                          (const float*)a.dq_part, (__bf16*)a.dq, n, a.dq_splits);
       return hipGetLastError();
     }
-    auto kern = bwd_dq_kernel<D, true>;
+    auto kern = form_d ? bwd_dq_kernel<D, true, false, true> : bwd_dq_kernel<D, true>;
     if constexpr (D <= 128) {
-      if (!a.causal) kern = bwd_dq_kernel<D, false>;
+      if (!a.causal) kern = form_d ? bwd_dq_kernel<D, false, false, true> : bwd_dq_kernel<D, false>;
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)(BH * nqt)), dim3(kBwdThreads), 0, s,
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
-                       (const __bf16*)a.dout, a.lse, a.delta, (__bf16*)a.dq, BH, a.Nq, a.Nk,
-                       dq_off, nqt, a.scale, a.scale * kLog2e, (float*)nullptr, 0);
+                       (const __bf16*)a.dout, (const __bf16*)a.o, a.lse, a.delta, (__bf16*)a.dq,
+                       BH, a.Nq, a.Nk, dq_off, nqt, a.scale, a.scale * kLog2e, (float*)nullptr, 0);
   }
   return hipGetLastError();
 }
@@ -474,12 +504,11 @@ BwdDqSplit bwd_dq_split_plan(int B, int H, int Nq, int Nk, int d) {
   return sp;
 }
 
+// dQ forming D (phase 3), then dK/dV, which reads that D (phase 1)
 hipError_t launch_bwd(const BwdArgs& a) {
-  for (int phase = 0; phase < 3; ++phase) {
-    const hipError_t e = launch_bwd_phase(a, phase);
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  const hipError_t e = launch_bwd_phase(a, 3);
+  if (e != hipSuccess) return e;
+  return launch_bwd_phase(a, 1);
 }
 
 }  // namespace attn

@@ -277,7 +277,7 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       // same VALU work beside its two MFMAs.
       constexpr int US = 2 * DB;
       constexpr int NSTEPS = 2 * KS + 2 * US;
-      constexpr int kPrefetch = D <= 32 ? 1 : D <= 64 ? 2 : 3;
+      constexpr int kPrefetch = D <= 32 ? 1 : D <= 64 ? 2 : D == 128 ? 1 : 3;
       auto read_step = [&](int g) {
         if (g < KS) { const RowFrag f = read_row(0, g); return TrFrag{f.q, f.d}; }
         if (g < 2 * KS) { const RowFrag f = read_row(1, g - KS); return TrFrag{f.q, f.d}; }
