@@ -13,7 +13,9 @@ Coverage:
 * the dV / dK sum invariants of the backward at full size;
 * scales other than 1/sqrt(d) (1.0 and 0.02) on causal and unmasked ragged
   shapes, forward (bf16 and fp32) and backward;
-* determinism of the forward and of the backward; lse at a 4-byte offset;
+* determinism of the forward and of the backward; the backward's phases one by one
+  (attn_bwd = phase 3 then 1, bitwise; phases 0, 1, 2 within the rounding of D); lse at a
+  4-byte offset;
 * a long sequence (N = 65573, both masks) on sampled rows, forward and backward (dQ rows
   against the oracle's row-wise dQ, dV / dK sum invariants over every key);
 * many heads (B = 6, H = 37) of a short sequence, forward and backward.
@@ -200,6 +202,49 @@ def test_backward_is_deterministic(d):
         outs.append(g)
     for a, b in zip(*outs):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("d,causal", [(64, True), (128, True), (128, False), (256, True)])
+def test_backward_phases(d, causal):
+    """attn_bwd is phase 3 (dQ forming D itself) then phase 1 (dK/dV): those
+    two phases called one by one give its results bit for bit, and the D
+    phase 3 leaves in the workspace is the D of phase 0 up to fp32 rounding
+    (the same products summed in another order).  Phases 0, 1, 2 then give
+    the same gradients within the rounding that difference in D makes, which
+    is far below a bf16 unit."""
+    import tiled_online_softmax_attn_amd as T
+    dev = torch.device("cuda:0")
+    B, H, N = 1, 3, 333
+    q, k, v, do = (t.to(dev) for t in make_inputs(B, H, N, d, torch.bfloat16, seed=21 + d,
+                                                   with_dout=True))
+    scale = d ** -0.5
+    o, lse = T.flash_attention_forward(q, k, v, causal, scale)
+    ws = torch.empty(T.attn_bwd_workspace_bytes(B, H, N, d), device=dev, dtype=torch.uint8)
+    D = ws[: B * H * N * 4].view(torch.float32)
+    nan = lambda: [torch.full_like(q, float("nan")) for _ in range(3)]
+    ref = nan()
+    T.attn_bwd(q, k, v, o, do, lse, ref[0], ref[1], ref[2], ws, causal, scale)
+    g31 = nan()
+    T.attn_bwd_phase(3, q, k, v, o, do, lse, g31[0], g31[1], g31[2], ws, causal, scale)
+    torch.cuda.synchronize()
+    d3 = D.clone()
+    T.attn_bwd_phase(1, q, k, v, o, do, lse, g31[0], g31[1], g31[2], ws, causal, scale)
+    g012 = nan()
+    for ph in (0, 1, 2):
+        T.attn_bwd_phase(ph, q, k, v, o, do, lse, g012[0], g012[1], g012[2], ws, causal, scale)
+    torch.cuda.synchronize()
+    d0 = D.clone()
+    for a, b in zip(ref, g31):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    d_exact = (do.double() * o.double()).sum(-1).flatten()
+    scale_d = (do.double().abs() * o.double().abs()).sum(-1).flatten()
+    for dd in (d3, d0):
+        # fp32 sums of d products: |error| <= d * 2^-24 * sum |dO O| (plus slack)
+        assert torch.all((dd.double() - d_exact).abs() <= 2 * d * 2.0 ** -24 * scale_d + 1e-30)
+    for a, b in zip(ref, g012):
+        diff = (a.float() - b.float()).abs()
+        ulp = a.float().abs().clamp_min(2.0 ** -60) * 2.0 ** -7
+        assert torch.all(diff <= ulp + 1e-6), float(diff.max())
 
 
 def test_lse_at_4_byte_offset():
