@@ -7,9 +7,9 @@
 // registers while it walks the query tiles that see them, recomputing
 //   S = Q K^T,  P = e^{scale*S - L},  dV += P^T dO,
 //   dP = dO V^T,  dS = P * (dP - D),  dK += scale * dS^T Q
-// from Q, dO, the saved logsumexp L and D = rowsum(dO * O) (phase 0,
-// attn_bwd.hip).  Every dK / dV element is written once, by the workgroup
-// that owns its key.
+// from Q, dO, the saved logsumexp L and D = rowsum(dO * O) (formed by the dQ
+// kernel, which runs first, or by the preprocess kernel; attn_bwd.hip).  Every
+// dK / dV element is written once, by the workgroup that owns its key.
 //
 // Register layout (v_mfma_f32_32x32x16_bf16; see device_common.h): S = Q K^T
 // and dP = dO V^T with K^T / V^T fragments resident in registers, so every
