@@ -72,7 +72,8 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   __shared__ __attribute__((aligned(1024))) unsigned char lds_q1[Tile::kBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char lds_do0[Tile::kBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char lds_do1[Tile::kBytes];
-  __shared__ __attribute__((aligned(16))) float lds_stats[2][2][kKvBQ];  // [buffer][L, D][query]
+  // [buffer][L, D][query]; D is stored negated at d <= 64 (see kDpFromNegD)
+  __shared__ __attribute__((aligned(16))) float lds_stats[2][2][kKvBQ];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -138,7 +139,7 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   auto store_stats = [&](auto buf_tag) {
     if (tid < kKvBQ) {
       lds_stats[decltype(buf_tag)::value][0][tid] = rl * kLog2e;
-      lds_stats[decltype(buf_tag)::value][1][tid] = rd;
+      lds_stats[decltype(buf_tag)::value][1][tid] = D <= 64 ? -rd : rd;
     }
   };
   using Buf0 = std::integral_constant<int, 0>;
@@ -178,7 +179,7 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       const ATTN_LDS unsigned char* qs = q_lds(cur_tag);
       const ATTN_LDS unsigned char* dos = do_lds(cur_tag);
       const float* lq = lds_stats[CUR][0];
-      const float* dq_d = lds_stats[CUR][1];
+      const float* dstat = lds_stats[CUR][1];  // -D at d <= 64, D above
       const bool need_mask =
           (q0 + kKvBQ > Nq) || (key_w0 + 32 > Nk) || (CAUSAL && q0 + off < key_w0 + 31);
 
@@ -190,15 +191,36 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       //   C  dV, dK of block 0  |  P, dS of block 1
       //   D  dV, dK of block 1
       // Every LDS operand is read one step before the MFMAs that use it, and
-      // each softmax part's L and D values one part ahead, so that with a
-      // single wave per SIMD the LDS latency stays off the critical path.
+      // each softmax part's L values one part ahead, so that with a single
+      // wave per SIMD the LDS latency stays off the critical path.
       f32x16 sacc[2] = {f32x16{}, f32x16{}};
+      // d <= 64: dP = dO V^T accumulates on top of -D.  Entry i of block qb
+      // belongs to query row qb*32 + (i/4)*8 + half*4 + i%4, so its four
+      // consecutive entries 4r .. 4r+3 start from four consecutive -D values
+      // of the LDS stats, and the matrix unit delivers dP - D itself: 32 VALU
+      // subtractions fewer per tile (fp32 sums in another order than dP
+      // first, then - D).  B4 H16 N4096 causal, one box: d = 64 145.2 ->
+      // 142.1 us, d = 32 175.3 -> 167.1 us; at d = 128, one wave per SIMD,
+      // 551.7 -> 561.3 us, so d >= 96 subtract in the softmax as before.
+      constexpr bool kDpFromNegD = D <= 64;
       f32x16 pacc[2] = {f32x16{}, f32x16{}};
+      auto init_dp = [&](int qb) {
+        if constexpr (!kDpFromNegD) return;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float4 nd = *reinterpret_cast<const float4*>(dstat + qb * 32 + r * 8 + half * 4);
+          pacc[qb][4 * r] = nd.x;
+          pacc[qb][4 * r + 1] = nd.y;
+          pacc[qb][4 * r + 2] = nd.z;
+          pacc[qb][4 * r + 3] = nd.w;
+        }
+      };
+      init_dp(0);
       bf16x8 pa[2][2], sa[2][2];
 
       struct RowFrag { bf16x8 q, d; };   // Q and dO rows: one k-step of one block
       struct TrFrag { bf16x8 d, q; };    // dO and Q transposed: one (t, b) step
-      struct Stats { float4 l, d; };     // L and D of 4 query rows
+      struct Stats { float4 l, d; };     // L (and D) of 4 query rows
       // k-step s of S = Q K^T and dP = dO V^T for block qb
       auto read_row = [&](int qb, int s) {
         const int at = (rd_base ^ (32 * s)) + qb * 32 * RB;
@@ -225,17 +247,20 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         dv_acc[b] = mfma_32x32x16(pa[qb][t], f.d, dv_acc[b]);
         dk_acc[b] = mfma_32x32x16(sa[qb][t], f.q, dk_acc[b]);
       };
-      // L and D of query rows qb*32 + r*8 + half*4 + e, e = 0..3
+      // L (and D, where the softmax subtracts it) of query rows
+      // qb*32 + r*8 + half*4 + e, e = 0..3
       auto read_stats = [&](int qb, int r) {
         const int qrow0 = qb * 32 + r * 8 + half * 4;
-        return Stats{*reinterpret_cast<const float4*>(lq + qrow0),
-                     *reinterpret_cast<const float4*>(dq_d + qrow0)};
+        Stats st;
+        st.l = *reinterpret_cast<const float4*>(lq + qrow0);
+        if constexpr (!kDpFromNegD) st.d = *reinterpret_cast<const float4*>(dstat + qrow0);
+        return st;
       };
       // Entries [lo, hi) of block qb: P = 2^{S scale log2e - L log2e} and
       // dS = P (dP - D), each bf16 pair converted as soon as both are done.
-      // Entry i belongs to query row qb*32 + (i/4)*8 + half*4 + i%4; its L and
-      // D are part i/4 of the block, held in sv[(i/4) & 1] and read one part
-      // ahead (the last part of block 0 reads the first of block 1).
+      // Entry i belongs to query row qb*32 + (i/4)*8 + half*4 + i%4; its L
+      // (and -D) are part i/4 of the block, held in sv[(i/4) & 1] and read one
+      // part ahead (the last part of block 0 reads the first of block 1).
       Stats sv[2];
       auto soft_range = [&](int qb, int lo, int hi, auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
@@ -248,7 +273,6 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
           }
           const Stats& st4 = sv[r & 1];
           const float lv = e == 0 ? st4.l.x : e == 1 ? st4.l.y : e == 2 ? st4.l.z : st4.l.w;
-          const float dv1 = e == 0 ? st4.d.x : e == 1 ? st4.d.y : e == 2 ? st4.d.z : st4.d.w;
           float p = fast_exp2(fmaf(sacc[qb][i], scale_log2, -lv));
           if constexpr (MASK) {
             const int qq = q0 + qb * 32 + r * 8 + half * 4 + e;
@@ -257,7 +281,12 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
           // keep the exponential at this point of the issue order
           __asm__ volatile("" ::"v"(p));
           sacc[qb][i] = p;
-          pacc[qb][i] = p * (pacc[qb][i] - dv1);
+          if constexpr (kDpFromNegD) {
+            pacc[qb][i] = p * pacc[qb][i];
+          } else {
+            const float dv1 = e == 0 ? st4.d.x : e == 1 ? st4.d.y : e == 2 ? st4.d.z : st4.d.w;
+            pacc[qb][i] = p * (pacc[qb][i] - dv1);
+          }
           if (i & 1) {
             pa[qb][i >> 3][(i & 7) - 1] = (__bf16)sacc[qb][i - 1];
             pa[qb][i >> 3][i & 7] = (__bf16)sacc[qb][i];
@@ -295,7 +324,10 @@ bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
           if (g < KS) {
             // A: S, dP of block 0
             mma_sdp(0, g, RowFrag{f.d, f.q});
-            if (g == KS - 1) sv[0] = read_stats(0, 0);
+            if (g == KS - 1) {
+              sv[0] = read_stats(0, 0);
+              init_dp(1);
+            }
           } else if (g < 2 * KS) {
             // B: S, dP of block 1 | entries 16s/KS .. 16(s+1)/KS of block 0
             const int s = g - KS;
