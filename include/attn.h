@@ -275,7 +275,8 @@ const char* attn_status_str(int status);
  * a calling contract changes (2: attn_fwd_kv and attn_fwd_kv_workspace_bytes;
  * 3: attn_softmax_rows, and head dimensions 32, 96 and 256; 4: attn_fwd_mx;
  * 5: attn_bwd_noalloc; 6: attn_bwd_kv and attn_bwd_kv_workspace_bytes;
- * 7: attn_fwd_fp8; 8: attn_fwd_kv with one key chunk needs no workspace). */
+ * 7: attn_fwd_fp8; 8: attn_fwd_kv with one key chunk needs no workspace;
+ * 9: attn_bwd_phase 3, and attn_bwd as phase 3 then phase 1). */
 int attn_abi_version(void);
 
 #ifdef __cplusplus

@@ -71,7 +71,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = _lib()
-    assert lib.attn_abi_version() == 8
+    assert lib.attn_abi_version() == 9
     for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, 12345]:
         s = lib.attn_status_str(code)
         assert isinstance(s, bytes) and len(s) > 0

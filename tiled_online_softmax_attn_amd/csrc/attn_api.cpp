@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 8;
+constexpr int kAbiVersion = 9;
 
 // Device scratch of attn_bwd_noalloc: the D vector (one fp32 per query row)
 // that attn_bwd keeps in the caller's workspace.  16 MiB per GPU, so
