@@ -147,41 +147,10 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
   }
   const float lq2 = qok ? lse[(int64_t)bh * Nq + qry] * kLog2e : 0.f;
-  // D of the lane's query.  FORM_D: from the dO^T fragments already in
-  // registers and the same columns of the query's O row, then one add across
-  // the two lane halves (both halves get the same sum); half 0 stores it.
-  float dlt;
-  if constexpr (FORM_D) {
-    float part = 0.f;
-    if (qok) {
-      const __bf16* orow = o + qhead + (int64_t)qry * D + half * 8;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const bf16x8 of = *reinterpret_cast<const bf16x8*>(orow + 16 * s);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) part = fmaf((float)of[e], (float)df[s][e], part);
-      }
-    }
-    dlt = sum_across_halves(part);
-    if (qok && half == 0) delta[(int64_t)bh * Nq + qry] = dlt;
-  } else {
-    dlt = qok ? delta[(int64_t)bh * Nq + qry] : 0.f;
-  }
-  // d <= 64: dP^T - D on the matrix unit.  One more k-step of dP^T = V dO^T
-  // with an all-ones column pair in V (A operand) against -D split into two
-  // bf16 parts in dO (B operand) subtracts D_hi + D_lo = D (to 2^-16
-  // relative) from every entry of the lane's query, in place of 16 VALU
-  // subtractions per 32-key half.
-  constexpr bool kFoldD = D <= 64;
-  bf16x8 ones_x = {}, negd_x = {};
-  if (kFoldD && half == 0) {
-    const __bf16 dhi = (__bf16)(-dlt);
-    const __bf16 dlo = (__bf16)(-dlt - (float)dhi);
-    ones_x[0] = (__bf16)1.f;
-    ones_x[1] = (__bf16)1.f;
-    negd_x[0] = dhi;
-    negd_x[1] = dlo;
-  }
+  // D of the lane's query: read from the preprocess kernel's output, or
+  // (FORM_D) formed below once the O rows of the workgroup are in LDS.
+  float dlt = 0.f;
+  if constexpr (!FORM_D) dlt = qok ? delta[(int64_t)bh * Nq + qry] : 0.f;
 
   // keys past the last one the workgroup's last query sees are not visited;
   // a split visits only its chunk (key tiles t_begin .. t_begin + n_tiles - 1)
@@ -204,8 +173,49 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   for (int b = 0; b < DB; ++b) dq_acc[b] = f32x16{};
 
   if (n_tiles > 0) load_tile(t_begin, Buf0{});
+  if constexpr (FORM_D) {
+    // the workgroup's 128 O rows into the second K / V buffers, which the
+    // first copies of the loop fill only after the barrier below
+    Tile::template load<kBwdThreads / 64>(o + qhead, qt * kDqBQ, Nq, k_lds(Buf1{}), wave, lane);
+    Tile::template load<kBwdThreads / 64>(o + qhead, qt * kDqBQ + kDqBK, Nq, v_lds(Buf1{}), wave,
+                                          lane);
+  }
   wait_vmem();
   __syncthreads();
+  if constexpr (FORM_D) {
+    // D = rowsum(dO * O): the lane's dO^T fragments are in registers, and the
+    // same columns of its query's O row are read from LDS with the row-read
+    // pattern of the K tiles (query row 32 (wave & 1) + l32 of buffer
+    // wave / 2); one add across the two lane halves (both halves get the same
+    // sum), and half 0 stores D for the dK/dV kernel.
+    const ATTN_LDS unsigned char* obuf = wave < 2 ? k_lds(Buf1{}) : v_lds(Buf1{});
+    const int orow = (wave & 1) * 32 * RB;
+    float part = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const bf16x8 of = *reinterpret_cast<const ATTN_LDS bf16x8*>(obuf + (rd_base ^ (32 * s)) + orow);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = fmaf((float)of[e], (float)df[s][e], part);
+    }
+    dlt = sum_across_halves(part);
+    if (qok && half == 0) delta[(int64_t)bh * Nq + qry] = dlt;
+    __syncthreads();  // every wave has read its O rows before tile 1 is copied over them
+  }
+  // d <= 64: dP^T - D on the matrix unit.  One more k-step of dP^T = V dO^T
+  // with an all-ones column pair in V (A operand) against -D split into two
+  // bf16 parts in dO (B operand) subtracts D_hi + D_lo = D (to 2^-16
+  // relative) from every entry of the lane's query, in place of 16 VALU
+  // subtractions per 32-key half.
+  constexpr bool kFoldD = D <= 64;
+  bf16x8 ones_x = {}, negd_x = {};
+  if (kFoldD && half == 0) {
+    const __bf16 dhi = (__bf16)(-dlt);
+    const __bf16 dlo = (__bf16)(-dlt - (float)dhi);
+    ones_x[0] = (__bf16)1.f;
+    ones_x[1] = (__bf16)1.f;
+    negd_x[0] = dhi;
+    negd_x[1] = dlo;
+  }
 
   // One K/V tile t_begin + j, held in buffer CUR; the copies of the next go to
   // the other buffer meanwhile.
