@@ -299,12 +299,12 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
           __builtin_amdgcn_sched_barrier(0);
           // B: entries 16s/KS .. 16(s+1)/KS of half 0's softmax per k-step.
           // Through B and C, the two phases that carry a softmax beside their
-          // MFMAs, the wave takes issue priority over the other wave of its
-          // SIMD (two waves per SIMD at d <= 128), so that its matrix steps
-          // are not held behind the other wave's MFMA-only phases (B4 H16
-          // N4096 causal dQ forming D: d = 128 395.1 -> 388.0 us, d = 64
-          // 110.7 -> 106.2 us).
-          if constexpr (D <= 128) __builtin_amdgcn_s_setprio(1);
+          // MFMAs, the wave takes issue priority over the other waves of its
+          // SIMD (d = 64 .. 128), so that its matrix steps are not held behind
+          // their MFMA-only phases (B4 H16 N4096 causal dQ forming D: d = 128
+          // 395.1 -> 388.0 us, d = 64 110.7 -> 106.2 us).  At d = 32, three
+          // waves per SIMD and a short softmax, it cost 142.1 against 129.6 us.
+          if constexpr (D >= 64 && D <= 128) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
             sdp_step(1, s);
@@ -321,7 +321,7 @@ bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             dq_step(g, kr[g & 1]);
             if (g < UQ) soft_range(1, 16 * g / UQ, 16 * (g + 1) / UQ, mask_tag);
             __builtin_amdgcn_sched_barrier(0);
-            if (D <= 128 && g == UQ - 1) __builtin_amdgcn_s_setprio(0);
+            if (D >= 64 && D <= 128 && g == UQ - 1) __builtin_amdgcn_s_setprio(0);
           }
         };
         if (need_mask)
